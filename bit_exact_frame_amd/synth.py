@@ -1,0 +1,116 @@
+"""Seeded synthetic luma planes for the five frame workloads.
+
+This module only draws samples.  It holds none of the reductions'
+arithmetic (no squares, no sums), so the CPU oracle and the HIP path can
+both take their inputs from it.
+
+Every plane is drawn by ``numpy.random.Generator(PCG64(SeedSequence(
+[SEED, workload, frame])))``: the reference plane first, then the distorted
+one.  Planes are C-ordered ``(h, stride)``; samples beyond ``w`` in each row
+are padding, filled with the container's all-ones value so that a kernel
+that reads them gives a wrong answer.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+SEED = 0xBEF
+
+
+@dataclass(frozen=True)
+class Workload:
+    key: int
+    name: str
+    bpc: int
+    w: int
+    h: int
+    stride: int
+    frames: int
+    recipe: str
+
+    @property
+    def dtype(self):
+        return np.uint8 if self.bpc == 8 else np.uint16
+
+    @property
+    def sample_bytes(self) -> int:
+        return 1 if self.bpc == 8 else 2
+
+    @property
+    def bytes_per_frame(self) -> int:
+        """Algorithmic bytes: each of the two planes' w*h samples read once."""
+        return 2 * self.w * self.h * self.sample_bytes
+
+
+WORKLOADS = {
+    1: Workload(1, "8bit_176x144_uniform", 8, 176, 144, 176, 4,
+                "ref, dis i.i.d. uniform [0,255]"),
+    2: Workload(2, "10bit_1920x1080_lowbits_noise8", 10, 1920, 1080, 1920,
+                32, "ref = 4*U[0,255] + U[1,3]; dis = clip(ref + rint(N(0,8^2)), 0, 1023)"),
+    3: Workload(3, "12bit_2560x1440_stride2624_noise64", 12, 2560, 1440,
+                2624, 32, "ref U[0,4095]; dis = clip(ref + rint(N(0,64^2)), 0, 4095)"),
+    4: Workload(4, "16bit_3840x2160_fullrange", 16, 3840, 2160, 3840, 16,
+                "ref, dis i.i.d. uniform [0,65535]"),
+    5: Workload(5, "16bit_3840x2160_halfrange", 16, 3840, 2160, 3840, 8,
+                "ref U[32768,65535], dis U[0,32767]"),
+}
+
+
+def rng_for(key: int, frame: int) -> np.random.Generator:
+    return np.random.Generator(
+        np.random.PCG64(np.random.SeedSequence([SEED, int(key), int(frame)])))
+
+
+def _draw(wl: Workload, rng: np.random.Generator):
+    h, w = wl.h, wl.w
+    if wl.key == 1:
+        ref = rng.integers(0, 256, size=(h, w))
+        dis = rng.integers(0, 256, size=(h, w))
+    elif wl.key == 2:
+        # "low two bits forced non-zero": the 2-bit field is drawn from
+        # {1, 2, 3}, so every codeword has a fractional part at 10 bpc.
+        ref = 4 * rng.integers(0, 256, size=(h, w)) + rng.integers(1, 4, size=(h, w))
+        dis = np.clip(ref + np.rint(rng.normal(0.0, 8.0, size=(h, w))), 0, 1023)
+    elif wl.key == 3:
+        ref = rng.integers(0, 4096, size=(h, w))
+        dis = np.clip(ref + np.rint(rng.normal(0.0, 64.0, size=(h, w))), 0, 4095)
+    elif wl.key == 4:
+        ref = rng.integers(0, 65536, size=(h, w))
+        dis = rng.integers(0, 65536, size=(h, w))
+    elif wl.key == 5:
+        ref = rng.integers(32768, 65536, size=(h, w))
+        dis = rng.integers(0, 32768, size=(h, w))
+    else:
+        raise KeyError(wl.key)
+    return ref, dis
+
+
+def make_frames(key: int, frames: int | None = None, first: int = 0):
+    """Return (ref, dis): arrays of shape (F, h, stride) of the workload's
+    container dtype, frames ``first .. first+F-1``."""
+    wl = WORKLOADS[key]
+    n = wl.frames if frames is None else int(frames)
+    pad = np.iinfo(wl.dtype).max
+    ref = np.full((n, wl.h, wl.stride), pad, dtype=wl.dtype)
+    dis = np.full((n, wl.h, wl.stride), pad, dtype=wl.dtype)
+    for k in range(n):
+        r, d = _draw(wl, rng_for(key, first + k))
+        ref[k, :, :wl.w] = r
+        dis[k, :, :wl.w] = d
+    return ref, dis
+
+
+def uniform_planes(seed: int, frames: int, h: int, w: int, stride: int,
+                   bpc: int, lo: int = 0, hi: int | None = None):
+    """Generic seeded uniform planes for parity cases of arbitrary shape."""
+    dtype = np.uint8 if bpc == 8 else np.uint16
+    top = (1 << (8 if bpc == 8 else 16)) if hi is None else hi
+    pad = np.iinfo(dtype).max
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([SEED, 99, seed])))
+    ref = np.full((frames, h, stride), pad, dtype=dtype)
+    dis = np.full((frames, h, stride), pad, dtype=dtype)
+    ref[:, :, :w] = rng.integers(lo, top, size=(frames, h, w))
+    dis[:, :, :w] = rng.integers(lo, top, size=(frames, h, w))
+    return ref, dis
