@@ -1,0 +1,171 @@
+"""Benchmark: fused float_moment + float_psnr over 16-bit 3840x2160 frames.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4]
+
+One step = the whole hot path (per-row exact sums, plan, walk with its
+fallbacks, PSNR row chain, divisions) over one batch of the workload's
+frames already resident in HBM.  Batches rotate through a ring of device
+copies larger than the 256 MB Infinity Cache, so every step reads its
+frames from HBM.  Prints ONE JSON line.
+
+value          frames per second over the timed steps (torch events on the
+               launch stream, bracketed by synchronisations)
+roofline       the row-sum kernel (the dominant one): algorithmic bytes per
+               launch (2 planes x w x h x 2 B x frames) over its average
+               duration, measured with HIP events the library records on the
+               launch stream; peak = MI355X HBM3E 8 TB/s
+cpu_baseline   the CPU oracle (plain loops), timed on this host's cores, one
+               frame per thread, on a bounded sample of the same frames
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+
+
+def cpu_baseline(ref, dis, bpc, w, budget_s=12.0, max_threads=16):
+    """Time the oracle over host copies of the batch, one frame per thread."""
+    import concurrent.futures as cf
+
+    import numpy as np
+
+    import oracle
+
+    orc = oracle.Oracle()
+    t0 = time.perf_counter()
+    orc.frames(ref[:1], dis[:1], bpc, w=w)
+    one = time.perf_counter() - t0
+    threads = max(1, min(max_threads, os.cpu_count() or 1))
+    frames = ref.shape[0]
+    # enough frames for about budget_s of CPU work in total, at least one
+    # pass over the batch
+    n = max(frames, int(math.ceil(budget_s / max(one, 1e-6))))
+    n = int(math.ceil(n / threads) * threads)
+    idx = [k % frames for k in range(n)]
+
+    def work(k):
+        return orc.frames(ref[k:k + 1], dis[k:k + 1], bpc, w=w)
+
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(work, idx))
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "frames/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} frames of the batch ({frames} distinct), one frame per thread, "
+                      f"{threads} threads, {dt:.1f} s wall; one frame alone took {one * 1e3:.1f} ms"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=4)
+    ap.add_argument("--ring", type=int, default=0, help="device copies of the batch (0 = auto)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): this path is a "
+              "per-frame reduction with no cross-GPU exchange; frames shard with no "
+              "communication, so one GPU's throughput is the figure.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from bit_exact_frame_amd import api, synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    wl = synth.WORKLOADS[args.workload]
+    ref_h, dis_h = synth.make_frames(args.workload)
+    F = ref_h.shape[0]
+    batch_bytes = F * wl.bytes_per_frame
+    ring = args.ring or max(2, int(math.ceil(4 * 256e6 / batch_bytes)))
+    refs = [torch.from_numpy(ref_h).cuda() for _ in range(ring)]
+    diss = [torch.from_numpy(dis_h).cuda() for _ in range(ring)]
+    out = torch.empty((F, 6), dtype=torch.float64, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    # correctness of this very configuration, outside the timed region
+    api.bef_debug_set(0)
+    mom, ps = api.bef_frames(refs[0], diss[0], wl.bpc, w=wl.w)
+
+    for k in range(args.warmup):
+        api.bef_frames_async(refs[k % ring], diss[k % ring], wl.bpc, out, w=wl.w, stream=stream)
+    torch.cuda.synchronize()
+
+    api.bef_timing_enable(True)
+    api.bef_timing_reset()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for k in range(args.steps):
+        api.bef_frames_async(refs[k % ring], diss[k % ring], wl.bpc, out, w=wl.w, stream=stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    api.bef_timing_enable(False)
+    total_ms = ev0.elapsed_time(ev1)
+    rows_ms, rows_n = api.bef_timing_read("rows")
+    walk_ms, walk_n = api.bef_timing_read("walk")
+
+    # the same steps untimed by the library (no per-kernel events)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for k in range(args.steps):
+        api.bef_frames_async(refs[k % ring], diss[k % ring], wl.bpc, out, w=wl.w, stream=stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    clean_ms = ev0.elapsed_time(ev1)
+
+    ms_per_step = clean_ms / args.steps
+    fps = F * args.steps / (clean_ms / 1e3)
+    rows_avg_ms = rows_ms / max(rows_n, 1)
+    achieved = batch_bytes / (rows_avg_ms / 1e3) / 1e9
+
+    got = out.cpu().numpy()
+    assert (got[:, :4].view(np.uint64) == mom.view(np.uint64)).all()
+
+    rec = {
+        "metric": "frames/sec and achieved HBM GB/s (% of peak), 16-bit 3840x2160, 1 MI355X",
+        "value": round(fps, 1),
+        "unit": "frames/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u16 in, u64/f64 sums",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "frames_per_step": F, "w": wl.w, "h": wl.h,
+                   "bpc": wl.bpc, "recipe": wl.recipe, "ring_copies": ring,
+                   "whole_path_GBps": round(batch_bytes * args.steps / (clean_ms / 1e3) / 1e9, 1),
+                   "whole_path_frac": round(batch_bytes * args.steps / (clean_ms / 1e3) / 1e9
+                                            / PEAK_HBM_GBS, 4),
+                   "walk_avg_us": round(1e3 * walk_ms / max(walk_n, 1), 2),
+                   "timed_with_events_ms_per_step": round(total_ms / args.steps, 5)},
+        "roofline": {"bound": "hbm", "kernel": "k_rows16", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "bytes_per_launch": batch_bytes,
+                     "avg_launch_us": round(rows_avg_ms * 1e3, 2)},
+    }
+    if not args.no_cpu:
+        rec["cpu_baseline"] = cpu_baseline(ref_h, dis_h, wl.bpc, wl.w)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,210 @@
+"""Thin ctypes binding of libbef.so (include/bef.h), same names as the C ABI.
+
+Argument marshalling only: tensors in, pointers and sizes to the C entry
+points, results out.  Every step of the reductions runs in the library's
+HIP kernels.  If libbef.so is missing this module raises at import: there is
+no CPU fallback.
+
+Planes are torch tensors in device memory (uint8 for bpc 8, uint16
+otherwise), shaped (h, stride) for one frame or (F, h, stride) for a batch,
+C-contiguous; ``w`` defaults to the last dimension.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbef.so")
+
+if not os.path.exists(LIB_PATH):
+    raise RuntimeError(
+        f"{LIB_PATH} is missing: build it first "
+        "(python -m bit_exact_frame_amd.build or __graft_entry__.build())")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_vp, _i, _pd, _u = ctypes.c_void_p, ctypes.c_int, ctypes.c_ssize_t, ctypes.c_uint
+_dp = ctypes.POINTER(ctypes.c_double)
+_u64p = ctypes.POINTER(ctypes.c_uint64)
+
+_lib.moment_frame.argtypes = [_vp, _vp, _i, _i, _pd, _i, _dp]
+_lib.psnr_noise.argtypes = [_vp, _vp, _i, _i, _pd, _i, _dp]
+_lib.bef_frames.argtypes = [_vp, _vp, _i, _i, _pd, _pd, _i, _i, _vp, _dp, _dp]
+_lib.bef_frames_async.argtypes = [_vp, _vp, _i, _i, _pd, _pd, _i, _i, _vp, _vp]
+_lib.bef_frames_units.argtypes = [_vp, _vp, _i, _i, _pd, _pd, _i, _i, _vp, _u64p]
+for _n in ("moment_frame", "psnr_noise", "bef_frames", "bef_frames_async",
+           "bef_frames_units"):
+    getattr(_lib, _n).restype = _i
+_lib.bef_last_error.restype = ctypes.c_char_p
+_lib.bef_debug_set.argtypes = [_u]
+_lib.bef_debug_set.restype = _u
+_lib.bef_timing_enable.argtypes = [_i]
+_lib.bef_timing_read.argtypes = [_i, _dp, ctypes.POINTER(ctypes.c_long)]
+_lib.bef_release.restype = None
+_lib.bef_timing_reset.restype = None
+
+# test hooks (host only)
+_lib.bef_host_plane_units.argtypes = [_vp, _i, _i, _pd, _i, _u, _u64p]
+_lib.bef_host_noise_units.argtypes = [_vp, _vp, _i, _i, _pd, _i, _u64p, _u64p]
+_lib.bef_host_rne53_add.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
+_lib.bef_host_rne53_add.restype = ctypes.c_uint64
+_lib.bef_host_run_pair.argtypes = [_vp, _i, _i, _u64p]
+
+DBG_PLAN_WRONG = 1
+DBG_PLAN_NONE = 2
+DBG_TERMS_ONLY = 4
+DBG_FORCE_ROUND = 8
+DBG_NO_STRETCH = 16
+DBG_NO_CLOSED_FORM = 32
+
+KERNELS = {"rows": 0, "plan": 1, "pairs": 2, "walk": 3}
+
+
+class BefError(RuntimeError):
+    pass
+
+
+def lib():
+    return _lib
+
+
+def last_error() -> str:
+    return _lib.bef_last_error().decode()
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise BefError(f"{what} returned {rc}: {last_error()}")
+
+
+def _geom(t, bpc, w):
+    import torch
+    if not t.is_cuda:
+        raise BefError("planes must be device tensors")
+    want = torch.uint8 if bpc == 8 else torch.uint16
+    if t.dtype != want:
+        raise BefError(f"bpc {bpc} needs {want} planes, got {t.dtype}")
+    if not t.is_contiguous():
+        raise BefError("planes must be contiguous")
+    h, stride = t.shape[-2], t.shape[-1]
+    f = t.shape[0] if t.dim() == 3 else 1
+    return f, h, stride, (stride if w is None else int(w))
+
+
+def _stream_ptr(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def moment_frame(ref, dis, bpc: int, w: int | None = None):
+    """Four moments of one frame: [ref_1st, dis_1st, ref_2nd, dis_2nd]."""
+    _, h, stride, w = _geom(ref, bpc, w)
+    out = (ctypes.c_double * 4)()
+    _check(_lib.moment_frame(ref.data_ptr(), dis.data_ptr(), w, h, stride, bpc, out),
+           "moment_frame")
+    return list(out)
+
+
+def psnr_noise(ref, dis, bpc: int, w: int | None = None):
+    """[noise, mse] of one frame."""
+    _, h, stride, w = _geom(ref, bpc, w)
+    out = (ctypes.c_double * 2)()
+    _check(_lib.psnr_noise(ref.data_ptr(), dis.data_ptr(), w, h, stride, bpc, out),
+           "psnr_noise")
+    return list(out)
+
+
+def bef_frames(ref, dis, bpc: int, w: int | None = None, stream=None):
+    """Batch: returns (moments float64[F,4], psnr float64[F,2])."""
+    f, h, stride, w = _geom(ref, bpc, w)
+    mom = np.zeros((f, 4), np.float64)
+    ps = np.zeros((f, 2), np.float64)
+    _check(_lib.bef_frames(ref.data_ptr(), dis.data_ptr(), w, h, stride, h * stride, f,
+                           bpc, _stream_ptr(stream), mom.ctypes.data_as(_dp),
+                           ps.ctypes.data_as(_dp)), "bef_frames")
+    return mom, ps
+
+
+def bef_frames_async(ref, dis, bpc: int, out, w: int | None = None, stream=None):
+    """Batch into the float64 device tensor ``out`` [F,6]; no sync."""
+    import torch
+    f, h, stride, w = _geom(ref, bpc, w)
+    if out.dtype != torch.float64 or not out.is_cuda or out.numel() < 6 * f:
+        raise BefError("out must be a float64 device tensor of at least 6*F")
+    _check(_lib.bef_frames_async(ref.data_ptr(), dis.data_ptr(), w, h, stride, h * stride,
+                                 f, bpc, _stream_ptr(stream), ctypes.c_void_p(out.data_ptr())),
+           "bef_frames_async")
+
+
+def bef_frames_units(ref, dis, bpc: int, w: int | None = None, stream=None):
+    """Batch diagnostics: uint64[F,8] integer sums in units."""
+    f, h, stride, w = _geom(ref, bpc, w)
+    units = np.zeros((f, 8), np.uint64)
+    _check(_lib.bef_frames_units(ref.data_ptr(), dis.data_ptr(), w, h, stride, h * stride,
+                                 f, bpc, _stream_ptr(stream), units.ctypes.data_as(_u64p)),
+           "bef_frames_units")
+    return units
+
+
+def bef_debug_set(flags: int) -> int:
+    return int(_lib.bef_debug_set(int(flags)))
+
+
+def bef_timing_enable(on: bool):
+    _lib.bef_timing_enable(1 if on else 0)
+
+
+def bef_timing_reset():
+    _lib.bef_timing_reset()
+
+
+def bef_timing_read(kernel: str):
+    ms = ctypes.c_double()
+    n = ctypes.c_long()
+    _check(_lib.bef_timing_read(KERNELS[kernel], ctypes.byref(ms), ctypes.byref(n)),
+           "bef_timing_read")
+    return ms.value, n.value
+
+
+def bef_release():
+    _lib.bef_release()
+
+
+# ---- host-only test hooks --------------------------------------------------
+
+def bef_host_plane_units(plane: np.ndarray, bpc: int, w: int | None = None, dbg: int = 0):
+    h, stride = plane.shape
+    w = stride if w is None else w
+    out = (ctypes.c_uint64 * 3)()
+    _check(_lib.bef_host_plane_units(plane.ctypes.data, w, h, stride, bpc, dbg, out),
+           "bef_host_plane_units")
+    return list(out)
+
+
+def bef_host_noise_units(ref: np.ndarray, dis: np.ndarray, bpc: int, w: int | None = None):
+    h, stride = ref.shape
+    w = stride if w is None else w
+    bits = ctypes.c_uint64()
+    ex = ctypes.c_uint64()
+    _check(_lib.bef_host_noise_units(ref.ctypes.data, dis.ctypes.data, w, h, stride, bpc,
+                                     ctypes.byref(bits), ctypes.byref(ex)),
+           "bef_host_noise_units")
+    return bits.value, ex.value
+
+
+def bef_host_rne53_add(s: int, t: int) -> int:
+    return int(_lib.bef_host_rne53_add(s, t))
+
+
+def bef_host_run_pair(terms: np.ndarray, e: int):
+    t = np.ascontiguousarray(terms, dtype=np.uint32)
+    out = (ctypes.c_uint64 * 2)()
+    _check(_lib.bef_host_run_pair(t.ctypes.data, t.size, e, out), "bef_host_run_pair")
+    return list(out)

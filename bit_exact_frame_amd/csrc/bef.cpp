@@ -1,0 +1,374 @@
+// bef.cpp -- host runtime behind include/bef.h: argument checks, device
+// scratch, the launch sequence on the caller's stream, read-back.
+//
+// Every step of the reductions runs in the kernels (kernels.hip), the final
+// divisions included; the host only validates, allocates scratch, launches
+// and copies the per-frame results back.
+#include <errno.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "bef_internal.h"
+#include "ordsum.h"
+
+using namespace bef;
+
+namespace {
+
+std::mutex g_mu;
+thread_local std::string g_err;
+unsigned g_dbg = 0;
+
+constexpr int kMaxDev = 64;
+struct Arena {
+  void* base = nullptr;
+  size_t cap = 0;
+  void* host = nullptr;  // pinned read-back staging
+  size_t host_cap = 0;
+};
+Arena g_arena[kMaxDev];
+
+// Kernel timing (events recorded on the launch stream).
+struct EvPair {
+  int kernel;
+  hipEvent_t a, b;
+};
+bool g_timing = false;
+std::vector<EvPair> g_ev_live;
+std::vector<hipEvent_t> g_ev_pool;
+double g_ms[4] = {0, 0, 0, 0};
+long g_n[4] = {0, 0, 0, 0};
+
+int fail(int rc, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return rc;
+}
+
+#define BEF_HIP(call)                                                              \
+  do {                                                                             \
+    const hipError_t e_ = (call);                                                  \
+    if (e_ != hipSuccess) return fail(-EIO, "%s: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+
+int validate(const void* ref, const void* dis, int w, int h, ptrdiff_t stride,
+             ptrdiff_t pitch, int nframes, int bpc) {
+  if (!ref || !dis) return fail(-EINVAL, "NULL plane pointer");
+  if (w <= 0 || h <= 0 || w > 32768 || h > 32768)
+    return fail(-EINVAL, "w=%d h=%d outside 1..32768", w, h);
+  if (stride < w) return fail(-EINVAL, "stride %ld < w %d", (long)stride, w);
+  if (bpc < 8 || bpc > 16) return fail(-EINVAL, "bpc %d outside 8..16", bpc);
+  if (nframes <= 0 || nframes > 65535) return fail(-EINVAL, "nframes %d outside 1..65535", nframes);
+  if (pitch < 0) return fail(-EINVAL, "negative frame pitch");
+  if (nframes > 1 && pitch == 0) return fail(-EINVAL, "frame pitch 0 with several frames");
+  return 0;
+}
+
+size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Layout {
+  size_t r1, r2, rn, codd, prefix, plan, pairs, results, units, total;
+};
+
+Layout layout(int F, int h) {
+  const size_t rows = (size_t)F * h;
+  Layout L;
+  size_t o = 0;
+  L.r1 = o; o = up256(o + 2 * rows * 4);
+  L.r2 = o; o = up256(o + 2 * rows * 8);
+  L.rn = o; o = up256(o + rows * 8);
+  L.codd = o; o = up256(o + 2 * rows * 4);
+  L.prefix = o; o = up256(o + 2 * rows * 8);
+  L.plan = o; o = up256(o + 2 * rows);
+  L.pairs = o; o = up256(o + 4 * rows * 8);
+  L.results = o; o = up256(o + (size_t)F * 6 * 8);
+  L.units = o; o = up256(o + (size_t)F * 8 * 8);
+  L.total = o;
+  return L;
+}
+
+int ensure(int dev, size_t bytes, size_t host_bytes) {
+  Arena& a = g_arena[dev];
+  if (a.cap < bytes) {
+    if (a.base) BEF_HIP(hipFree(a.base));
+    a.base = nullptr;
+    a.cap = 0;
+    if (hipMalloc(&a.base, bytes) != hipSuccess) {
+      (void)hipGetLastError();
+      a.base = nullptr;
+      return fail(-ENOMEM, "hipMalloc of %zu bytes of scratch failed", bytes);
+    }
+    a.cap = bytes;
+  }
+  if (a.host_cap < host_bytes) {
+    if (a.host) BEF_HIP(hipHostFree(a.host));
+    a.host = nullptr;
+    a.host_cap = 0;
+    if (hipHostMalloc(&a.host, host_bytes, hipHostMallocDefault) != hipSuccess) {
+      (void)hipGetLastError();
+      a.host = nullptr;
+      return fail(-ENOMEM, "hipHostMalloc of %zu bytes failed", host_bytes);
+    }
+    a.host_cap = host_bytes;
+  }
+  return 0;
+}
+
+int device_of(const void* p, int* dev) {
+  hipPointerAttribute_t at;
+  memset(&at, 0, sizeof at);
+  const hipError_t e = hipPointerGetAttributes(&at, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(-EINVAL, "plane pointer %p is not device memory (%s)", p, hipGetErrorString(e));
+  }
+  if (at.type != hipMemoryTypeDevice && at.type != hipMemoryTypeManaged)
+    return fail(-EINVAL, "plane pointer %p is not device memory", p);
+  if (at.device < 0 || at.device >= kMaxDev) return fail(-EINVAL, "device %d out of range", at.device);
+  *dev = at.device;
+  return 0;
+}
+
+hipEvent_t ev_get() {
+  if (!g_ev_pool.empty()) {
+    hipEvent_t e = g_ev_pool.back();
+    g_ev_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Drain finished event pairs into the totals (blocking on each).
+void ev_collect() {
+  for (EvPair& p : g_ev_live) {
+    float ms = 0.f;
+    if (hipEventSynchronize(p.b) == hipSuccess && hipEventElapsedTime(&ms, p.a, p.b) == hipSuccess) {
+      g_ms[p.kernel] += ms;
+      g_n[p.kernel] += 1;
+    }
+    g_ev_pool.push_back(p.a);
+    g_ev_pool.push_back(p.b);
+  }
+  g_ev_live.clear();
+}
+
+template <class F>
+hipError_t timed(int kernel, hipStream_t st, F launch) {
+  if (!g_timing) return launch();
+  hipEvent_t a = ev_get(), b = ev_get();
+  if (!a || !b) return launch();
+  (void)hipEventRecord(a, st);
+  const hipError_t e = launch();
+  (void)hipEventRecord(b, st);
+  g_ev_live.push_back(EvPair{kernel, a, b});
+  return e;
+}
+
+struct Call {
+  Geometry g;
+  int dev;
+  Layout L;
+  RowArrays ra;
+  double* d_results;
+  uint64_t* d_units;
+  bool need_pairs;
+};
+
+int prepare(Call& c, const void* ref, const void* dis, int w, int h, ptrdiff_t stride,
+            ptrdiff_t pitch, int nframes, int bpc) {
+  int rc = validate(ref, dis, w, h, stride, pitch, nframes, bpc);
+  if (rc) return rc;
+  int dev2 = 0;
+  if ((rc = device_of(ref, &c.dev)) || (rc = device_of(dis, &dev2))) return rc;
+  if (dev2 != c.dev) return fail(-EINVAL, "ref and dis on different devices");
+  BEF_HIP(hipSetDevice(c.dev));
+  const int B = bpc == 8 ? 1 : 2;
+  Geometry& g = c.g;
+  g.ref = ref;
+  g.dis = dis;
+  g.w = w;
+  g.h = h;
+  g.stride = (long)stride;
+  g.pitch = (long)pitch;
+  g.nframes = nframes;
+  g.bpc = bpc;
+  g.vec = ((uintptr_t)ref % 16 == 0) && ((uintptr_t)dis % 16 == 0) &&
+          ((long)stride * B) % 16 == 0 && (nframes == 1 || ((long)pitch * B) % 16 == 0);
+  // Largest possible exact plane sum: every sample at the container's top.
+  const uint64_t tmax = bpc == 8 ? 65025ull : 0xFFFE0000ull;
+  const uint64_t maxsum = (uint64_t)w * (uint64_t)h * tmax;
+  const bool force = (g_dbg & BEF_DBG_FORCE_ROUND) != 0;
+  g.may_round = (maxsum > kTwo53) || force;
+  g.need_odd = g.may_round && bpc != 8;
+  c.need_pairs = g.may_round && (maxsum >= (1ull << 55) || g_dbg != 0);
+  c.L = layout(nframes, h);
+  if ((rc = ensure(c.dev, c.L.total, (size_t)nframes * 8 * 8 + (size_t)nframes * 6 * 8 + 256))) return rc;
+  char* base = (char*)g_arena[c.dev].base;
+  c.ra.r1 = (uint32_t*)(base + c.L.r1);
+  c.ra.r2 = (uint64_t*)(base + c.L.r2);
+  c.ra.rn = (uint64_t*)(base + c.L.rn);
+  c.ra.codd = (uint32_t*)(base + c.L.codd);
+  c.ra.prefix = (uint64_t*)(base + c.L.prefix);
+  c.ra.plan = (int8_t*)(base + c.L.plan);
+  c.ra.pairs = (uint64_t*)(base + c.L.pairs);
+  c.d_results = (double*)(base + c.L.results);
+  c.d_units = (uint64_t*)(base + c.L.units);
+  return 0;
+}
+
+int enqueue(const Call& c, hipStream_t st, double* d_results) {
+  const unsigned dbg = g_dbg;
+  BEF_HIP(timed(0, st, [&] { return launch_rows(c.g, c.ra, st); }));
+  if (c.need_pairs) {
+    BEF_HIP(timed(1, st, [&] { return launch_plan(c.g, c.ra, dbg, st); }));
+    BEF_HIP(timed(2, st, [&] { return launch_pairs(c.g, c.ra, dbg, st); }));
+  }
+  BEF_HIP(timed(3, st, [&] { return launch_walk(c.g, c.ra, d_results, c.d_units, dbg, st); }));
+  return 0;
+}
+
+// Synchronous batch: results and units copied back to the host.
+int run_sync(const void* ref, const void* dis, int w, int h, ptrdiff_t stride, ptrdiff_t pitch,
+             int nframes, int bpc, void* stream, double* moments, double* psnr, uint64_t* units) {
+  Call c;
+  int rc = prepare(c, ref, dis, w, h, stride, pitch, nframes, bpc);
+  if (rc) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  if ((rc = enqueue(c, st, c.d_results))) return rc;
+  double* hres = (double*)g_arena[c.dev].host;
+  uint64_t* hun = (uint64_t*)((char*)hres + up256((size_t)nframes * 6 * 8));
+  BEF_HIP(hipMemcpyAsync(hres, c.d_results, (size_t)nframes * 6 * 8, hipMemcpyDeviceToHost, st));
+  BEF_HIP(hipMemcpyAsync(hun, c.d_units, (size_t)nframes * 8 * 8, hipMemcpyDeviceToHost, st));
+  BEF_HIP(hipStreamSynchronize(st));
+  if (g_timing) ev_collect();
+  for (int f = 0; f < nframes; ++f) {
+    if (moments)
+      for (int k = 0; k < 4; ++k) moments[4 * f + k] = hres[6 * f + k];
+    if (psnr)
+      for (int k = 0; k < 2; ++k) psnr[2 * f + k] = hres[6 * f + 4 + k];
+    if (units)
+      for (int k = 0; k < 8; ++k) units[8 * f + k] = hun[8 * f + k];
+  }
+  return 0;
+}
+
+struct DevGuard {
+  int prev = -1;
+  DevGuard() {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+  }
+  ~DevGuard() {
+    if (prev >= 0) (void)hipSetDevice(prev);
+  }
+};
+
+}  // namespace
+
+extern "C" {
+
+int bef_frames(const void* ref, const void* dis, int w, int h, ptrdiff_t stride,
+               ptrdiff_t frame_pitch, int nframes, int bpc, void* stream, double* moments,
+               double* psnr) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_err.clear();
+  DevGuard dg;
+  return run_sync(ref, dis, w, h, stride, frame_pitch, nframes, bpc, stream, moments, psnr,
+                  nullptr);
+}
+
+int bef_frames_units(const void* ref, const void* dis, int w, int h, ptrdiff_t stride,
+                     ptrdiff_t frame_pitch, int nframes, int bpc, void* stream, uint64_t* units) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_err.clear();
+  if (!units) return fail(-EINVAL, "NULL units");
+  DevGuard dg;
+  return run_sync(ref, dis, w, h, stride, frame_pitch, nframes, bpc, stream, nullptr, nullptr,
+                  units);
+}
+
+int bef_frames_async(const void* ref, const void* dis, int w, int h, ptrdiff_t stride,
+                     ptrdiff_t frame_pitch, int nframes, int bpc, void* stream,
+                     double* dev_results) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_err.clear();
+  if (!dev_results) return fail(-EINVAL, "NULL dev_results");
+  DevGuard dg;
+  Call c;
+  int rc = prepare(c, ref, dis, w, h, stride, frame_pitch, nframes, bpc);
+  if (rc) return rc;
+  return enqueue(c, (hipStream_t)stream, dev_results);
+}
+
+int moment_frame(const void* ref, const void* dis, int w, int h, ptrdiff_t stride, int bpc,
+                 double out[4]) {
+  if (!out) return -EINVAL;
+  return bef_frames(ref, dis, w, h, stride, 0, 1, bpc, nullptr, out, nullptr);
+}
+
+int psnr_noise(const void* ref, const void* dis, int w, int h, ptrdiff_t stride, int bpc,
+               double out[2]) {
+  if (!out) return -EINVAL;
+  return bef_frames(ref, dis, w, h, stride, 0, 1, bpc, nullptr, nullptr, out);
+}
+
+const char* bef_last_error(void) { return g_err.c_str(); }
+
+unsigned bef_debug_set(unsigned flags) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  const unsigned old = g_dbg;
+  g_dbg = flags;
+  return old;
+}
+
+int bef_timing_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_timing = on != 0;
+  return 0;
+}
+
+int bef_timing_read(int kernel, double* ms, long* launches) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (kernel < 0 || kernel > 3 || !ms || !launches) return -EINVAL;
+  ev_collect();
+  *ms = g_ms[kernel];
+  *launches = g_n[kernel];
+  return 0;
+}
+
+void bef_timing_reset(void) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  ev_collect();
+  for (int k = 0; k < 4; ++k) {
+    g_ms[k] = 0;
+    g_n[k] = 0;
+  }
+}
+
+void bef_release(void) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  ev_collect();
+  for (hipEvent_t e : g_ev_pool) (void)hipEventDestroy(e);
+  g_ev_pool.clear();
+  DevGuard dg;
+  for (int d = 0; d < kMaxDev; ++d) {
+    Arena& a = g_arena[d];
+    if (!a.base && !a.host) continue;
+    (void)hipSetDevice(d);
+    if (a.base) (void)hipFree(a.base);
+    if (a.host) (void)hipHostFree(a.host);
+    a = Arena();
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,42 @@
+// bef_internal.h -- types shared by the kernels and the host runtime.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/bef.h"
+
+namespace bef {
+
+// One batch of frames: geometry in samples, device plane pointers.
+struct Geometry {
+  const void* ref;
+  const void* dis;
+  int w, h;
+  long stride;   // samples between rows
+  long pitch;    // samples between frames
+  int nframes;
+  int bpc;
+  int vec;       // rows start on 16-byte boundaries
+  int need_odd;  // count odd squares per row (frames that can pass 2^53)
+  int may_round; // some frame can pass 2^53 units (or forced)
+};
+
+// Device scratch, [plane][frame][row] (plane 0 = ref, 1 = dis) unless noted.
+struct RowArrays {
+  uint32_t* r1;     // sum of codewords
+  uint64_t* r2;     // exact sum of float squares, units
+  uint64_t* rn;     // [frame][row] exact noise sum, units
+  uint32_t* codd;   // number of odd float squares
+  uint64_t* prefix; // exact exclusive prefix of r2
+  int8_t* plan;     // kPlanExact, kPlanCross or a binade
+  uint64_t* pairs;  // [plane][frame][row][2] row pair (binades >= 55)
+};
+
+hipError_t launch_rows(const Geometry& g, const RowArrays& ra, hipStream_t st);
+hipError_t launch_plan(const Geometry& g, const RowArrays& ra, unsigned dbg, hipStream_t st);
+hipError_t launch_pairs(const Geometry& g, const RowArrays& ra, unsigned dbg, hipStream_t st);
+hipError_t launch_walk(const Geometry& g, const RowArrays& ra, double* results, uint64_t* units,
+                       unsigned dbg, hipStream_t st);
+
+}  // namespace bef

@@ -1,0 +1,220 @@
+// ordsum.h -- integer steps of the CPU's double accumulation, in units.
+//
+// Everything here counts in units of 1/s^2 (s = 2^(bpc-8)), where every
+// second-moment or noise term is an integer below 2^32 and every running sum
+// of the CPU's double loop is an integer (ADR-1497, Decision; ADR-1499,
+// Decision, argument step 1).  Shared by the HIP kernels and the host
+// emulation of their algorithm; the CPU oracle never includes it.
+//
+// Facts used (ADR-1497, Decision):
+//  * One CPU step S <- fl64(S + t) is, in units, the exact integer S + t
+//    rounded to 53 significant bits, ties to even.
+//  * Binade e (S in [2^e, 2^(e+1)), e >= 53) has last place u = 2^(e-52);
+//    there S is a multiple of u and adding t moves S by t rounded to a
+//    multiple of u, a tie going to the multiple that leaves S/u even.
+//  * A run of terms added inside one binade is therefore described by two
+//    increments, one for each parity of S/u at its start; two runs compose
+//    associatively, in order (not commutatively).
+//
+// Representation: a "pair" {a0, a1} holds the increment a run applies to S
+// when S/u is even (a0) or odd (a1).  Inside a lane the increments are kept
+// modulo 2^32 (they differ from the run's exact sum by less than 2^31, so
+// the exact sum restores them); across rows they are full 64-bit values.
+//
+// BEF_MUTANT (host test builds only) plants one of the breaks the pages list
+// for this header (ADR-1497, Consequences) so that the host tests can show
+// each one is caught.  0 = none.
+#pragma once
+
+#include <stdint.h>
+
+#ifndef BEF_MUTANT
+#define BEF_MUTANT 0
+#endif
+
+#if defined(__HIPCC__)
+#include <hip/hip_runtime.h>
+#define BEF_HD __host__ __device__ __forceinline__
+#else
+#define BEF_HD static inline
+#endif
+
+namespace bef {
+
+static constexpr uint64_t kTwo53 = 1ull << 53;
+
+// Plan codes for a row or a run.
+static constexpr int kPlanExact = -1;  // every add stays at or below 2^53
+static constexpr int kPlanCross = 0;   // no single binade can be promised
+// any value >= 53: the binade the item is expected to stay in
+
+// floor(log2(s)) for s > 0.
+BEF_HD int binade(uint64_t s) { return 63 - __builtin_clzll(s); }
+
+// The CPU's step S <- fl64(S + t) in units.  S and t below 2^62.
+BEF_HD uint64_t rne53_add(uint64_t s, uint64_t t) {
+  uint64_t n = s + t;
+#if BEF_MUTANT == 5 || BEF_MUTANT == 6
+  return n;  // mutant: term-by-term adds done exactly / no rounding at all
+#else
+  if (n <= kTwo53) return n;
+  const int sh = binade(n) - 52;
+  const uint64_t r = n & ((1ull << sh) - 1);
+  uint64_t q = n - r;
+  const uint64_t half = 1ull << (sh - 1);
+  if (r > half || (r == half && ((q >> sh) & 1))) q += 1ull << sh;
+  return q;
+#endif
+}
+
+// Float32 square of a codeword x, in units: RNE24(x^2) for x < 2^16 (the
+// float multiply of the exact float x rounds exactly that).
+BEF_HD uint32_t fsq_units(uint32_t x) {
+  const float f = (float)x;
+#if defined(__HIP_DEVICE_COMPILE__)
+  return (uint32_t)__fmul_rn(f, f);
+#else
+  volatile float p = f * f;  // a float multiply, never contracted
+  return (uint32_t)p;
+#endif
+}
+
+// One term of a run inside binade e (sh = e - 52, u = 2^sh): v holds S
+// modulo 2^32 (a multiple of u); returns S + t rounded to a multiple of u,
+// ties to the even multiple, modulo 2^32.
+BEF_HD uint32_t traj_step(uint32_t v, uint32_t t, int sh) {
+#if BEF_MUTANT == 4
+  sh = sh - 1;  // mutant: the run's units taken from the wrong binade
+#endif
+  const uint32_t u = 1u << sh;
+  const uint32_t z = v + t;
+#if BEF_MUTANT == 1
+  const uint32_t lsb = 1u - ((z >> sh) & 1u);  // mutant: ties to odd
+#else
+  const uint32_t lsb = (z >> sh) & 1u;
+#endif
+  return (z + ((u >> 1) - 1u) + lsb) & ~(u - 1u);
+}
+
+struct Pair32 {
+  uint32_t a0, a1;
+};
+struct Pair64 {
+  uint64_t a0, a1;
+};
+
+// Identity of composition.
+BEF_HD Pair32 pair32_id() { return Pair32{0u, 0u}; }
+BEF_HD Pair64 pair64_id() { return Pair64{0ull, 0ull}; }
+
+// Run A then run B (both inside binade sh): from parity p, A moves S by
+// A[p], which flips the parity by bit sh of A[p]; B then starts there.
+BEF_HD Pair32 then32(Pair32 A, Pair32 B, int sh) {
+#if BEF_MUTANT == 3
+  Pair32 t = A; A = B; B = t;  // mutant: tree composed in reverse
+#endif
+  Pair32 r;
+#if BEF_MUTANT == 2
+  r.a0 = A.a0 + B.a0;  // mutant: parity ignored
+  r.a1 = A.a1 + B.a1;
+#else
+  r.a0 = A.a0 + (((A.a0 >> sh) & 1u) ? B.a1 : B.a0);
+  r.a1 = A.a1 + (((A.a1 >> sh) & 1u) ? B.a0 : B.a1);
+#endif
+  return r;
+}
+
+BEF_HD Pair64 then64(Pair64 A, Pair64 B, int sh) {
+#if BEF_MUTANT == 3
+  Pair64 t = A; A = B; B = t;  // mutant: tree composed in reverse
+#endif
+  Pair64 r;
+#if BEF_MUTANT == 2
+  r.a0 = A.a0 + B.a0;  // mutant: parity ignored
+  r.a1 = A.a1 + B.a1;
+#else
+  r.a0 = A.a0 + (((A.a0 >> sh) & 1ull) ? B.a1 : B.a0);
+  r.a1 = A.a1 + (((A.a1 >> sh) & 1ull) ? B.a0 : B.a1);
+#endif
+  return r;
+}
+
+// Increments of a run known modulo 2^32 -> full values, given the run's
+// exact sum E (|increment - E| < 2^31 always holds for a run of at most
+// 2^15 terms: each term moves by at most u/2 <= 2^8 from its exact value).
+BEF_HD uint64_t widen(uint32_t d, uint64_t E) {
+  const int32_t adj = (int32_t)(d - (uint32_t)E);
+  return E + (uint64_t)(int64_t)adj;
+}
+BEF_HD Pair64 widen_pair(Pair32 p, uint64_t E) {
+  return Pair64{widen(p.a0, E), widen(p.a1, E)};
+}
+
+// The increment a pair applies to S (S inside the pair's binade).
+BEF_HD uint64_t pick(Pair64 p, uint64_t s, int sh) {
+#if BEF_MUTANT == 2
+  (void)s; (void)sh;
+  return p.a0;  // mutant: parity ignored
+#else
+  return ((s >> sh) & 1ull) ? p.a1 : p.a0;
+#endif
+}
+
+// Try to add an item (row, stretch of rows, or run) whose pair was formed
+// inside binade e.  Accepted only when S is inside binade e and the result
+// stays strictly below 2^(e+1): terms are non-negative, so every partial
+// sum of the item then stayed inside binade e, where the pair's steps are
+// the CPU's steps (the add-chunk acceptance of ADR-1497, Decision, read as
+// this test).  Returns false (S untouched) otherwise.
+BEF_HD bool try_apply(uint64_t* s, Pair64 p, int e) {
+  if (e < 53 || *s < kTwo53 || binade(*s) != e) return false;
+  const uint64_t a = pick(p, *s, e - 52);
+  const uint64_t n = *s + a;
+#if BEF_MUTANT == 6
+  (void)n;
+  return false;
+#else
+  if (n >= (1ull << (e + 1))) return false;
+  *s = n;
+  return true;
+#endif
+}
+
+// Exact add, allowed while the result stays at or below 2^53.
+BEF_HD bool try_exact(uint64_t* s, uint64_t E) {
+  if (*s + E > kTwo53) return false;
+  *s += E;
+  return true;
+}
+
+// Plan of an item from its exact prefix P (sum of everything before it,
+// exactly) and exact sum E, given a bound M on |S_cpu - P| where rounding
+// may already have happened.
+BEF_HD int plan_of(uint64_t P, uint64_t E, uint64_t M) {
+  if (P + E <= kTwo53) return kPlanExact;
+  const uint64_t lo = P > M ? P - M : 0;
+  const uint64_t hi = P + E + M;
+  if (lo < kTwo53) return kPlanCross;
+  const int e = binade(lo);
+  return binade(hi) == e ? e : kPlanCross;
+}
+
+// Pair of a run of terms t[0..n) inside binade e: the two trajectories of S
+// modulo 2^32 from an even and from an odd start.
+template <class Terms>
+BEF_HD Pair32 run_pair(const Terms& terms, int n, int sh) {
+  const uint32_t u = 1u << sh;
+  uint32_t v0 = 0u, v1 = u;
+#if BEF_MUTANT == 7
+  for (int j = n - 1; j >= 0; --j) {  // mutant: run order reversed in a lane
+#else
+  for (int j = 0; j < n; ++j) {
+#endif
+    const uint32_t t = terms(j);
+    v0 = traj_step(v0, t, sh);
+    v1 = traj_step(v1, t, sh);
+  }
+  return Pair32{v0, v1 - u};
+}
+
+}  // namespace bef

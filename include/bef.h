@@ -1,0 +1,147 @@
+/*
+ * bef.h -- C ABI of libbef.so: bit-exact float_moment and float_psnr frame
+ * reductions on MI355X (gfx950).
+ *
+ * What is computed (the CPU loops these calls reproduce bit for bit):
+ *   Each codeword x of a luma plane is read as the float x / s with
+ *   s = 2^(bpc-8) (Research-2081: Float moment Metal exact reduction
+ *   restoration, Finding).
+ *   - float_moment: the first moment of a plane is the sum of those floats,
+ *     added into a double in raster order, over the pixel count; the second
+ *     moment is the sum of their float32 squares, added into a double in
+ *     raster order, over the pixel count (ADR-1497, Context).  Past 2^53
+ *     units (1/s^2) the CPU's running double rounds as it adds; the result
+ *     here is that rounded sum, not the exact one (ADR-1497, Decision).
+ *   - float_psnr: each row's float32 squares of (ref - dis) / s are added
+ *     into a row double, the rows are added into one double in row order
+ *     (the noise), and MSE = noise / (w*h) (ADR-1499, Context and
+ *     Decision).
+ *   Every returned double equals the plain CPU loop's double (==).
+ *
+ * Conventions shared by every entry point:
+ *   ref, dis   DEVICE pointers (e.g. a torch tensor's data_ptr()), owned by
+ *              the caller, read only, not retained after the call.  Samples
+ *              are uint8_t when bpc == 8 and native-endian uint16_t when
+ *              9 <= bpc <= 16.  Values are used as they are (no clipping to
+ *              2^bpc - 1).
+ *   w, h       frame width and height in pixels, 1 <= w <= 32768 (a row
+ *              then adds fewer than 2^47 units: ADR-1499, Decision, argument
+ *              step 1) and 1 <= h <= 32768.
+ *   stride     distance between row starts, in SAMPLES, >= w.  Samples
+ *              between w and stride are never read.
+ *   bpc        bits per sample, 8..16.
+ *   return     0 on success; -EINVAL (-22) for invalid arguments; -ENOMEM
+ *              (-12) when scratch memory cannot be allocated; -EIO (-5) for
+ *              a HIP runtime error (text in bef_last_error()).  Outputs are
+ *              unspecified after an error.
+ *   threads    calls are serialised by a process-wide lock; the library
+ *              owns its device scratch (grown on demand, freed by
+ *              bef_release()).
+ */
+#ifndef BEF_H
+#define BEF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* One frame's four moments, synchronously, on the default stream.
+ * out (HOST, 4 doubles) = {ref_1st, dis_1st, ref_2nd, dis_2nd}
+ * (ADR-1497, Context; output order of the float_moment feature in the
+ * Metal kernel batch digest, Feature scope). */
+int moment_frame(const void *ref, const void *dis, int w, int h,
+                 ptrdiff_t stride, int bpc, double out[4]);
+
+/* One frame's PSNR noise sum and MSE, synchronously, on the default stream.
+ * out (HOST, 2 doubles) = {noise, mse}: noise is the CPU's double row-order
+ * sum at true scale, mse = noise / (w*h) (ADR-1499, Decision). */
+int psnr_noise(const void *ref, const void *dis, int w, int h,
+               ptrdiff_t stride, int bpc, double out[2]);
+
+/* Fused, batched: nframes frames, frame_pitch samples apart (>= h*stride
+ * not required; frames may not overlap in a way that matters since they
+ * are only read).  Each plane is read once for both reductions.
+ * stream: a hipStream_t (NULL = the default stream).  The call enqueues
+ * its kernels on that stream and waits once at the end for the results.
+ * moments (HOST, [nframes][4]) and psnr (HOST, [nframes][2]) may each be
+ * NULL.  1 <= nframes <= 65535. */
+int bef_frames(const void *ref, const void *dis, int w, int h,
+               ptrdiff_t stride, ptrdiff_t frame_pitch, int nframes, int bpc,
+               void *stream, double *moments, double *psnr);
+
+/* As bef_frames, but asynchronous: results go to DEVICE memory
+ * dev_results ([nframes][6] doubles: ref_1st, dis_1st, ref_2nd, dis_2nd,
+ * noise, mse), caller-owned, written when the stream reaches that point.
+ * The call returns after enqueueing; it does not synchronise.  Calls share
+ * the library's per-device scratch: two calls whose GPU work overlaps (on
+ * different streams) race; enqueue them on one stream. */
+int bef_frames_async(const void *ref, const void *dis, int w, int h,
+                     ptrdiff_t stride, ptrdiff_t frame_pitch, int nframes,
+                     int bpc, void *stream, double *dev_results);
+
+/* Diagnostics: per-frame integer sums in units, synchronously.
+ * units (HOST, [nframes][8]) = {S1_ref, S1_dis, S2_ref_exact, S2_dis_exact,
+ * S2_ref_cpu, S2_dis_cpu, noise_exact, bits of the noise double in units}.
+ * The *_cpu values are the CPU's rounded running sums (integers). */
+int bef_frames_units(const void *ref, const void *dis, int w, int h,
+                     ptrdiff_t stride, ptrdiff_t frame_pitch, int nframes,
+                     int bpc, void *stream, uint64_t *units);
+
+/* Thread-local text of the last failure ("" if none). */
+const char *bef_last_error(void);
+
+/* Test hooks (process-wide, default 0).  Every setting must return the
+ * same bits; they only change which path forms them.
+ *   BEF_DBG_PLAN_WRONG  shift every planned binade by one
+ *   BEF_DBG_PLAN_NONE   plan no row: every row past 2^53 goes to its runs
+ *   BEF_DBG_TERMS_ONLY  rows that leave the plan are added term by term
+ *   BEF_DBG_FORCE_ROUND run the ordered-sum kernels on every frame
+ *   BEF_DBG_NO_STRETCH  apply planned rows one by one, not as stretches
+ *   BEF_DBG_NO_CLOSED_FORM  form every planned row's pair from lane runs,
+ *                       also in the binades of 2^53 and 2^54
+ * Returns the previous flags. */
+#define BEF_DBG_PLAN_WRONG 1u
+#define BEF_DBG_PLAN_NONE 2u
+#define BEF_DBG_TERMS_ONLY 4u
+#define BEF_DBG_FORCE_ROUND 8u
+#define BEF_DBG_NO_STRETCH 16u
+#define BEF_DBG_NO_CLOSED_FORM 32u
+unsigned bef_debug_set(unsigned flags);
+
+/* Kernel timing: when enabled, the library records HIP events around each
+ * kernel it launches (on the stream it launches on) and accumulates their
+ * durations.  kernel: 0 row sums, 1 plan, 2 row pairs, 3 walk.
+ * bef_timing_read returns the summed milliseconds and launch count since
+ * the last reset (0 / -EINVAL). */
+int bef_timing_enable(int on);
+int bef_timing_read(int kernel, double *ms, long *launches);
+void bef_timing_reset(void);
+
+/* Free the device scratch of every device. */
+void bef_release(void);
+
+/* ---- host-only test entry points (no GPU needed) ----
+ * They run the steps of the device algorithm (row sums, plan, row pairs by
+ * lane runs and an ordered tree, stretch and row walk with fallbacks to runs
+ * and terms) on the host, with the same integer step functions as the
+ * kernels, on HOST planes.  For tests only. */
+
+/* out = {S1, S2_exact, S2_cpu} of one plane, in units. */
+int bef_host_plane_units(const void *plane, int w, int h, ptrdiff_t stride,
+                         int bpc, unsigned dbg_flags, uint64_t out[3]);
+/* *bits = bit pattern of the noise double in units; *exact = exact sum. */
+int bef_host_noise_units(const void *ref, const void *dis, int w, int h,
+                         ptrdiff_t stride, int bpc, uint64_t *bits,
+                         uint64_t *exact);
+/* The one-term step: fl64(s + t) in units. */
+uint64_t bef_host_rne53_add(uint64_t s, uint64_t t);
+/* Pair of a run of terms inside binade e: out = {inc_even, inc_odd}. */
+int bef_host_run_pair(const uint32_t *terms, int n, int e, uint64_t out[2]);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

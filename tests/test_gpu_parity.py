@@ -1,0 +1,212 @@
+"""HIP path vs the oracle, bit for bit (needs an MI355X).
+
+Every comparison is ``==`` on the 64-bit patterns of the doubles: the
+float_moment and float_psnr outputs must be the CPU loop's own bits
+(ADR-1497, Consequences; ADR-1499, Consequences: tolerance 0).
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+import boundary
+import oracle
+from bit_exact_frame_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def api():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from bit_exact_frame_amd import api as _api
+    _api.bef_debug_set(0)
+    return _api
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.Oracle()
+
+
+def dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def bits(x):
+    return np.asarray(x, dtype=np.float64).view(np.uint64)
+
+
+def expect(orc, ref, dis, bpc, w):
+    return orc.frames(ref, dis, bpc, w=w)
+
+
+def check_batch(api, orc, ref, dis, bpc, w=None, label=""):
+    say(f"[gpu] {label} frames={ref.shape[0]} h={ref.shape[1]} stride={ref.shape[2]} "
+        f"w={w} bpc={bpc}")
+    mom, ps = api.bef_frames(dev(ref), dev(dis), bpc, w=w)
+    emom, eps = expect(orc, ref, dis, bpc, w)
+    bad = np.nonzero((bits(mom) != bits(emom)).any(axis=1) | (bits(ps) != bits(eps)).any(axis=1))[0]
+    assert bad.size == 0, (
+        f"{label}: {bad.size} frames differ; first {bad[0]}: gpu {mom[bad[0]]} {ps[bad[0]]} "
+        f"oracle {emom[bad[0]]} {eps[bad[0]]}")
+    return mom, ps
+
+
+@pytest.mark.parametrize("key", [1, 2, 3, 4, 5])
+def test_workload_parity(api, orc, key):
+    """Every frame of each of the five workloads."""
+    wl = synth.WORKLOADS[key]
+    ref, dis = synth.make_frames(key)
+    check_batch(api, orc, ref, dis, wl.bpc, w=wl.w, label=wl.name)
+
+
+def test_workload_units_past_2_53(api, orc):
+    """On full-range 16-bit 4K noise every plane's second-moment sum passes
+    2^53 and the CPU's rounded sum differs from the exact one (the twins'
+    old exact-once result failed on every such frame: ADR-1497, Context)."""
+    ref, dis = synth.make_frames(4, frames=4)
+    u = api.bef_frames_units(dev(ref), dev(dis), 16)
+    assert (u[:, 2] > (1 << 53)).all() and (u[:, 3] > (1 << 53)).all()
+    assert (u[:, 4] != u[:, 2]).all() and (u[:, 5] != u[:, 3]).all()
+    for f in range(4):
+        acc = orc.moment_sums(ref[f], dis[f], 16)
+        assert int(np.float64(acc[2]) * 65536.0) == int(u[f, 4])
+        assert int(np.float64(acc[3]) * 65536.0) == int(u[f, 5])
+
+
+@pytest.mark.parametrize("kind", boundary.KINDS)
+def test_boundary_frames(api, orc, kind):
+    """The pages' boundary frames, both orientations, with the expected
+    accumulators of tests/golden/boundary_frames.txt."""
+    import oracle_checks
+    gold = oracle_checks.load_golden()[kind]
+    p = boundary.build(kind)
+    z = np.zeros_like(p)
+    ref = np.stack([p, z])
+    dis = np.stack([z, p])
+    check_batch(api, orc, ref, dis, 16, label=f"boundary {kind}")
+    u = api.bef_frames_units(dev(ref), dev(dis), 16)
+    assert int(u[0, 4]) == gold["moment"] and int(u[1, 5]) == gold["moment"]
+    assert int(u[0, 2]) == gold["exact"] and int(u[1, 3]) == gold["exact"]
+    for f in range(2):
+        d = np.array([u[f, 7]], dtype=np.uint64).view(np.float64)[0]
+        assert int(d) == gold["psnr"]
+
+
+SHAPES = [
+    # (w, h, stride, bpc, frames)
+    (1, 1, 1, 8, 1),
+    (1, 1, 1, 16, 2),
+    (7, 3, 7, 10, 3),          # ragged, unaligned rows
+    (64, 2, 64, 16, 2),
+    (100, 9, 100, 16, 2),      # 200-byte rows: not 16-byte aligned
+    (511, 17, 513, 12, 2),     # odd stride
+    (512, 5, 512, 16, 1),
+    (520, 33, 520, 16, 3),     # one vector tail lane group
+    (4100, 3, 4104, 16, 2),    # more than one 512-vector batch per lane
+    (176, 144, 192, 8, 2),     # 8-bit with stride padding
+    (1000, 37, 1000, 8, 2),    # 8-bit ragged
+    (32768, 2, 32768, 16, 1),  # widest row
+]
+
+
+@pytest.mark.parametrize("w,h,stride,bpc,frames", SHAPES)
+def test_shapes(api, orc, w, h, stride, bpc, frames):
+    ref, dis = synth.uniform_planes(w * 7 + h, frames, h, w, stride, bpc)
+    check_batch(api, orc, ref, dis, bpc, w=w, label=f"shape {w}x{h}/{stride}")
+
+
+def test_single_frame_entry_points(api, orc):
+    wl = synth.WORKLOADS[3]
+    ref, dis = synth.make_frames(3, frames=1)
+    r, d = dev(ref[0]), dev(dis[0])
+    m = api.moment_frame(r, d, 12, w=wl.w)
+    p = api.psnr_noise(r, d, 12, w=wl.w)
+    assert bits(m).tolist() == bits(orc.moment_frame(ref[0], dis[0], 12, w=wl.w)).tolist()
+    assert bits(p).tolist() == bits(orc.psnr_noise(ref[0], dis[0], 12, w=wl.w)).tolist()
+
+
+DEBUG = [1, 2, 4, 8, 16, 32, 1 | 16, 2 | 32, 8 | 32]
+
+
+@pytest.mark.parametrize("flags", DEBUG)
+def test_debug_paths_same_bits(api, orc, flags):
+    """Wrong plans, no plans, terms only, forced rounding, no stretches, no
+    closed form: every path must give the CPU's bits (ADR-1497, Decision:
+    any plan, even a wrong one, only changes which increments are used)."""
+    r4, d4 = synth.make_frames(4, frames=2)
+    r5, d5 = synth.make_frames(5, frames=1)
+    b = boundary.build("b53p3")
+    ref = np.concatenate([r4, r5, b[None]])
+    dis = np.concatenate([d4, d5, np.zeros_like(b)[None]])
+    old = api.bef_debug_set(flags)
+    try:
+        check_batch(api, orc, ref, dis, 16, label=f"debug {flags}")
+    finally:
+        api.bef_debug_set(old)
+
+
+def test_past_2_55_8k_noise(api, orc):
+    """16-bit 7680x4320 noise crosses the binades of 2^53, 2^54 and 2^55
+    (ADR-1497, Consequences: 4 of 4 such frames identical)."""
+    ref, dis = synth.uniform_planes(8000, 2, 4320, 7680, 7680, 16)
+    check_batch(api, orc, ref, dis, 16, label="8k noise")
+
+
+def test_past_2_55_4096x2560(api, orc):
+    """A 4096x2560 frame past 2^55 (ADR-1497, Consequences): high content
+    with small codewords mixed in, so that the binade of 2^55 holds ties."""
+    rng = np.random.Generator(np.random.PCG64(2555))
+    ref = rng.integers(40000, 65536, size=(2, 2560, 4096)).astype(np.uint16)
+    mask = rng.random(size=ref.shape) < 0.2
+    ref[mask] = rng.integers(0, 8192, size=int(mask.sum())).astype(np.uint16)
+    dis = rng.integers(0, 65536, size=ref.shape).astype(np.uint16)
+    check_batch(api, orc, ref, dis, 16, label="4096x2560 past 2^55")
+
+
+def test_async_matches_sync(api, orc):
+    import torch
+    ref, dis = synth.make_frames(5, frames=3)
+    r, d = dev(ref), dev(dis)
+    out = torch.zeros((3, 6), dtype=torch.float64, device="cuda")
+    api.bef_frames_async(r, d, 16, out)
+    torch.cuda.synchronize()
+    mom, ps = api.bef_frames(r, d, 16)
+    got = out.cpu().numpy()
+    assert (bits(got[:, :4]) == bits(mom)).all() and (bits(got[:, 4:]) == bits(ps)).all()
+
+
+def test_deterministic(api):
+    ref, dis = synth.make_frames(4, frames=2)
+    r, d = dev(ref), dev(dis)
+    a = api.bef_frames_units(r, d, 16)
+    b = api.bef_frames_units(r, d, 16)
+    assert (a == b).all()
+
+
+def test_bad_arguments(api):
+    import torch
+    r = torch.zeros((4, 4), dtype=torch.uint16, device="cuda")
+    lib = api.lib()
+    out = (api.ctypes.c_double * 4)()
+    p = r.data_ptr()
+    assert lib.moment_frame(p, p, 0, 4, 4, 16, out) == -22
+    assert lib.moment_frame(p, p, 4, 0, 4, 16, out) == -22
+    assert lib.moment_frame(p, p, 4, 4, 3, 16, out) == -22
+    assert lib.moment_frame(p, p, 4, 4, 4, 7, out) == -22
+    assert lib.moment_frame(p, p, 40000, 4, 40000, 16, out) == -22
+    assert lib.moment_frame(None, p, 4, 4, 4, 16, out) == -22
+    host = np.zeros((4, 4), np.uint16)
+    assert lib.moment_frame(host.ctypes.data, host.ctypes.data, 4, 4, 4, 16, out) == -22
+    assert api.last_error() != ""
