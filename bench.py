@@ -72,7 +72,20 @@ def main():
     ap.add_argument("--workload", type=int, default=4)
     ap.add_argument("--ring", type=int, default=0, help="device copies of the batch (0 = auto)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
+                    help="only run device-to-device copies of MIB MiB (HBM counter "
+                         "calibration) and exit")
     args = ap.parse_args()
+    if args.calib_copy:
+        import torch
+        n = args.calib_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes": n, "copies": 5}), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): this path is a "
               "per-frame reduction with no cross-GPU exchange; frames shard with no "

@@ -1,0 +1,238 @@
+"""The C-ABI library on the CPU: exported symbols, the integer step functions,
+and the device algorithm's steps run on the host against the oracle.
+
+No GPU call is made here: libbef.so is loaded (it links the HIP runtime,
+which loads without a GPU) and only its bef_host_* entry points are called.
+Those run the kernels' decomposition serially with the same step header
+(ADR-1497, Decision: the host test runs the kernels' steps against the CPU
+loop, with real and deliberately wrong plans, and checks the one-term step
+against the double add on 400 000 random pairs and every boundary pair).
+"""
+from __future__ import annotations
+
+import ctypes
+import functools
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import boundary
+import checkers
+import oracle
+from bit_exact_frame_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bef.h")
+
+
+@pytest.fixture(scope="module")
+def api():
+    from bit_exact_frame_amd import api as _api
+    return _api
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.Oracle()
+
+
+def test_every_declared_symbol_is_exported():
+    from bit_exact_frame_amd import api
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)
+    decl = sorted({n for n in names if n not in ("defined",)})
+    assert "moment_frame" in decl and "psnr_noise" in decl and "bef_frames" in decl
+    lib = ctypes.CDLL(api.LIB_PATH)
+    missing = [n for n in decl if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+# --------------------------------------------------------------- one step --
+
+def test_one_term_step_against_double_add(api):
+    """fl64(S + t) in units for 400 000 random pairs: S a double holding an
+    integer between 2^50 and 2^58, t below 2^32."""
+    rng = np.random.Generator(np.random.PCG64(53))
+    n = 400_000
+    e = rng.integers(50, 58, size=n)
+    mant = rng.integers(1 << 52, 1 << 53, size=n, dtype=np.int64)
+    s = np.ldexp(mant.astype(np.float64), (e - 52).astype(np.int64))
+    s = np.maximum(np.round(s), 1.0)
+    t = rng.integers(0, 1 << 32, size=n, dtype=np.int64)
+    want = (s + t.astype(np.float64))  # IEEE double add, round to nearest even
+    f = api.lib().bef_host_rne53_add
+    for k in range(n):
+        assert f(int(s[k]), int(t[k])) == int(want[k]), (int(s[k]), int(t[k]))
+
+
+def test_one_term_step_boundary_pairs(api):
+    """Every pair around the binade edges 2^53..2^58 and around the ties."""
+    f = api.bef_host_rne53_add
+    for e in range(53, 59):
+        u = 1 << (e - 52)
+        for base in (1 << e, (1 << e) - u // 2 if u > 1 else (1 << e) - 1, (1 << (e + 1)) - u):
+            base = int(float(base))  # a value the double can hold
+            for t in {0, 1, u // 2 - 1, u // 2, u // 2 + 1, u - 1, u, u + 1, 3 * u // 2,
+                      (1 << 32) - 1}:
+                if t < 0:
+                    continue
+                assert f(base, t) == int(float(base) + float(t)), (e, base, t)
+    for s in range((1 << 53) - 4, (1 << 53) + 1):
+        for t in range(0, 8):
+            assert f(s, t) == int(float(s) + float(t)), (s, t)
+
+
+# --------------------------------------------------------------- run pair --
+
+def brute_pair(terms, e):
+    """Both starting parities of binade e, term by term with the integer
+    IEEE step, from a start well inside the binade."""
+    u = 1 << (e - 52)
+    out = []
+    for p in (0, 1):
+        s0 = (1 << e) + (1 << (e - 2)) + p * u
+        s = s0
+        for t in terms:
+            s = checkers.rne(s + int(t), 53)
+        assert s < (1 << (e + 1))
+        out.append(s - s0)
+    return out
+
+
+def test_run_pair_brute_force(api):
+    rng = np.random.Generator(np.random.PCG64(7))
+    tt = checkers.t_table()
+    for trial in range(400):
+        e = int(rng.integers(53, 60))
+        n = int(rng.integers(0, 80))
+        if trial % 2:
+            x = rng.integers(0, 65536, size=n)
+        else:  # small codewords: dense ties and parity flips
+            x = rng.integers(0, 9000, size=n)
+        terms = tt[x].astype(np.uint32)
+        assert api.bef_host_run_pair(terms, e) == brute_pair(terms.tolist(), e), (e, n)
+
+
+def test_closed_form_premise():
+    """Every float square in units is 0 or 1 modulo 4, and odd exactly when
+    the codeword is odd and below 4096 (exhaustive over 16-bit samples)."""
+    tt = checkers.t_table().astype(np.int64)
+    x = np.arange(65536)
+    assert set(np.unique(tt % 4).tolist()) <= {0, 1}
+    assert ((tt % 2 == 1) == ((x % 2 == 1) & (x < 4096))).all()
+    assert (tt[1::2][: 2048] % 8 == 1).all()  # odd squares are 1 mod 8
+
+
+def test_closed_form_against_runs(api):
+    """Binades of 2^53 and 2^54: the row pair from (exact sum, odd count)
+    equals the pair of the same terms formed by the two-trajectory fold."""
+    rng = np.random.Generator(np.random.PCG64(11))
+    tt = checkers.t_table()
+    for trial in range(300):
+        n = int(rng.integers(0, 3000))
+        x = rng.integers(0, 65536 if trial % 3 else 6000, size=n)
+        terms = tt[x].astype(np.uint32)
+        E = int(terms.astype(np.uint64).sum())
+        c = int((terms & 1).sum())
+        assert api.bef_host_run_pair(terms, 53) == [E - c, E - c + (2 if c else 0)]
+        assert api.bef_host_run_pair(terms, 54) == [E - c, E - c]
+
+
+# ------------------------------------------------- host emulation vs oracle --
+
+@functools.lru_cache(maxsize=None)
+def planes():
+    """(name, plane) cases: both planes of a full-range and a half-range 4K
+    frame, the boundary frames, 8K noise (binades 53..55) and a 4096x2560
+    frame past 2^55 with small codewords mixed in."""
+    out = []
+    r4, d4 = synth.make_frames(4, frames=1)
+    r5, d5 = synth.make_frames(5, frames=1)
+    out += [("c4 ref", r4[0]), ("c4 dis", d4[0]), ("c5 ref", r5[0])]
+    out += [(f"boundary {k}", boundary.build(k)) for k in boundary.KINDS]
+    r8, _ = synth.uniform_planes(8000, 1, 4320, 7680, 7680, 16)
+    out.append(("8k noise", r8[0]))
+    rng = np.random.Generator(np.random.PCG64(2555))
+    p = rng.integers(40000, 65536, size=(2560, 4096)).astype(np.uint16)
+    m = rng.random(size=p.shape) < 0.2
+    p[m] = rng.integers(0, 8192, size=int(m.sum())).astype(np.uint16)
+    out.append(("4096x2560 mixed", p))
+    return out
+
+
+@functools.lru_cache(maxsize=None)
+def oracle_units(name):
+    orc = oracle.Oracle()
+    p = dict(planes())[name]
+    z = np.zeros_like(p)
+    acc = orc.moment_sums(p, z, 16)
+    return int(math.ldexp(acc[0], 8)), int(math.ldexp(acc[2], 16))
+
+
+FLAGS = [0, 1, 2, 8, 16, 32, 1 | 16 | 32, 2 | 32]
+
+
+@pytest.mark.parametrize("flags", FLAGS)
+def test_host_emulation_matches_oracle(api, flags):
+    for name, p in planes():
+        s1, s2 = oracle_units(name)
+        got = api.bef_host_plane_units(p, 16, dbg=flags)
+        assert got[0] == s1, name
+        assert got[1] == int(checkers.terms_moment(p).sum(dtype=np.uint64)), name
+        assert got[2] == s2, (name, flags, got[2], s2)
+
+
+def test_host_emulation_terms_only(api):
+    """Rows that leave the plan go term by term (a slow path: two frames)."""
+    for name, p in planes()[:4]:
+        assert api.bef_host_plane_units(p, 16, dbg=4 | 2)[2] == oracle_units(name)[1], name
+
+
+def test_host_noise_matches_oracle(api, orc):
+    for key in (4, 5):
+        r, d = synth.make_frames(key, frames=1)
+        bits, ex = api.bef_host_noise_units(r[0], d[0], 16)
+        noise = orc.psnr_sum(r[0], d[0], 16)
+        assert np.array([bits], np.uint64).view(np.float64)[0] == math.ldexp(noise, 16)
+        assert ex == checkers.psnr_units(r[0], d[0])[1]
+
+
+# ------------------------------------------------ planted breaks (header) --
+
+MUTANTS = {
+    1: "a tie to the odd value",
+    2: "the parity ignored",
+    3: "the tree composed in reverse",
+    4: "a run's units under the wrong binade",
+    5: "the term-by-term fallback as exact adds",
+    6: "no rounding at all",
+    7: "a lane's run order reversed",
+}
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS))
+def test_header_break_is_caught(tmp_path, mutant):
+    """Each of the breaks the pages list for the step header (ADR-1497,
+    Consequences), plus a reversed run order, makes the host emulation
+    disagree with the oracle on at least one frame."""
+    from bit_exact_frame_amd import build as b
+    so = b.build_host_emu(os.path.join(tmp_path, f"libemu_m{mutant}.so"), mutant)
+    lib = ctypes.CDLL(so)
+    lib.bef_host_plane_units.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_ssize_t, ctypes.c_int, ctypes.c_uint,
+                                         ctypes.POINTER(ctypes.c_uint64)]
+    wrong = []
+    for flags in (0, 32, 2):
+        for name, p in planes():
+            h, w = p.shape
+            out = (ctypes.c_uint64 * 3)()
+            assert lib.bef_host_plane_units(p.ctypes.data, w, h, w, 16, flags, out) == 0
+            if out[2] != oracle_units(name)[1]:
+                wrong.append((flags, name))
+        if wrong:
+            break
+    assert wrong, f"break '{MUTANTS[mutant]}' was not caught"
