@@ -19,6 +19,11 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libbef.so")
 
+# torch first: its HIP runtime (libamdhip64.so.7, same soname as the system
+# one) must be the one libbef.so binds to, so that a single runtime owns the
+# device in the process.
+import torch  # noqa: E402,F401
+
 if not os.path.exists(LIB_PATH):
     raise RuntimeError(
         f"{LIB_PATH} is missing: build it first "

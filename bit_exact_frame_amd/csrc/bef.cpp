@@ -76,7 +76,7 @@ int validate(const void* ref, const void* dis, int w, int h, ptrdiff_t stride,
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t r1, r2, rn, codd, prefix, plan, pairs, results, units, total;
+  size_t r1, r2, rn, codd, plan, pairs, results, units, total;
 };
 
 Layout layout(int F, int h) {
@@ -87,7 +87,6 @@ Layout layout(int F, int h) {
   L.r2 = o; o = up256(o + 2 * rows * 8);
   L.rn = o; o = up256(o + rows * 8);
   L.codd = o; o = up256(o + 2 * rows * 4);
-  L.prefix = o; o = up256(o + 2 * rows * 8);
   L.plan = o; o = up256(o + 2 * rows);
   L.pairs = o; o = up256(o + 4 * rows * 8);
   L.results = o; o = up256(o + (size_t)F * 6 * 8);
@@ -219,7 +218,6 @@ int prepare(Call& c, const void* ref, const void* dis, int w, int h, ptrdiff_t s
   c.ra.r2 = (uint64_t*)(base + c.L.r2);
   c.ra.rn = (uint64_t*)(base + c.L.rn);
   c.ra.codd = (uint32_t*)(base + c.L.codd);
-  c.ra.prefix = (uint64_t*)(base + c.L.prefix);
   c.ra.plan = (int8_t*)(base + c.L.plan);
   c.ra.pairs = (uint64_t*)(base + c.L.pairs);
   c.d_results = (double*)(base + c.L.results);

@@ -28,7 +28,6 @@ struct RowArrays {
   uint64_t* r2;     // exact sum of float squares, units
   uint64_t* rn;     // [frame][row] exact noise sum, units
   uint32_t* codd;   // number of odd float squares
-  uint64_t* prefix; // exact exclusive prefix of r2
   int8_t* plan;     // kPlanExact, kPlanCross or a binade
   uint64_t* pairs;  // [plane][frame][row][2] row pair (binades >= 55)
 };

@@ -88,6 +88,36 @@ __device__ __forceinline__ double wave_sum_f64i(double x) {
   return (a0 + a1) + (a2 + a3);
 }
 
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dpp32<0xB1>(v));
+  v = min(v, dpp32<0x4E>(v));
+  v = min(v, dpp32<0x141>(v));
+  v = min(v, dpp32<0x140>(v));
+  return min(min(rdl32(v, 15), rdl32(v, 31)), min(rdl32(v, 47), rdl32(v, 63)));
+}
+
+// Shift within each 16-lane row by CTRL (row_shr:k); lanes whose source is
+// outside the row, or rows not in ROWMASK, read 0.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ uint64_t dpp64_or0(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, ROWMASK, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, ROWMASK, 0xF, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Inclusive prefix sum over the 64 lanes: row_shr 1, 2, 4, 8 inside each row
+// of 16 lanes, then row_bcast:15 into rows 1 and 3 and row_bcast:31 into
+// rows 2 and 3.
+__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v) {
+  v += dpp64_or0<0x111, 0xF>(v);
+  v += dpp64_or0<0x112, 0xF>(v);
+  v += dpp64_or0<0x114, 0xF>(v);
+  v += dpp64_or0<0x118, 0xF>(v);
+  v += dpp64_or0<0x142, 0xA>(v);
+  v += dpp64_or0<0x143, 0xC>(v);
+  return v;
+}
+
 // ---------------------------------------------------------------------------
 // k_rows: per-row exact sums.
 
@@ -136,7 +166,11 @@ __device__ __forceinline__ void take_sample16(uint32_t a, uint32_t b, Acc16& q) 
   }
 }
 
-constexpr int kRowsU = 8;  // 16-byte loads in flight per lane per plane
+constexpr int kRowsU = 4;  // 16-byte loads in flight per lane per plane
+
+template <bool ODD, bool VEC>
+__device__ __forceinline__ void rows16_body(const Geometry& g, const RowArrays& ra, int i, int f,
+                                            int lane);
 
 template <bool ODD, bool VEC>
 __global__ void __launch_bounds__(256) k_rows16(Geometry g, RowArrays ra) {
@@ -144,6 +178,17 @@ __global__ void __launch_bounds__(256) k_rows16(Geometry g, RowArrays ra) {
   const long task = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (task >= (long)g.nframes * g.h) return;  // whole wave leaves together
   const int i = (int)(task / g.nframes), f = (int)(task % g.nframes);
+  // The odd-square count is only read for rows past 2^53; a row whose
+  // prefix cannot reach 2^53 even with every sample at 65535 skips it.
+  if (ODD && (uint64_t)(i + 1) * (uint64_t)g.w * 0xFFFE0000ull > kTwo53)
+    rows16_body<true, VEC>(g, ra, i, f, lane);
+  else
+    rows16_body<false, VEC>(g, ra, i, f, lane);
+}
+
+template <bool ODD, bool VEC>
+__device__ __forceinline__ void rows16_body(const Geometry& g, const RowArrays& ra, int i, int f,
+                                            int lane) {
   const uint16_t* rr = (const uint16_t*)g.ref + (long)f * g.pitch + (long)i * g.stride;
   const uint16_t* dr = (const uint16_t*)g.dis + (long)f * g.pitch + (long)i * g.stride;
   Acc16 q = {0, 0, 0, 0, 0, 0, 0u, 0u, {0, 0}, {0, 0}};
@@ -250,13 +295,17 @@ __global__ void __launch_bounds__(256) k_rows8(Geometry g, RowArrays ra) {
 }
 
 // ---------------------------------------------------------------------------
-// Block-level helpers (256 threads = 4 waves).  Every thread calls them with
-// the same arguments; results are uniform.
+// Block-level helpers for the plan and walk kernels (kT threads = kWaves
+// waves).  Every thread calls them with the same arguments; results are
+// uniform.
+
+constexpr int kT = 512;
+constexpr int kWaves = kT / 64;
 
 struct BlockScratch {
-  uint64_t w64[8];
+  uint64_t w64[2 * kWaves];
   uint64_t v[4];
-  int iv[4];
+  int iv[kWaves];
 };
 
 __device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, BlockScratch& sm) {
@@ -265,60 +314,89 @@ __device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, BlockScratch& sm) 
   __syncthreads();
   if ((threadIdx.x & 63) == 0) sm.w64[wv] = s;
   __syncthreads();
-  return sm.w64[0] + sm.w64[1] + sm.w64[2] + sm.w64[3];
+  uint64_t t = 0;
+#pragma unroll
+  for (int k = 0; k < kWaves; ++k) t += sm.w64[k];
+  return t;
 }
 
+// Minimum of non-negative ints.
 __device__ __forceinline__ int block_min_int(int v, BlockScratch& sm) {
-  for (int off = 32; off >= 1; off >>= 1) v = min(v, __shfl_xor(v, off));
+  v = (int)wave_min_u32((uint32_t)v);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) sm.iv[threadIdx.x >> 6] = v;
   __syncthreads();
-  return min(min(sm.iv[0], sm.iv[1]), min(sm.iv[2], sm.iv[3]));
+  int m = sm.iv[0];
+#pragma unroll
+  for (int k = 1; k < kWaves; ++k) m = min(m, sm.iv[k]);
+  return m;
 }
 
 // Exclusive prefix of v over the block's threads in order; *total = sum.
 __device__ __forceinline__ uint64_t block_excl_scan_u64(uint64_t v, uint64_t* total,
                                                         BlockScratch& sm) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  uint64_t inc = v;
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint64_t o = __shfl_up(inc, off);
-    if (lane >= off) inc += o;
-  }
+  const uint64_t inc = wave_incl_scan_u64(v);
   __syncthreads();
   if (lane == 63) sm.w64[wv] = inc;
   __syncthreads();
-  uint64_t before = 0;
-  for (int k = 0; k < wv; ++k) before += sm.w64[k];
-  *total = sm.w64[0] + sm.w64[1] + sm.w64[2] + sm.w64[3];
+  uint64_t before = 0, all = 0;
+#pragma unroll
+  for (int k = 0; k < kWaves; ++k) {
+    const uint64_t x = sm.w64[k];
+    before += k < wv ? x : 0;
+    all += x;
+  }
+  *total = all;
   return before + inc - v;
 }
 
-// Ordered composition of one pair per thread (thread 0 first): a
-// shuffle-down tree inside each wave, then (w0 then w1) then (w2 then w3).
+// Ordered composition of one pair per lane (lane 0 first) inside a wave:
+// lane l takes lane l+1 (quad_perm xor 1), l+2 (quad_perm xor 2), l+4
+// (row_shl:4), l+8 (row_shl:8); the four 16-lane row composites are read
+// into scalars and joined in order.  Uniform result.
+__device__ __forceinline__ Pair64 wave_then(Pair64 p, int sh) {
+  const int lane = threadIdx.x & 63;
+  Pair64 o;
+  o = Pair64{dpp64<0xB1>(p.a0), dpp64<0xB1>(p.a1)};
+  if (!(lane & 1)) p = then64(p, o, sh);
+  o = Pair64{dpp64<0x4E>(p.a0), dpp64<0x4E>(p.a1)};
+  if (!(lane & 3)) p = then64(p, o, sh);
+  o = Pair64{dpp64<0x104>(p.a0), dpp64<0x104>(p.a1)};
+  if (!(lane & 7)) p = then64(p, o, sh);
+  o = Pair64{dpp64<0x108>(p.a0), dpp64<0x108>(p.a1)};
+  if (!(lane & 15)) p = then64(p, o, sh);
+  const Pair64 r0 = {rdl64(p.a0, 0), rdl64(p.a1, 0)}, r1 = {rdl64(p.a0, 16), rdl64(p.a1, 16)};
+  const Pair64 r2 = {rdl64(p.a0, 32), rdl64(p.a1, 32)}, r3 = {rdl64(p.a0, 48), rdl64(p.a1, 48)};
+  return then64(then64(r0, r1, sh), then64(r2, r3, sh), sh);
+}
+
+// Block version: the waves' composites joined by an ordered tree.
 __device__ __forceinline__ Pair64 block_then(Pair64 p, int sh, BlockScratch& sm) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  for (int off = 1; off < 64; off <<= 1) {
-    Pair64 o;
-    o.a0 = __shfl_down(p.a0, off);
-    o.a1 = __shfl_down(p.a1, off);
-    if ((lane & (2 * off - 1)) == 0) p = then64(p, o, sh);
+  const Pair64 w = wave_then(p, sh);
+  const int wv = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) {
+    sm.w64[2 * wv] = w.a0;
+    sm.w64[2 * wv + 1] = w.a1;
   }
   __syncthreads();
-  if (lane == 0) {
-    sm.w64[2 * wv] = p.a0;
-    sm.w64[2 * wv + 1] = p.a1;
-  }
-  __syncthreads();
-  const Pair64 w0 = {sm.w64[0], sm.w64[1]}, w1 = {sm.w64[2], sm.w64[3]};
-  const Pair64 w2 = {sm.w64[4], sm.w64[5]}, w3 = {sm.w64[6], sm.w64[7]};
-  return then64(then64(w0, w1, sh), then64(w2, w3, sh), sh);
+  Pair64 q[kWaves];
+#pragma unroll
+  for (int k = 0; k < kWaves; ++k) q[k] = Pair64{sm.w64[2 * k], sm.w64[2 * k + 1]};
+#pragma unroll
+  for (int off = 1; off < kWaves; off <<= 1)
+#pragma unroll
+    for (int k = 0; k + off < kWaves; k += 2 * off) q[k] = then64(q[k], q[k + off], sh);
+  return q[0];
 }
 
 // ---------------------------------------------------------------------------
-// Plan (shared by k_plan and k_walk): exact exclusive prefix of the rows'
-// second-moment sums and each row's plan.  Writes P[], plan[]; returns the
-// plane's exact total.
+// Plan (shared by k_plan and k_walk), one pass: thread t owns a contiguous
+// chunk of rows; one block scan of the chunk totals gives every row's exact
+// prefix, hence its plan.  Also returns the first row that is not planned
+// exact and the exact sum before it (every add before it stays at or below
+// 2^53, so that sum is the CPU's running sum there).
 
 __device__ int debug_plan(int e, int i, unsigned dbg) {
   if (e >= 53 && (dbg & BEF_DBG_PLAN_NONE)) return kPlanCross;
@@ -326,34 +404,95 @@ __device__ int debug_plan(int e, int i, unsigned dbg) {
   return e;
 }
 
-__device__ uint64_t plan_plane(const uint64_t* R, uint64_t* P, int8_t* plan, int w, int h,
-                               unsigned dbg, BlockScratch& sm) {
-  uint64_t carry = 0;
-  for (int base = 0; base < h; base += 256) {
-    const int i = base + threadIdx.x;
-    const uint64_t r = i < h ? R[i] : 0;
-    uint64_t tot;
-    const uint64_t ex = block_excl_scan_u64(r, &tot, sm);
-    if (i < h) P[i] = carry + ex;
-    carry += tot;
+constexpr int kChunk = 2176;  // rows held in LDS by the walk
+
+struct RowLds {
+  uint64_t R[kChunk];
+  uint16_t C[kChunk];
+  int8_t plan[kChunk];
+};
+
+struct PlanInfo {
+  uint64_t E;   // exact plane sum
+  int i0;       // first row not planned exact (h if none)
+  uint64_t P0;  // exact sum of rows [0, i0)
+};
+
+// When cl is given and h <= kChunk, the rows' sums, odd counts and plans
+// are left in LDS, indexed by row, and the global plan array is not
+// written; *s1 (if given) receives the plane's first-moment sum from r1.
+__device__ PlanInfo plan_plane(const uint64_t* R, int8_t* plan, int w, int h, unsigned dbg,
+                               BlockScratch& sm, RowLds* cl = nullptr,
+                               const uint32_t* C = nullptr, const uint32_t* r1 = nullptr,
+                               uint64_t* s1 = nullptr) {
+  const int c = (h + kT - 1) / kT;
+  const int a = min((int)threadIdx.x * c, h), b = min(a + c, h);
+  const bool keep = cl != nullptr && h <= kChunk;
+  uint64_t loc = 0;
+  if (keep) {
+    // every load issued before the first is used: one memory round trip
+    constexpr int U = (kChunk + kT - 1) / kT;
+    uint64_t rv[U];
+    uint32_t cv[U], sv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = threadIdx.x + u * kT;
+      rv[u] = i < h ? R[i] : 0;
+      cv[u] = i < h ? C[i] : 0;
+      sv[u] = (i < h && r1) ? r1[i] : 0;
+    }
+    uint64_t s1l = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = threadIdx.x + u * kT;
+      if (i < h) {
+        cl->R[i] = rv[u];
+        cl->C[i] = (uint16_t)cv[u];
+      }
+      s1l += sv[u];
+    }
+    if (s1) *s1 = block_sum_u64(s1l, sm);  // also the barrier before reading cl
+    else __syncthreads();
+    for (int i = a; i < b; ++i) loc += cl->R[i];
+  } else {
+    uint64_t s1l = 0;
+    if (r1)
+      for (int i = threadIdx.x; i < h; i += kT) s1l += r1[i];
+    if (s1) *s1 = block_sum_u64(s1l, sm);
+    for (int i = a; i < b; ++i) loc += R[i];
   }
-  const uint64_t E = carry;
+  uint64_t E;
+  uint64_t p = block_excl_scan_u64(loc, &E, sm);
   const uint64_t M = E > kTwo53 ? ((uint64_t)w * (uint64_t)h) << (binade(E) - 53) : 0;
+  int first = h;
+  uint64_t pfirst = 0;
+  for (int i = a; i < b; ++i) {
+    const uint64_t r = keep ? cl->R[i] : R[i];
+    const int e = debug_plan(plan_of(p, r, M), i, dbg);
+    if (keep) cl->plan[i] = (int8_t)e;
+    else plan[i] = (int8_t)e;
+    if (e != kPlanExact && first == h) {
+      first = i;
+      pfirst = p;
+    }
+    p += r;
+  }
+  const int i0 = block_min_int(first, sm);
   __syncthreads();
-  for (int i = threadIdx.x; i < h; i += 256) plan[i] = (int8_t)debug_plan(plan_of(P[i], R[i], M), i, dbg);
+  if (i0 < h && first == i0) sm.v[0] = pfirst;
   __syncthreads();
-  return E;
+  return PlanInfo{E, i0, i0 < h ? sm.v[0] : E};
 }
 
 __device__ __forceinline__ bool may_round(uint64_t E, unsigned dbg) {
   return E > kTwo53 || (dbg & BEF_DBG_FORCE_ROUND);
 }
 
-__global__ void __launch_bounds__(256) k_plan(Geometry g, RowArrays ra, unsigned dbg) {
+__global__ void __launch_bounds__(kT) k_plan(Geometry g, RowArrays ra, unsigned dbg) {
   __shared__ BlockScratch sm;
   const int f = blockIdx.x >> 1, pl = blockIdx.x & 1;
   const long off = (long)(pl * g.nframes + f) * g.h;
-  plan_plane(ra.r2 + off, ra.prefix + off, ra.plan + off, g.w, g.h, dbg, sm);
+  plan_plane(ra.r2 + off, ra.plan + off, g.w, g.h, dbg, sm);
 }
 
 // ---------------------------------------------------------------------------
@@ -396,208 +535,607 @@ __global__ void __launch_bounds__(256) k_pairs(Geometry g, RowArrays ra, unsigne
 
 // ---------------------------------------------------------------------------
 // k_walk.
+//
+// The walk is latency-bound: one block per (frame, plane) and a short
+// sequential path.  Items (the rows of a plane, or the runs of a row that
+// leaves its plan) are grouped into segments of equal plan by one pass that
+// also records the exact prefix of the item sums and of the odd-square
+// counts at every segment start.  A segment planned exact adds its sum; a
+// segment planned in the binade of 2^53 or 2^54 adds its closed-form pair
+// (below), from the two prefix differences alone; other binades compose
+// their items' pairs with an ordered tree.  A segment that does not fit goes
+// item by item: a row to its runs, a run to its terms.
+//
+// Closed form: every float square in units is 0 or 1 modulo 4 (an odd
+// square is 1 mod 8; an even one is a multiple of 4; squares past 2^24 are
+// rounded to multiples of 2 whose significand is even, or coarser).  In the
+// binade of 2^53 (last place 2) an even term is exact and leaves S/2's
+// parity alone, and an odd term is a tie: from S = 0 mod 4 it goes down by
+// 1, from S = 2 mod 4 up by 1, and leaves S = 0 mod 4.  So a stretch of
+// terms with exact sum E and c odd terms adds E - c from an even start and
+// E - c + 2 from an odd one (E from both when c = 0).  In the binade of 2^54
+// (last place 4) an odd term is 1 mod 4, below half a place: it goes down by
+// 1 whatever the parity, so both starts add E - c.
 
-struct RunLds {
-  uint64_t E[256];
-  uint64_t A0[256], A1[256], B0[256], B1[256];
-  int8_t plan[256];
+constexpr int kStage = 4096;  // samples of one row staged in LDS by a fallback
+constexpr int kMaxSeg = 64;   // segments a walk handles as segments
+
+__device__ __forceinline__ Pair64 closed_pair(uint64_t E, uint64_t c, int e) {
+  const uint64_t a0 = E - c;
+  return Pair64{a0, (e == 53 && c > 0) ? a0 + 2 : a0};
+}
+
+struct Seg {
+  uint64_t P;   // exact sum of the items before the segment
+  uint64_t PC;  // odd squares before the segment
+  int start;
+  int plan;
 };
 
-template <typename T>
+// One run per thread of a fallback row: exact sum, odd count, plan, and the
+// pairs under the binade S is in (A) and the next one (B) as signed offsets
+// from the exact sum (a run of at most 32 terms moves less than 2^31).
+struct RunLds {
+  uint64_t E[kT];
+  uint32_t C[kT];
+  int32_t A0[kT], A1[kT], B0[kT], B1[kT];
+  int8_t plan[kT];
+};
+
+// Two-value exclusive block scan (one set of barriers).
+__device__ __forceinline__ void block_excl_scan2(uint64_t v, uint64_t u, uint64_t* ev,
+                                                 uint64_t* eu, uint64_t* tv, uint64_t* tu,
+                                                 BlockScratch& sm) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const uint64_t iv = wave_incl_scan_u64(v), iu = wave_incl_scan_u64(u);
+  __syncthreads();
+  if (lane == 63) {
+    sm.w64[2 * wv] = iv;
+    sm.w64[2 * wv + 1] = iu;
+  }
+  __syncthreads();
+  uint64_t bv = 0, bu = 0, av = 0, au = 0;
+  for (int k = 0; k < kWaves; ++k) {
+    const uint64_t x = sm.w64[2 * k], y = sm.w64[2 * k + 1];
+    if (k < wv) {
+      bv += x;
+      bu += y;
+    }
+    av += x;
+    au += y;
+  }
+  *ev = bv + iv - v;
+  *eu = bu + iu - u;
+  *tv = av;
+  *tu = au;
+}
+
+// Segment table of items [0, n) whose sums E, odd counts C and plans are in
+// LDS (plan already final and visible).  Thread t owns items
+// [t*c, t*c + c).  Returns the number of segments; the table holds
+// min(n_seg, kMaxSeg) entries plus a closing entry at n when it fits.
+template <class EAt, class CAt, class PlanAt>
+__device__ __forceinline__ int build_segments(int n, EAt e_at, CAt c_at, PlanAt plan_at,
+                                              Seg* tab, BlockScratch& sm) {
+  const int c = (n + kT - 1) / kT;
+  const int a = min((int)threadIdx.x * c, n), b = min(a + c, n);
+  uint64_t le = 0, lc = 0, ln = 0;
+  for (int k = a; k < b; ++k) {
+    le += e_at(k);
+    lc += c_at(k);
+    ln += (k == 0 || plan_at(k) != plan_at(k - 1)) ? 1 : 0;
+  }
+  uint64_t pe, pcn, te, tcn;
+  // odd counts (< 2^31) and boundary counts (< 2^31) share one 64-bit scan
+  block_excl_scan2(le, (lc << 32) | ln, &pe, &pcn, &te, &tcn, sm);
+  uint64_t P = pe, PC = pcn >> 32;
+  int idx = (int)(pcn & 0xFFFFFFFFu);
+  for (int k = a; k < b; ++k) {
+    if (k == 0 || plan_at(k) != plan_at(k - 1)) {
+      if (idx < kMaxSeg) tab[idx] = Seg{P, PC, k, plan_at(k)};
+      ++idx;
+    }
+    P += e_at(k);
+    PC += c_at(k);
+  }
+  const int nseg = (int)(tcn & 0xFFFFFFFFu);
+  if (threadIdx.x == 0 && nseg <= kMaxSeg) tab[nseg] = Seg{te, tcn >> 32, n, 0};
+  __syncthreads();
+  return nseg;
+}
+
+template <class PairAt>
+__device__ __forceinline__ Pair64 compose_items(int a, int b, int sh, PairAt pair_at,
+                                                BlockScratch& sm) {
+  const int c = (b - a + kT - 1) / kT;
+  Pair64 acc = pair64_id();
+  const int k0 = a + threadIdx.x * c;
+  for (int k = k0; k < k0 + c && k < b; ++k) acc = then64(acc, pair_at(k), sh);
+  return block_then(acc, sh, sm);
+}
+
 struct Walker {
-  const T* row0;  // plane of this frame
+  const void* plane;  // this frame's plane
   long stride;
-  int w, h;
-  const uint64_t* R;
+  int w, h, bpc8;
+  const uint64_t* R;  // global, for planes taller than one chunk
   const uint32_t* C;
-  const uint64_t* pairs;
   const int8_t* plan;
+  const uint64_t* pairs;
   unsigned dbg;
   BlockScratch& sm;
-  RunLds& rl;
+  RowLds& rows;
+  RunLds& runs;
+  Seg* rseg;
+  Seg* useg;
+  uint16_t* rowbuf;
+  int* staged;
 
-  __device__ uint32_t term(int i, int j) const { return fsq_units(row0[(long)i * stride + j]); }
-
-  // Pair of row i under its plan e (e >= 53): closed form in the binades of
-  // 2^53 and 2^54, else from k_pairs.
-  //
-  // Closed form: every float square in units is 0 or 1 modulo 4 (an odd
-  // square is 1 mod 8; an even one is a multiple of 4; squares past 2^24
-  // are rounded to multiples of 2 whose significand is even, or coarser).
-  // In the binade of 2^53 (last place 2) an even term is exact and leaves
-  // S/2's parity alone, and an odd term is a tie: from S = 0 mod 4 it goes
-  // down by 1, from S = 2 mod 4 up by 1, and leaves S = 0 mod 4.  So with c
-  // odd terms the row adds R - c from an even start and R - c + 2 from an
-  // odd one (R from both when c = 0).  In the binade of 2^54 (last place 4)
-  // an odd term is 1 mod 4, below half a place: it goes down by 1 whatever
-  // the parity, so both starts add R - c.
-  __device__ Pair64 row_pair(int i, int e) const {
-    if (e <= 54 && !(dbg & BEF_DBG_NO_CLOSED_FORM)) {
-      const uint64_t c = C[i];
-      const uint64_t a0 = R[i] - c;
-      const uint64_t a1 = (e == 53 && c > 0) ? a0 + 2 : a0;
-      return Pair64{a0, a1};
-    }
-    return Pair64{pairs[2 * (long)i], pairs[2 * (long)i + 1]};
+  __device__ uint32_t sample(long k) const {
+    return bpc8 ? ((const uint8_t*)plane)[k] : ((const uint16_t*)plane)[k];
   }
-
+  __device__ uint32_t term(int i, int j) const {
+    if (w <= kStage) return fsq_units(rowbuf[j]);
+    return fsq_units(sample((long)i * stride + j));
+  }
   __device__ uint64_t terms(uint64_t s, int i, int j0, int j1) const {
     for (int j = j0; j < j1; ++j) s = rne53_add(s, term(i, j));
     return s;
   }
 
-  // First item index >= i+1 whose plan differs from e (n if none).
-  template <class PlanAt>
-  __device__ int segment_end(int i, int n, int e, PlanAt plan_at) const {
-    for (int base = i + 1; base < n; base += 256) {
-      const int k = base + threadIdx.x;
-      const int hit = (k < n && plan_at(k) != e) ? k : n;
-      const int m = block_min_int(hit, sm);
-      if (m < n) return m;
+  // Pair of row k of the chunk starting at row c0, under its plan e.
+  __device__ Pair64 row_pair(int c0, int k, int e) const {
+    if (e <= 54 && !(dbg & BEF_DBG_NO_CLOSED_FORM)) return closed_pair(rows.R[k], rows.C[k], e);
+    const long i = c0 + k;
+    return Pair64{pairs[2 * i], pairs[2 * i + 1]};
+  }
+  __device__ Pair64 run_pair_at(int k, int e, int eA) const {
+    const uint64_t E = runs.E[k];
+    if (e == eA) return Pair64{E + (uint64_t)(int64_t)runs.A0[k], E + (uint64_t)(int64_t)runs.A1[k]};
+    return Pair64{E + (uint64_t)(int64_t)runs.B0[k], E + (uint64_t)(int64_t)runs.B1[k]};
+  }
+
+  // A row the plan does not fit, from S: kT runs of ceil(w/kT) terms, each
+  // with its pairs under the binade S is in and the next one, planned from
+  // their own exact prefix; a run that fits neither is added term by term.
+  __device__ uint64_t fallback_row(uint64_t s, int i) const {
+    if (w <= kStage && *staged != i) {
+      __syncthreads();
+      const long base = (long)i * stride;
+      for (int j = threadIdx.x; j < w; j += kT) rowbuf[j] = (uint16_t)sample(base + j);
+      if (threadIdx.x == 0) *staged = i;
+      __syncthreads();
     }
-    return n;
+    if (dbg & BEF_DBG_TERMS_ONLY) return terms(s, i, 0, w);
+    const int eA = s < kTwo53 ? 53 : binade(s);
+    const int eB = eA + 1;
+    const int L = (w + kT - 1) / kT;
+    const int t = threadIdx.x;
+    const int j0 = min(t * L, w), j1 = min(j0 + L, w);
+    uint64_t E = 0;
+    uint32_t c = 0;
+    for (int j = j0; j < j1; ++j) {
+      const uint32_t x = term(i, j);
+      E += x;
+      c += x & 1u;
+    }
+    int32_t d[4];
+    for (int q = 0; q < 2; ++q) {
+      const int e = q ? eB : eA;
+      if (e <= 54 && !(dbg & BEF_DBG_NO_CLOSED_FORM)) {
+        const Pair64 p = closed_pair(E, c, e);
+        d[2 * q] = (int32_t)(p.a0 - E);
+        d[2 * q + 1] = (int32_t)(p.a1 - E);
+      } else {
+        const Pair32 p = run_pair([&](int j) { return term(i, j0 + j); }, j1 - j0, e - 52);
+        d[2 * q] = (int32_t)(p.a0 - (uint32_t)E);
+        d[2 * q + 1] = (int32_t)(p.a1 - (uint32_t)E);
+      }
+    }
+    uint64_t q, tot;
+    q = block_excl_scan_u64(E, &tot, sm);
+    const uint64_t Mr = (uint64_t)w << (eB - 53);
+    runs.E[t] = E;
+    runs.C[t] = c;
+    runs.A0[t] = d[0];
+    runs.A1[t] = d[1];
+    runs.B0[t] = d[2];
+    runs.B1[t] = d[3];
+    runs.plan[t] = (int8_t)plan_of(s + q, E, Mr);
+    __syncthreads();
+    const int nseg = build_segments(
+        kT, [&](int k) { return runs.E[k]; }, [&](int k) { return (uint64_t)runs.C[k]; },
+        [&](int k) { return (int)runs.plan[k]; }, useg, sm);
+    auto step = [&](uint64_t s2, int k) {
+      if (try_exact(&s2, runs.E[k])) return s2;
+      if (try_apply(&s2, run_pair_at(k, eA, eA), eA)) return s2;
+      if (try_apply(&s2, run_pair_at(k, eB, eA), eB)) return s2;
+      const int a = min(k * L, w);
+      return terms(s2, i, a, min(a + L, w));
+    };
+    if (nseg > kMaxSeg) {
+      for (int k = 0; k < kT; ++k) s = step(s, k);
+    } else {
+      for (int g = 0; g < nseg; ++g) {
+        const Seg A = useg[g], B = useg[g + 1];
+        const int e = A.plan;
+        bool done = false;
+        if (e == kPlanExact) {
+          done = try_exact(&s, B.P - A.P);
+        } else if (e >= 53 && !(dbg & BEF_DBG_NO_STRETCH)) {
+          const Pair64 p = (e <= 54 && !(dbg & BEF_DBG_NO_CLOSED_FORM))
+                               ? closed_pair(B.P - A.P, B.PC - A.PC, e)
+                               : compose_items(A.start, B.start, e - 52,
+                                               [&](int k) { return run_pair_at(k, e, eA); }, sm);
+          done = try_apply(&s, p, e);
+        }
+        if (!done)
+          for (int k = A.start; k < B.start; ++k) s = step(s, k);
+      }
+    }
+    __syncthreads();  // the run arrays are reused by the next fallback
+    return s;
   }
 
-  // Items [a, b): each thread folds a contiguous chunk, then block tree.
-  template <class PairAt>
-  __device__ Pair64 compose_range(int a, int b, int sh, PairAt pair_at) const {
-    const int c = (b - a + 255) >> 8;
-    Pair64 acc = pair64_id();
-    const int k0 = a + threadIdx.x * c;
-    for (int k = k0; k < k0 + c && k < b; ++k) acc = then64(acc, pair_at(k), sh);
-    return block_then(acc, sh, sm);
-  }
-
-  template <class EAt>
-  __device__ uint64_t sum_range(int a, int b, EAt e_at) const {
-    uint64_t v = 0;
-    for (int k = a + threadIdx.x; k < b; k += 256) v += e_at(k);
-    return block_sum_u64(v, sm);
-  }
-
-  // The walk over n items (rows or runs): stretches first, item steps when
-  // a stretch does not fit.
-  template <class PlanAt, class EAt, class PairAt, class Step>
-  __device__ uint64_t walk(uint64_t s, int n, PlanAt plan_at, EAt e_at, PairAt pair_at,
-                           Step step) const {
-    int i = 0;
-    while (i < n) {
-      const int e = plan_at(i);
-      const int j = segment_end(i, n, e, plan_at);
+  // Rows [0, n) of the chunk held in `rows` (first row c0), from s.
+  __device__ uint64_t walk_chunk(int c0, int n, uint64_t s) const {
+    const int nseg = build_segments(
+        n, [&](int k) { return rows.R[k]; }, [&](int k) { return (uint64_t)rows.C[k]; },
+        [&](int k) { return (int)rows.plan[k]; }, rseg, sm);
+    auto step = [&](uint64_t s2, int k) {
+      if (try_exact(&s2, rows.R[k])) return s2;
+      const int e = rows.plan[k];
+      if (e >= 53 && try_apply(&s2, row_pair(c0, k, e), e)) return s2;
+      return fallback_row(s2, c0 + k);
+    };
+    if (nseg > kMaxSeg) {
+      for (int k = 0; k < n; ++k) s = step(s, k);
+      return s;
+    }
+    for (int g = 0; g < nseg; ++g) {
+      const Seg A = rseg[g], B = rseg[g + 1];
+      const int e = A.plan;
       bool done = false;
       if (e == kPlanExact) {
-        done = try_exact(&s, sum_range(i, j, e_at));
+        done = try_exact(&s, B.P - A.P);
       } else if (e >= 53 && !(dbg & BEF_DBG_NO_STRETCH)) {
-        done = try_apply(&s, compose_range(i, j, e - 52, pair_at), e);
+        const Pair64 p = (e <= 54 && !(dbg & BEF_DBG_NO_CLOSED_FORM))
+                             ? closed_pair(B.P - A.P, B.PC - A.PC, e)
+                             : compose_items(A.start, B.start, e - 52,
+                                             [&](int k) { return row_pair(c0, k, e); }, sm);
+        done = try_apply(&s, p, e);
       }
       if (!done)
-        for (int k = i; k < j; ++k) s = step(s, k);
-      i = j;
+        for (int k = A.start; k < B.start; ++k) s = step(s, k);
     }
     return s;
   }
 
-  // A row the plan does not fit, from S: 256 runs of ceil(w/256) terms with
-  // their pairs under the binade S is in and the next one, planned from their
-  // own exact prefix; a run that fits neither is added term by term.
-  __device__ uint64_t fallback_row(uint64_t s, int i) const {
-    if (dbg & BEF_DBG_TERMS_ONLY) return terms(s, i, 0, w);
-    const int eA = s < kTwo53 ? 53 : binade(s);
-    const int eB = eA + 1;
-    const int L = (w + 255) >> 8;
-    const int t = threadIdx.x;
-    const int j0 = min(t * L, w), j1 = min(j0 + L, w);
-    uint64_t E = 0;
-    for (int j = j0; j < j1; ++j) E += term(i, j);
-    auto tt = [&](int j) { return term(i, j0 + j); };
-    const Pair64 pA = widen_pair(run_pair(tt, j1 - j0, eA - 52), E);
-    const Pair64 pB = widen_pair(run_pair(tt, j1 - j0, eB - 52), E);
-    uint64_t tot;
-    const uint64_t q = s + block_excl_scan_u64(E, &tot, sm);
-    const uint64_t Mr = (uint64_t)w << (eB - 53);
-    __syncthreads();
-    rl.E[t] = E;
-    rl.A0[t] = pA.a0;
-    rl.A1[t] = pA.a1;
-    rl.B0[t] = pB.a0;
-    rl.B1[t] = pB.a1;
-    rl.plan[t] = (int8_t)plan_of(q, E, Mr);
-    __syncthreads();
-    const RunLds& r = rl;
-    const uint64_t out = walk(
-        s, 256, [&](int k) { return (int)r.plan[k]; }, [&](int k) { return r.E[k]; },
-        [&](int k) {
-          return r.plan[k] == eA ? Pair64{r.A0[k], r.A1[k]} : Pair64{r.B0[k], r.B1[k]};
-        },
-        [&](uint64_t s2, int k) {
-          if (try_exact(&s2, r.E[k])) return s2;
-          if (try_apply(&s2, Pair64{r.A0[k], r.A1[k]}, eA)) return s2;
-          if (try_apply(&s2, Pair64{r.B0[k], r.B1[k]}, eB)) return s2;
-          const int a = min(k * L, w);
-          return terms(s2, i, a, min(a + L, w));
-        });
-    __syncthreads();  // rl is reused by the next fallback
-    return out;
-  }
-
+  // The plane from S = 0, a chunk of rows at a time (plan_plane has left the
+  // rows in LDS when the plane fits one chunk).
   __device__ uint64_t walk_rows() const {
-    return walk(
-        0, h, [&](int i) { return (int)plan[i]; }, [&](int i) { return R[i]; },
-        [&](int i) { return row_pair(i, plan[i]); },
-        [&](uint64_t s, int i) {
-          if (try_exact(&s, R[i])) return s;
-          const int e = plan[i];
-          if (e >= 53 && try_apply(&s, row_pair(i, e), e)) return s;
-          return fallback_row(s, i);
-        });
+    if (h <= kChunk) return walk_chunk(0, h, 0);
+    uint64_t s = 0;
+    for (int a = 0; a < h; a += kChunk) {
+      const int n = min(kChunk, h - a);
+      __syncthreads();
+      for (int k = threadIdx.x; k < n; k += kT) {
+        rows.R[k] = R[a + k];
+        rows.C[k] = (uint16_t)C[a + k];
+        rows.plan[k] = plan[a + k];
+      }
+      __syncthreads();
+      s = walk_chunk(a, n, s);
+    }
+    return s;
   }
 };
 
+// ---------------------------------------------------------------------------
+// Fast walk: the common case, with a short sequential path.  Rows held in
+// LDS; one pass gives every row's exact prefix and odd-square prefix and the
+// segment table; segments planned exact or in the binades of 2^53 and 2^54
+// are added from prefix differences (closed form); a row planned across a
+// binade edge is split into kT runs the same way, and only its crossing
+// run(s) go term by term.  Anything else (planes taller than one chunk,
+// rows wider than kStage, binades from 2^55, many segments, a stretch that
+// is refused, test modes) returns false and the general walk runs instead.
+
+// With every sum below 2^55 an item's plan follows from where its exact
+// interval [P - M, P + E + M] lies against 2^53, 2^54 and 2^55.  Each edge
+// of a plan is the first item at which a non-decreasing quantity (P + E, or
+// P - M, or P + E + M) reaches a threshold, so one block minimum over the
+// items finds all of them:
+//   x0: P + E > 2^53        (end of the exact items)
+//   x1: P - M >= 2^53       (first item inside the binade of 2^53)
+//   x2: P + E + M >= 2^54   (first item that may leave it)
+//   x3: P - M >= 2^54       (first item inside the binade of 2^54)
+//   x4: P + E + M >= 2^55   (first item that may leave that one)
+// The segments, in order, are exact [0, x0), across [x0, x1), 53 [x1, x2),
+// across [x2, x3), 54 [x3, x4), beyond [x4, n); empty ones are skipped.
+
+constexpr int kEdges = 5;
+
+struct FastLds {
+  uint64_t P[kEdges + 2], PC[kEdges + 2];  // exact prefixes at the edges (and at n)
+  int x[kEdges + 2];
+  int xw[kEdges][kWaves];  // per-wave edge minima
+  uint16_t rowbuf[kStage];
+  uint64_t runE[kT];
+};
+
+// Edges of n items (thread t owns items [t*c, t*c + c)); base is the sum
+// before item 0.  Fills fl.x / fl.P / fl.PC (entries 0..4 the edges, 5 = n),
+// the edges made non-decreasing so that the segments tile [0, n).
+template <class EAt, class CAt>
+__device__ __forceinline__ void fast_edges(int n, uint64_t base, uint64_t M, EAt e_at, CAt c_at,
+                                           FastLds& fl, BlockScratch& sm) {
+  const int c = (n + kT - 1) / kT;
+  const int a = min((int)threadIdx.x * c, n), b = min(a + c, n);
+  uint64_t le = 0, lc = 0;
+  for (int k = a; k < b; ++k) {
+    le += e_at(k);
+    lc += c_at(k);
+  }
+  uint64_t P, PC, TE, TC;
+  block_excl_scan2(le, lc, &P, &PC, &TE, &TC, sm);
+  constexpr uint64_t T53 = 1ull << 53, T54 = 1ull << 54, T55 = 1ull << 55;
+  int x[kEdges] = {n, n, n, n, n};
+  {
+    uint64_t q = base + P;
+    for (int k = a; k < b; ++k) {
+      const uint64_t e = e_at(k);
+      const uint64_t lo = q > M ? q - M : 0, hi = q + e + M;
+      if (x[0] == n && q + e > T53) x[0] = k;
+      if (x[1] == n && lo >= T53) x[1] = k;
+      if (x[2] == n && hi >= T54) x[2] = k;
+      if (x[3] == n && lo >= T54) x[3] = k;
+      if (x[4] == n && hi >= T55) x[4] = k;
+      q += e;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kEdges; ++j) x[j] = (int)wave_min_u32((uint32_t)x[j]);
+  if ((threadIdx.x & 63) == 0)
+#pragma unroll
+    for (int j = 0; j < kEdges; ++j) fl.xw[j][threadIdx.x >> 6] = x[j];
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kEdges; ++j) {
+    int m = fl.xw[j][0];
+#pragma unroll
+    for (int q = 1; q < kWaves; ++q) m = min(m, fl.xw[j][q]);
+    x[j] = j ? max(m, x[j - 1]) : m;
+  }
+  // the owners of the edge items record the exact prefixes there
+  {
+    uint64_t q = base + P, qc = PC;
+    for (int k = a; k < b; ++k) {
+#pragma unroll
+      for (int j = 0; j < kEdges; ++j)
+        if (x[j] == k) {
+          fl.P[j] = q;
+          fl.PC[j] = qc;
+        }
+      q += e_at(k);
+      qc += c_at(k);
+    }
+  }
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int j = 0; j < kEdges; ++j) {
+      fl.x[j] = x[j];
+      if (x[j] == n) {
+        fl.P[j] = base + TE;
+        fl.PC[j] = TC;
+      }
+    }
+    fl.x[kEdges] = n;
+    fl.P[kEdges] = base + TE;
+    fl.PC[kEdges] = TC;
+  }
+  __syncthreads();
+}
+
+// The segments of fast_edges, in order: plan of segment g (0 exact, 1
+// across, 2 the binade of 2^53, 3 across, 4 the binade of 2^54, 5 beyond).
+__device__ __forceinline__ int fast_plan(int g) {
+  return g == 0 ? kPlanExact : g == 2 ? 53 : g == 4 ? 54 : (g == 5 ? -2 : kPlanCross);
+}
+
+// s + t1 + t2 + ... with the CPU's double adds (exact integers in units).
+__device__ __forceinline__ uint64_t add_terms_f64(uint64_t s, const uint16_t* x, int j0, int j1) {
+  double d = (double)s;  // s is a double the CPU could hold: exact
+  for (int j = j0; j < j1; ++j) d = d + (double)fsq_units(x[j]);
+  return (uint64_t)d;
+}
+
+// Row i planned across an edge, from S: kT runs, closed forms, the runs
+// across an edge term by term.  Returns false when it needs the general walk.
+__device__ bool fast_cross_row(uint64_t* sp, int i, const void* plane, long stride, int w,
+                               int bpc8, FastLds& fl, BlockScratch& sm) {
+  if (w > kStage) return false;
+  const uint64_t s0 = *sp;
+  __syncthreads();
+  {
+    const long base = (long)i * stride;
+    constexpr int U = kStage / kT;
+    uint32_t v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = threadIdx.x + u * kT;
+      v[u] = j < w ? (bpc8 ? ((const uint8_t*)plane)[base + j] : ((const uint16_t*)plane)[base + j]) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = threadIdx.x + u * kT;
+      if (j < w) fl.rowbuf[j] = (uint16_t)v[u];
+    }
+  }
+  const int L = (w + kT - 1) / kT;
+  const int t = threadIdx.x;
+  const int j0 = min(t * L, w), j1 = min(j0 + L, w);
+  __syncthreads();
+  uint32_t c = 0;
+  uint64_t E = 0;
+  for (int j = j0; j < j1; ++j) {
+    const uint32_t x = fsq_units(fl.rowbuf[j]);
+    E += x;
+    c += x & 1u;
+  }
+  const int eB = (s0 < kTwo53 ? 53 : binade(s0)) + 1;
+  const uint64_t Mr = (uint64_t)w << (eB - 53);
+  fast_edges(
+      kT, s0, Mr, [&](int) { return E; }, [&](int) { return (uint64_t)c; }, fl, sm);
+  uint64_t s = s0;
+  int a = 0;
+  for (int g = 0; g <= kEdges; ++g) {
+    const int b = fl.x[g] > a ? fl.x[g] : a;  // edges are non-decreasing
+    if (b > a) {
+      const int e = fast_plan(g);
+      const uint64_t Pa = g == 0 ? s0 : fl.P[g - 1], PCa = g == 0 ? 0 : fl.PC[g - 1];
+      const uint64_t Eg = fl.P[g] - Pa, Cg = fl.PC[g] - PCa;
+      if (e == kPlanExact) {
+        if (!try_exact(&s, Eg)) return false;
+      } else if (e == 53 || e == 54) {
+        if (!try_apply(&s, closed_pair(Eg, Cg, e), e)) return false;
+      } else if (e == kPlanCross) {
+        s = add_terms_f64(s, fl.rowbuf, min(a * L, w), min(b * L, w));
+      } else {
+        return false;
+      }
+    }
+    a = b;
+  }
+  *sp = s;
+  return true;
+}
+
+// The plane's rows are in rows.R / rows.C (h <= kChunk).  Returns false when
+// the plane needs the general walk.  Margin: with every sum below 2^55 the
+// CPU's sum strays from the exact prefix by at most 2 units per term added
+// past 2^53.
+__device__ bool fast_walk(uint64_t* out, uint64_t* exact, int h, const void* plane, long stride,
+                          int w, int bpc8, RowLds& rows, FastLds& fl, BlockScratch& sm) {
+  const uint64_t M = 2ull * (uint64_t)w * (uint64_t)h;
+  fast_edges(
+      h, 0, M, [&](int k) { return rows.R[k]; }, [&](int k) { return (uint64_t)rows.C[k]; },
+      fl, sm);
+  const uint64_t E = fl.P[kEdges];
+  *exact = E;
+  if (E >= (1ull << 55)) return false;
+  int x[kEdges + 1];
+  uint64_t P[kEdges + 1], PC[kEdges + 1];
+#pragma unroll
+  for (int j = 0; j <= kEdges; ++j) {
+    x[j] = fl.x[j];
+    P[j] = fl.P[j];
+    PC[j] = fl.PC[j];
+  }
+  uint64_t s = 0;
+  int a = 0;
+  for (int g = 0; g <= kEdges; ++g) {
+    const int b = x[g] > a ? x[g] : a;
+    if (b > a) {
+      const int e = fast_plan(g);
+      const uint64_t Pa = g == 0 ? 0 : P[g - 1], PCa = g == 0 ? 0 : PC[g - 1];
+      const uint64_t Eg = P[g] - Pa, Cg = PC[g] - PCa;
+      if (e == kPlanExact) {
+        if (!try_exact(&s, Eg)) return false;
+      } else if (e == 53 || e == 54) {
+        if (!try_apply(&s, closed_pair(Eg, Cg, e), e)) return false;
+      } else if (e == kPlanCross) {
+        for (int i = a; i < b; ++i)
+          if (!fast_cross_row(&s, i, plane, stride, w, bpc8, fl, sm)) return false;
+      } else {
+        return false;
+      }
+    }
+    a = b;
+  }
+  *out = s;
+  return true;
+}
+
 // The PSNR noise: rows added into a double in order.  Exact while the sum
 // stays at or below 2^53 units; from the first row that takes it past, one
-// hardware double add per row, as the CPU does (ADR-1499, Decision).
-__device__ double noise_chain(const uint64_t* RN, int h, BlockScratch& sm, uint64_t* exact) {
-  __shared__ uint64_t stage[256];
-  uint64_t carry = 0;
+// hardware double add per row, as the CPU does (ADR-1499, Decision).  The
+// rows go through LDS (stage, kChunk values) a chunk at a time.
+__device__ double noise_chain(const uint64_t* RN, int h, BlockScratch& sm, uint64_t* stage,
+                              uint64_t* exact) {
+  uint64_t E = 0, p = 0;
   int first = h;
-  for (int base = 0; base < h; base += 256) {
-    const int i = base + threadIdx.x;
-    const uint64_t r = i < h ? RN[i] : 0;
-    uint64_t tot;
-    const uint64_t ex = carry + block_excl_scan_u64(r, &tot, sm);
-    const int hit = (i < h && first == h && ex + r > kTwo53) ? i : h;
-    const int m = block_min_int(hit, sm);
-    if (first == h && m < h) first = m;
-    carry += tot;
+  uint64_t pfirst = 0;
+  {
+    const int c = (h + kT - 1) / kT;
+    const int a = min((int)threadIdx.x * c, h), b = min(a + c, h);
+    uint64_t loc = 0;
+    for (int i = a; i < b; ++i) loc += RN[i];
+    p = block_excl_scan_u64(loc, &E, sm);
+    for (int i = a; i < b && first == h; ++i) {
+      const uint64_t r = RN[i];
+      if (p + r > kTwo53) {
+        first = i;
+        pfirst = p;
+      }
+      p += r;
+    }
   }
-  *exact = carry;
-  if (first == h) return (double)carry;
-  // exact prefix before the first row that passes 2^53
-  uint64_t pre = 0;
-  for (int i = threadIdx.x; i < first; i += 256) pre += RN[i];
-  pre = block_sum_u64(pre, sm);
-  double d = (double)pre;
-  for (int base = first; base < h; base += 256) {
-    const int n = min(256, h - base);
+  const int i0 = block_min_int(first, sm);
+  *exact = E;
+  if (i0 >= h) return (double)E;
+  __syncthreads();
+  if (first == i0) sm.v[0] = pfirst;
+  __syncthreads();
+  double d = (double)sm.v[0];  // exact: at most 2^53
+  for (int base = i0; base < h; base += kChunk) {
+    const int n = min(kChunk, h - base);
     __syncthreads();
-    if ((int)threadIdx.x < n) stage[threadIdx.x] = RN[base + threadIdx.x];
+    for (int k = threadIdx.x; k < n; k += kT) stage[k] = RN[base + k];
     __syncthreads();
     for (int k = 0; k < n; ++k) d = d + (double)stage[k];
   }
   return d;
 }
 
-template <typename T>
-__global__ void __launch_bounds__(256) k_walk(Geometry g, RowArrays ra, double* results,
-                                              uint64_t* units, unsigned dbg) {
+// The general walk of one plane (any geometry, any plan, every test mode):
+// plan, then the Walker.  Not inlined: the common case never calls it.
+__device__ __noinline__ void general_walk(const Geometry& g, const RowArrays& ra, int f, int pl,
+                                          unsigned dbg, BlockScratch& sm, RowLds& rows,
+                                          RunLds& runs, Seg* rseg, Seg* useg,
+                                          uint16_t* rowbuf, int* staged, uint64_t* S,
+                                          uint64_t* E, uint64_t* s1) {
+  const long off = (long)(pl * g.nframes + f) * g.h;
+  __syncthreads();
+  const PlanInfo pi = plan_plane(ra.r2 + off, ra.plan + off, g.w, g.h, dbg, sm, &rows,
+                                 ra.codd + off, ra.r1 + off, s1);
+  *E = *S = pi.E;
+  if (may_round(pi.E, dbg)) {
+    if (threadIdx.x == 0) *staged = -1;
+    __syncthreads();
+    const Walker wk{(const char*)(pl == 0 ? g.ref : g.dis) +
+                        (long)f * g.pitch * (g.bpc == 8 ? 1 : 2),
+                    g.stride, g.w, g.h, g.bpc == 8, ra.r2 + off, ra.codd + off,
+                    ra.plan + off, ra.pairs + 2 * off, dbg, sm, rows, runs, rseg, useg,
+                    rowbuf, staged};
+    *S = wk.walk_rows();
+  }
+}
+
+__global__ void __launch_bounds__(kT) k_walk(Geometry g, RowArrays ra, double* results,
+                                             uint64_t* units, unsigned dbg) {
   __shared__ BlockScratch sm;
-  __shared__ RunLds rl;
+  __shared__ RowLds rows;
+  __shared__ RunLds runs;
+  __shared__ Seg rseg[kMaxSeg + 1], useg[kMaxSeg + 1];
+  __shared__ FastLds fl;
+  __shared__ int staged;
   const int f = blockIdx.x / 3, job = blockIdx.x % 3;
   const int k = g.bpc - 8;
   const double n = (double)g.w * (double)g.h;
   if (job == 2) {
     uint64_t ex;
-    const double d = noise_chain(ra.rn + (long)f * g.h, g.h, sm, &ex);
+    const double d = noise_chain(ra.rn + (long)f * g.h, g.h, sm, rows.R, &ex);
     if (threadIdx.x == 0) {
       const double noise = d * (1.0 / (double)(1u << (2 * k)));
       results[6 * f + 4] = noise;
@@ -609,16 +1147,47 @@ __global__ void __launch_bounds__(256) k_walk(Geometry g, RowArrays ra, double* 
   }
   const int pl = job;
   const long off = (long)(pl * g.nframes + f) * g.h;
-  uint64_t s1 = 0;
-  for (int i = threadIdx.x; i < g.h; i += 256) s1 += ra.r1[off + i];
-  s1 = block_sum_u64(s1, sm);
-  const uint64_t E = plan_plane(ra.r2 + off, ra.prefix + off, ra.plan + off, g.w, g.h, dbg, sm);
-  uint64_t S = E;
-  if (g.may_round && may_round(E, dbg)) {
-    const Walker<T> wk{(const T*)(pl == 0 ? g.ref : g.dis) + (long)f * g.pitch,
-                       g.stride, g.w, g.h, ra.r2 + off, ra.codd + off, ra.pairs + 2 * off,
-                       ra.plan + off, dbg, sm, rl};
-    S = wk.walk_rows();
+  uint64_t S = 0, E = 0, s1 = 0;
+  if (!g.may_round) {
+    uint64_t a = 0, b = 0;
+    for (int i = threadIdx.x; i < g.h; i += kT) {
+      a += ra.r1[off + i];
+      b += ra.r2[off + i];
+    }
+    s1 = block_sum_u64(a, sm);
+    E = S = block_sum_u64(b, sm);
+  } else {
+    bool fast = false;
+    if (dbg == 0 && g.h <= kChunk) {
+      uint64_t a = 0;
+      {
+        constexpr int U = (kChunk + kT - 1) / kT;
+        uint64_t rv[U];
+        uint32_t cv[U], sv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {  // every load issued before the first use
+          const int i = threadIdx.x + u * kT;
+          rv[u] = i < g.h ? ra.r2[off + i] : 0;
+          cv[u] = i < g.h ? ra.codd[off + i] : 0;
+          sv[u] = i < g.h ? ra.r1[off + i] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int i = threadIdx.x + u * kT;
+          if (i < g.h) {
+            rows.R[i] = rv[u];
+            rows.C[i] = (uint16_t)cv[u];
+          }
+          a += sv[u];
+        }
+      }
+      s1 = block_sum_u64(a, sm);  // also the barrier before the rows are read
+      const char* plane = (const char*)(pl == 0 ? g.ref : g.dis) +
+                          (long)f * g.pitch * (g.bpc == 8 ? 1 : 2);
+      fast = fast_walk(&S, &E, g.h, plane, g.stride, g.w, g.bpc == 8, rows, fl, sm);
+    }
+    if (!fast) general_walk(g, ra, f, pl, dbg, sm, rows, runs, rseg, useg, fl.rowbuf, &staged,
+                            &S, &E, &s1);
   }
   if (threadIdx.x == 0) {
     const double m1 = ((double)s1 * (1.0 / (double)(1u << k))) / n;
@@ -651,7 +1220,7 @@ hipError_t launch_rows(const Geometry& g, const RowArrays& ra, hipStream_t st) {
 }
 
 hipError_t launch_plan(const Geometry& g, const RowArrays& ra, unsigned dbg, hipStream_t st) {
-  hipLaunchKernelGGL(k_plan, dim3(2 * g.nframes), dim3(256), 0, st, g, ra, dbg);
+  hipLaunchKernelGGL(k_plan, dim3(2 * g.nframes), dim3(kT), 0, st, g, ra, dbg);
   return hipGetLastError();
 }
 
@@ -665,12 +1234,7 @@ hipError_t launch_pairs(const Geometry& g, const RowArrays& ra, unsigned dbg, hi
 
 hipError_t launch_walk(const Geometry& g, const RowArrays& ra, double* results, uint64_t* units,
                        unsigned dbg, hipStream_t st) {
-  if (g.bpc == 8)
-    hipLaunchKernelGGL(k_walk<uint8_t>, dim3(3 * g.nframes), dim3(256), 0, st, g, ra, results,
-                       units, dbg);
-  else
-    hipLaunchKernelGGL(k_walk<uint16_t>, dim3(3 * g.nframes), dim3(256), 0, st, g, ra, results,
-                       units, dbg);
+  hipLaunchKernelGGL(k_walk, dim3(3 * g.nframes), dim3(kT), 0, st, g, ra, results, units, dbg);
   return hipGetLastError();
 }
 
