@@ -79,12 +79,14 @@ def main():
     if args.calib_copy:
         import torch
         n = args.calib_copy << 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        # an elementwise kernel (not a DMA copy) that reads n bytes and writes n
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(5):
-            dst.copy_(src)
+            torch.neg(src, out=dst)
         torch.cuda.synchronize()
-        print(json.dumps({"calib_copy_bytes": n, "copies": 5}), flush=True)
+        print(json.dumps({"calib_copy_bytes_read": n, "calib_copy_bytes_written": n,
+                          "launches": 5}), flush=True)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): this path is a "

@@ -1100,26 +1100,29 @@ __device__ double noise_chain(const uint64_t* RN, int h, BlockScratch& sm, uint6
 
 // The general walk of one plane (any geometry, any plan, every test mode):
 // plan, then the Walker.  Not inlined: the common case never calls it.
-__device__ __noinline__ void general_walk(const Geometry& g, const RowArrays& ra, int f, int pl,
+__device__ __noinline__ void general_walk(const char* plane, long stride, int w, int h, int bpc8,
+                                          const uint64_t* r2, const uint32_t* codd,
+                                          const uint32_t* r1, int8_t* plan, uint64_t* pairs,
                                           unsigned dbg, BlockScratch& sm, RowLds& rows,
                                           RunLds& runs, Seg* rseg, Seg* useg,
-                                          uint16_t* rowbuf, int* staged, uint64_t* S,
-                                          uint64_t* E, uint64_t* s1) {
-  const long off = (long)(pl * g.nframes + f) * g.h;
+                                          uint16_t* rowbuf, int* staged, uint64_t* res) {
   __syncthreads();
-  const PlanInfo pi = plan_plane(ra.r2 + off, ra.plan + off, g.w, g.h, dbg, sm, &rows,
-                                 ra.codd + off, ra.r1 + off, s1);
-  *E = *S = pi.E;
+  uint64_t s1 = 0;
+  const PlanInfo pi = plan_plane(r2, plan, w, h, dbg, sm, &rows, codd, r1, &s1);
+  uint64_t S = pi.E;
   if (may_round(pi.E, dbg)) {
     if (threadIdx.x == 0) *staged = -1;
     __syncthreads();
-    const Walker wk{(const char*)(pl == 0 ? g.ref : g.dis) +
-                        (long)f * g.pitch * (g.bpc == 8 ? 1 : 2),
-                    g.stride, g.w, g.h, g.bpc == 8, ra.r2 + off, ra.codd + off,
-                    ra.plan + off, ra.pairs + 2 * off, dbg, sm, rows, runs, rseg, useg,
-                    rowbuf, staged};
-    *S = wk.walk_rows();
+    const Walker wk{plane, stride, w,   h,     bpc8, r2,   codd,  plan,   pairs,
+                    dbg,   sm,     rows, runs, rseg, useg, rowbuf, staged};
+    S = wk.walk_rows();
   }
+  if (threadIdx.x == 0) {
+    res[0] = S;
+    res[1] = pi.E;
+    res[2] = s1;
+  }
+  __syncthreads();
 }
 
 __global__ void __launch_bounds__(kT) k_walk(Geometry g, RowArrays ra, double* results,
@@ -1130,6 +1133,7 @@ __global__ void __launch_bounds__(kT) k_walk(Geometry g, RowArrays ra, double* r
   __shared__ Seg rseg[kMaxSeg + 1], useg[kMaxSeg + 1];
   __shared__ FastLds fl;
   __shared__ int staged;
+  __shared__ uint64_t res[3];
   const int f = blockIdx.x / 3, job = blockIdx.x % 3;
   const int k = g.bpc - 8;
   const double n = (double)g.w * (double)g.h;
@@ -1186,8 +1190,16 @@ __global__ void __launch_bounds__(kT) k_walk(Geometry g, RowArrays ra, double* r
                           (long)f * g.pitch * (g.bpc == 8 ? 1 : 2);
       fast = fast_walk(&S, &E, g.h, plane, g.stride, g.w, g.bpc == 8, rows, fl, sm);
     }
-    if (!fast) general_walk(g, ra, f, pl, dbg, sm, rows, runs, rseg, useg, fl.rowbuf, &staged,
-                            &S, &E, &s1);
+    if (!fast) {
+      const char* plane = (const char*)(pl == 0 ? g.ref : g.dis) +
+                          (long)f * g.pitch * (g.bpc == 8 ? 1 : 2);
+      general_walk(plane, g.stride, g.w, g.h, g.bpc == 8, ra.r2 + off, ra.codd + off,
+                   ra.r1 + off, ra.plan + off, ra.pairs + 2 * off, dbg, sm, rows, runs, rseg,
+                   useg, fl.rowbuf, &staged, res);
+      S = res[0];
+      E = res[1];
+      s1 = res[2];
+    }
   }
   if (threadIdx.x == 0) {
     const double m1 = ((double)s1 * (1.0 / (double)(1u << k))) / n;
