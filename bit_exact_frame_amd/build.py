@@ -3,8 +3,9 @@
     python -m bit_exact_frame_amd.build          # libbef.so
     build(mutant=k, host_only=True, out=...)     # host-only test variants
 
-The library holds the kernels (kernels.hip), the host runtime behind the C
-ABI (bef.cpp) and the host emulation test entry points (host_emu.cpp).
+The library holds the streaming row kernels (rows.hip), the ordered plan /
+pair / walk kernels (walk.hip), the host runtime behind the C ABI (bef.cpp)
+and the host emulation test entry points (host_emu.cpp).
 Every HIP source is compiled for gfx950 with packed FP32 instructions
 disabled and no floating-point contraction.
 """
@@ -20,7 +21,7 @@ LIB = os.path.join(HERE, "libbef.so")
 ARCH = os.environ.get("BEF_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["kernels.hip", "bef.cpp", "host_emu.cpp"]
+SOURCES = ["rows.hip", "walk.hip", "bef.cpp", "host_emu.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-fno-fast-math",
           "-Wall", "-Wno-unused-function", f"-I{os.path.join(ROOT, 'include')}"]

@@ -1,7 +1,7 @@
 // bef.cpp -- host runtime behind include/bef.h: argument checks, device
 // scratch, the launch sequence on the caller's stream, read-back.
 //
-// Every step of the reductions runs in the kernels (kernels.hip), the final
+// Every step of the reductions runs in the kernels (rows.hip, walk.hip), the final
 // divisions included; the host only validates, allocates scratch, launches
 // and copies the per-frame results back.
 #include <errno.h>
@@ -143,8 +143,10 @@ hipEvent_t ev_get() {
     g_ev_pool.pop_back();
     return e;
   }
+  // timing only: read after the stream is synchronised, so no system-scope
+  // fence (its cache writeback would land inside the measured intervals)
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
 }
 
@@ -162,14 +164,14 @@ void ev_collect() {
   g_ev_live.clear();
 }
 
+// launch(ev0, ev1): the events (null when timing is off) go with the
+// dispatch, so the interval is the kernel's own execution.
 template <class F>
-hipError_t timed(int kernel, hipStream_t st, F launch) {
-  if (!g_timing) return launch();
+hipError_t timed(int kernel, F launch) {
+  if (!g_timing) return launch(nullptr, nullptr);
   hipEvent_t a = ev_get(), b = ev_get();
-  if (!a || !b) return launch();
-  (void)hipEventRecord(a, st);
-  const hipError_t e = launch();
-  (void)hipEventRecord(b, st);
+  if (!a || !b) return launch(nullptr, nullptr);
+  const hipError_t e = launch(a, b);
   g_ev_live.push_back(EvPair{kernel, a, b});
   return e;
 }
@@ -227,12 +229,18 @@ int prepare(Call& c, const void* ref, const void* dis, int w, int h, ptrdiff_t s
 
 int enqueue(const Call& c, hipStream_t st, double* d_results) {
   const unsigned dbg = g_dbg;
-  BEF_HIP(timed(0, st, [&] { return launch_rows(c.g, c.ra, st); }));
+  BEF_HIP(timed(0, [&](hipEvent_t a, hipEvent_t b) { return launch_rows(c.g, c.ra, st, a, b); }));
   if (c.need_pairs) {
-    BEF_HIP(timed(1, st, [&] { return launch_plan(c.g, c.ra, dbg, st); }));
-    BEF_HIP(timed(2, st, [&] { return launch_pairs(c.g, c.ra, dbg, st); }));
+    BEF_HIP(timed(1, [&](hipEvent_t a, hipEvent_t b) {
+      return launch_plan(c.g, c.ra, dbg, st, a, b);
+    }));
+    BEF_HIP(timed(2, [&](hipEvent_t a, hipEvent_t b) {
+      return launch_pairs(c.g, c.ra, dbg, st, a, b);
+    }));
   }
-  BEF_HIP(timed(3, st, [&] { return launch_walk(c.g, c.ra, d_results, c.d_units, dbg, st); }));
+  BEF_HIP(timed(3, [&](hipEvent_t a, hipEvent_t b) {
+    return launch_walk(c.g, c.ra, d_results, c.d_units, dbg, st, a, b);
+  }));
   return 0;
 }
 

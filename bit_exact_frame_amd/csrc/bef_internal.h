@@ -1,6 +1,7 @@
 // bef_internal.h -- types shared by the kernels and the host runtime.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -32,10 +33,15 @@ struct RowArrays {
   uint64_t* pairs;  // [plane][frame][row][2] row pair (binades >= 55)
 };
 
-hipError_t launch_rows(const Geometry& g, const RowArrays& ra, hipStream_t st);
-hipError_t launch_plan(const Geometry& g, const RowArrays& ra, unsigned dbg, hipStream_t st);
-hipError_t launch_pairs(const Geometry& g, const RowArrays& ra, unsigned dbg, hipStream_t st);
+// Each launch goes out with hipExtLaunchKernel; ev0 / ev1 (or null) are
+// recorded by the dispatch itself at the kernel's start and end.
+hipError_t launch_rows(const Geometry& g, const RowArrays& ra, hipStream_t st, hipEvent_t ev0,
+                       hipEvent_t ev1);
+hipError_t launch_plan(const Geometry& g, const RowArrays& ra, unsigned dbg, hipStream_t st,
+                       hipEvent_t ev0, hipEvent_t ev1);
+hipError_t launch_pairs(const Geometry& g, const RowArrays& ra, unsigned dbg, hipStream_t st,
+                        hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_walk(const Geometry& g, const RowArrays& ra, double* results, uint64_t* units,
-                       unsigned dbg, hipStream_t st);
+                       unsigned dbg, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
 
 }  // namespace bef

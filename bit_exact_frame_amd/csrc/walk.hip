@@ -1,22 +1,17 @@
-// kernels.hip -- gfx950 kernels of the bit-exact frame reductions.
+// walk.hip -- the ordered part: plan, pairs and the walk of each plane.
 //
-// Pipeline for a batch of frames (all on the caller's stream):
-//   k_rows     one wave per (row, frame): reads the row of both planes once
-//              (16-byte loads), forms every term in registers and writes the
-//              row's exact integer sums: sum of x per plane, sum of float
-//              squares per plane, noise sum, and the count of odd squares.
-//              Per-row sums: ADR-1497 Decision (each row's exact sum);
-//              ADR-1499 Decision (blocks of one row, exact 64-bit row sums).
-//   k_plan     (only for frames that can pass 2^55 units) exact row prefix
-//              and per-row binade plan, for k_pairs.
+//   k_plan     (only for frames that can pass 2^55 units, or under a test
+//              flag) exact row prefix and per-row binade plan, for k_pairs.
 //   k_pairs    (same condition) the row's pair under its planned binade:
 //              64 lane runs joined by an ordered tree (ADR-1497 Decision).
-//   k_walk     one 256-thread block per (frame, plane) walks the rows in
-//              order: exact adds up to 2^53, stretches of rows that share a
-//              planned binade applied as one composed pair, unfit rows
-//              split into 256 runs, unfit runs added term by term (ADR-1497
-//              Decision); one block per frame adds the noise rows into a
-//              double in row order (ADR-1499 Decision); then the divisions.
+//   k_walk     one 512-thread block per (frame, plane) takes the rows in
+//              order: exact adds up to 2^53, stretches of rows inside one
+//              binade applied as one pair (closed form in the binades of
+//              2^53 and 2^54), rows that cross a binade edge split into runs,
+//              runs that cross added term by term with the double add
+//              (ADR-1497 Decision); one block per frame adds the noise rows
+//              into a double in row order (ADR-1499 Decision); then the
+//              divisions.
 //
 // Units: 1/s^2 for squares, 1/s for first moments (s = 2^(bpc-8)).  No
 // atomics anywhere: every sum has one owner and a fixed order.
@@ -25,274 +20,11 @@
 
 #include "bef_internal.h"
 #include "ordsum.h"
+#include "wave.h"
 
 using namespace bef;
 
 namespace {
-
-typedef unsigned short us2 __attribute__((ext_vector_type(2)));
-typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-
-// ---------------------------------------------------------------------------
-// Wave-level reductions (64 lanes).  Within each 16-lane row: DPP
-// quad_perm xor-1, quad_perm xor-2, row_half_mirror, row_mirror; across the
-// four rows: lanes 15, 31, 47 and 63 read into scalars.  64-bit values move
-// as two 32-bit halves and are added with carry.
-
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
-}
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
-  const uint32_t lo = dpp32<CTRL>((uint32_t)v), hi = dpp32<CTRL>((uint32_t)(v >> 32));
-  return ((uint64_t)hi << 32) | lo;
-}
-__device__ __forceinline__ uint32_t rdl32(uint32_t v, int lane) {
-  return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
-}
-__device__ __forceinline__ uint64_t rdl64(uint64_t v, int lane) {
-  return ((uint64_t)rdl32((uint32_t)(v >> 32), lane) << 32) | rdl32((uint32_t)v, lane);
-}
-
-__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
-  v += dpp64<0xB1>(v);   // quad_perm [1,0,3,2]
-  v += dpp64<0x4E>(v);   // quad_perm [2,3,0,1]
-  v += dpp64<0x141>(v);  // row_half_mirror
-  v += dpp64<0x140>(v);  // row_mirror
-  return rdl64(v, 15) + rdl64(v, 31) + rdl64(v, 47) + rdl64(v, 63);
-}
-__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-  v += dpp32<0xB1>(v);
-  v += dpp32<0x4E>(v);
-  v += dpp32<0x141>(v);
-  v += dpp32<0x140>(v);
-  return rdl32(v, 15) + rdl32(v, 31) + rdl32(v, 47) + rdl32(v, 63);
-}
-// Doubles holding integers below 2^53: every partial sum is exact, so the
-// order of this tree does not matter.
-__device__ __forceinline__ double wave_sum_f64i(double x) {
-  uint64_t b = __builtin_bit_cast(uint64_t, x);
-#define BEF_DSTEP(C)                                                \
-  {                                                                 \
-    const double o = __builtin_bit_cast(double, dpp64<C>(b));       \
-    x += o;                                                         \
-    b = __builtin_bit_cast(uint64_t, x);                            \
-  }
-  BEF_DSTEP(0xB1) BEF_DSTEP(0x4E) BEF_DSTEP(0x141) BEF_DSTEP(0x140)
-#undef BEF_DSTEP
-  const double a0 = __builtin_bit_cast(double, rdl64(b, 15));
-  const double a1 = __builtin_bit_cast(double, rdl64(b, 31));
-  const double a2 = __builtin_bit_cast(double, rdl64(b, 47));
-  const double a3 = __builtin_bit_cast(double, rdl64(b, 63));
-  return (a0 + a1) + (a2 + a3);
-}
-
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-  v = min(v, dpp32<0xB1>(v));
-  v = min(v, dpp32<0x4E>(v));
-  v = min(v, dpp32<0x141>(v));
-  v = min(v, dpp32<0x140>(v));
-  return min(min(rdl32(v, 15), rdl32(v, 31)), min(rdl32(v, 47), rdl32(v, 63)));
-}
-
-// Shift within each 16-lane row by CTRL (row_shr:k); lanes whose source is
-// outside the row, or rows not in ROWMASK, read 0.
-template <int CTRL, int ROWMASK>
-__device__ __forceinline__ uint64_t dpp64_or0(uint64_t v) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, ROWMASK, 0xF, false);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, ROWMASK, 0xF, false);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-// Inclusive prefix sum over the 64 lanes: row_shr 1, 2, 4, 8 inside each row
-// of 16 lanes, then row_bcast:15 into rows 1 and 3 and row_bcast:31 into
-// rows 2 and 3.
-__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v) {
-  v += dpp64_or0<0x111, 0xF>(v);
-  v += dpp64_or0<0x112, 0xF>(v);
-  v += dpp64_or0<0x114, 0xF>(v);
-  v += dpp64_or0<0x118, 0xF>(v);
-  v += dpp64_or0<0x142, 0xA>(v);
-  v += dpp64_or0<0x143, 0xC>(v);
-  return v;
-}
-
-// ---------------------------------------------------------------------------
-// k_rows: per-row exact sums.
-
-struct Acc16 {
-  double m2r0, m2r1, m2d0, m2d1, mn0, mn1;  // float squares, exact in f64
-  uint32_t s1r, s1d;                        // first-moment sums
-  us2 oddr, oddd;                           // odd squares (per half-word)
-};
-
-// Two 16-bit samples of each plane.
-template <bool ODD>
-__device__ __forceinline__ void take_dword16(uint32_t a, uint32_t b, Acc16& q) {
-  const uint32_t a0 = a & 0xFFFFu, a1 = a >> 16, b0 = b & 0xFFFFu, b1 = b >> 16;
-  const float fa0 = (float)a0, fa1 = (float)a1, fb0 = (float)b0, fb1 = (float)b1;
-  q.m2r0 += (double)__fmul_rn(fa0, fa0);
-  q.m2r1 += (double)__fmul_rn(fa1, fa1);
-  q.m2d0 += (double)__fmul_rn(fb0, fb0);
-  q.m2d1 += (double)__fmul_rn(fb1, fb1);
-  const float e0 = (float)((int32_t)a0 - (int32_t)b0);
-  const float e1 = (float)((int32_t)a1 - (int32_t)b1);
-  q.mn0 += (double)__fmul_rn(e0, e0);
-  q.mn1 += (double)__fmul_rn(e1, e1);
-  q.s1r = __builtin_amdgcn_udot2(__builtin_bit_cast(us2, a), (us2){1, 1}, q.s1r, false);
-  q.s1d = __builtin_amdgcn_udot2(__builtin_bit_cast(us2, b), (us2){1, 1}, q.s1d, false);
-  if (ODD) {
-    // A float square is odd exactly when x is odd and below 4096:
-    // min(x, 4096) & 1.
-    const us2 cap = {4096, 4096}, one = {1, 1};
-    q.oddr += __builtin_elementwise_min(__builtin_bit_cast(us2, a), cap) & one;
-    q.oddd += __builtin_elementwise_min(__builtin_bit_cast(us2, b), cap) & one;
-  }
-}
-
-template <bool ODD>
-__device__ __forceinline__ void take_sample16(uint32_t a, uint32_t b, Acc16& q) {
-  const float fa = (float)a, fb = (float)b;
-  q.m2r0 += (double)__fmul_rn(fa, fa);
-  q.m2d0 += (double)__fmul_rn(fb, fb);
-  const float e = (float)((int32_t)a - (int32_t)b);
-  q.mn0 += (double)__fmul_rn(e, e);
-  q.s1r += a;
-  q.s1d += b;
-  if (ODD) {
-    q.oddr.x += (unsigned short)((a < 4096u ? a : 4096u) & 1u);
-    q.oddd.x += (unsigned short)((b < 4096u ? b : 4096u) & 1u);
-  }
-}
-
-constexpr int kRowsU = 4;  // 16-byte loads in flight per lane per plane
-
-template <bool ODD, bool VEC>
-__device__ __forceinline__ void rows16_body(const Geometry& g, const RowArrays& ra, int i, int f,
-                                            int lane);
-
-template <bool ODD, bool VEC>
-__global__ void __launch_bounds__(256) k_rows16(Geometry g, RowArrays ra) {
-  const int lane = threadIdx.x & 63;
-  const long task = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (task >= (long)g.nframes * g.h) return;  // whole wave leaves together
-  const int i = (int)(task / g.nframes), f = (int)(task % g.nframes);
-  // The odd-square count is only read for rows past 2^53; a row whose
-  // prefix cannot reach 2^53 even with every sample at 65535 skips it.
-  if (ODD && (uint64_t)(i + 1) * (uint64_t)g.w * 0xFFFE0000ull > kTwo53)
-    rows16_body<true, VEC>(g, ra, i, f, lane);
-  else
-    rows16_body<false, VEC>(g, ra, i, f, lane);
-}
-
-template <bool ODD, bool VEC>
-__device__ __forceinline__ void rows16_body(const Geometry& g, const RowArrays& ra, int i, int f,
-                                            int lane) {
-  const uint16_t* rr = (const uint16_t*)g.ref + (long)f * g.pitch + (long)i * g.stride;
-  const uint16_t* dr = (const uint16_t*)g.dis + (long)f * g.pitch + (long)i * g.stride;
-  Acc16 q = {0, 0, 0, 0, 0, 0, 0u, 0u, {0, 0}, {0, 0}};
-  int j0 = 0;
-  if (VEC) {
-    const int nv = g.w >> 3;  // 8 samples per 16-byte vector
-    const v4u* rv = (const v4u*)rr;
-    const v4u* dv = (const v4u*)dr;
-    for (int base = 0; base < nv; base += 64 * kRowsU) {
-      v4u a[kRowsU], b[kRowsU];
-#pragma unroll
-      for (int u = 0; u < kRowsU; ++u) {
-        const int c = base + u * 64 + lane;
-        if (c < nv) {
-          a[u] = __builtin_nontemporal_load(rv + c);
-          b[u] = __builtin_nontemporal_load(dv + c);
-        } else {
-          a[u] = (v4u){0u, 0u, 0u, 0u};  // zero samples add nothing
-          b[u] = (v4u){0u, 0u, 0u, 0u};
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kRowsU; ++u) {
-        take_dword16<ODD>(a[u].x, b[u].x, q);
-        take_dword16<ODD>(a[u].y, b[u].y, q);
-        take_dword16<ODD>(a[u].z, b[u].z, q);
-        take_dword16<ODD>(a[u].w, b[u].w, q);
-      }
-    }
-    j0 = nv << 3;
-  }
-  for (int j = j0 + lane; j < g.w; j += 64) take_sample16<ODD>(rr[j], dr[j], q);
-
-  const double m2r = wave_sum_f64i(q.m2r0 + q.m2r1);
-  const double m2d = wave_sum_f64i(q.m2d0 + q.m2d1);
-  const double mn = wave_sum_f64i(q.mn0 + q.mn1);
-  const uint32_t s1r = wave_sum_u32(q.s1r), s1d = wave_sum_u32(q.s1d);
-  uint32_t odr = 0, odd = 0;
-  if (ODD) {
-    odr = wave_sum_u32((uint32_t)q.oddr.x + q.oddr.y);
-    odd = wave_sum_u32((uint32_t)q.oddd.x + q.oddd.y);
-  }
-  if (lane == 0) {
-    const long k = (long)f * g.h + i, k2 = (long)(g.nframes + f) * g.h + i;
-    ra.r1[k] = s1r;
-    ra.r1[k2] = s1d;
-    ra.r2[k] = (uint64_t)m2r;
-    ra.r2[k2] = (uint64_t)m2d;
-    ra.rn[k] = (uint64_t)mn;
-    ra.codd[k] = odr;
-    ra.codd[k2] = odd;
-  }
-}
-
-// 8-bit planes: squares are exact integers (x <= 255), summed with 4-way
-// byte dot products; the noise is r^2 + d^2 - 2rd per pixel, exactly.
-__global__ void __launch_bounds__(256) k_rows8(Geometry g, RowArrays ra) {
-  const int lane = threadIdx.x & 63;
-  const long task = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (task >= (long)g.nframes * g.h) return;
-  const int i = (int)(task / g.nframes), f = (int)(task % g.nframes);
-  const uint8_t* rr = (const uint8_t*)g.ref + (long)f * g.pitch + (long)i * g.stride;
-  const uint8_t* dr = (const uint8_t*)g.dis + (long)f * g.pitch + (long)i * g.stride;
-  uint32_t s1r = 0, s1d = 0, s2r = 0, s2d = 0, x = 0;
-  int j0 = 0;
-  if (g.vec) {
-    const int nv = g.w >> 4;
-    const uint4* rv = (const uint4*)rr;
-    const uint4* dv = (const uint4*)dr;
-    for (int c = lane; c < nv; c += 64) {
-      const uint4 a = rv[c], b = dv[c];
-      const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        s1r = __builtin_amdgcn_udot4(av[k], 0x01010101u, s1r, false);
-        s1d = __builtin_amdgcn_udot4(bv[k], 0x01010101u, s1d, false);
-        s2r = __builtin_amdgcn_udot4(av[k], av[k], s2r, false);
-        s2d = __builtin_amdgcn_udot4(bv[k], bv[k], s2d, false);
-        x = __builtin_amdgcn_udot4(av[k], bv[k], x, false);
-      }
-    }
-    j0 = nv << 4;
-  }
-  for (int j = j0 + lane; j < g.w; j += 64) {
-    const uint32_t a = rr[j], b = dr[j];
-    s1r += a;
-    s1d += b;
-    s2r += a * a;
-    s2d += b * b;
-    x += a * b;
-  }
-  const uint32_t S1r = wave_sum_u32(s1r), S1d = wave_sum_u32(s1d);
-  const uint64_t S2r = wave_sum_u64(s2r), S2d = wave_sum_u64(s2d), X = wave_sum_u64(x);
-  if (lane == 0) {
-    const long k = (long)f * g.h + i, k2 = (long)(g.nframes + f) * g.h + i;
-    ra.r1[k] = S1r;
-    ra.r1[k2] = S1d;
-    ra.r2[k] = S2r;
-    ra.r2[k2] = S2d;
-    ra.rn[k] = S2r + S2d - 2 * X;
-    ra.codd[k] = 0;
-    ra.codd[k2] = 0;
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Block-level helpers for the plan and walk kernels (kT threads = kWaves
@@ -1216,37 +948,24 @@ __global__ void __launch_bounds__(kT) k_walk(Geometry g, RowArrays ra, double* r
 
 namespace bef {
 
-hipError_t launch_rows(const Geometry& g, const RowArrays& ra, hipStream_t st) {
-  const long tasks = (long)g.nframes * g.h;
-  const unsigned blocks = (unsigned)((tasks + 3) / 4);
-  if (g.bpc == 8) {
-    hipLaunchKernelGGL(k_rows8, dim3(blocks), dim3(256), 0, st, g, ra);
-  } else if (g.need_odd) {
-    if (g.vec) hipLaunchKernelGGL((k_rows16<true, true>), dim3(blocks), dim3(256), 0, st, g, ra);
-    else hipLaunchKernelGGL((k_rows16<true, false>), dim3(blocks), dim3(256), 0, st, g, ra);
-  } else {
-    if (g.vec) hipLaunchKernelGGL((k_rows16<false, true>), dim3(blocks), dim3(256), 0, st, g, ra);
-    else hipLaunchKernelGGL((k_rows16<false, false>), dim3(blocks), dim3(256), 0, st, g, ra);
-  }
+hipError_t launch_plan(const Geometry& g, const RowArrays& ra, unsigned dbg, hipStream_t st,
+                       hipEvent_t ev0, hipEvent_t ev1) {
+  hipExtLaunchKernelGGL(k_plan, dim3(2 * g.nframes), dim3(kT), 0, st, ev0, ev1, 0, g, ra, dbg);
   return hipGetLastError();
 }
 
-hipError_t launch_plan(const Geometry& g, const RowArrays& ra, unsigned dbg, hipStream_t st) {
-  hipLaunchKernelGGL(k_plan, dim3(2 * g.nframes), dim3(kT), 0, st, g, ra, dbg);
-  return hipGetLastError();
-}
-
-hipError_t launch_pairs(const Geometry& g, const RowArrays& ra, unsigned dbg, hipStream_t st) {
+hipError_t launch_pairs(const Geometry& g, const RowArrays& ra, unsigned dbg, hipStream_t st,
+                        hipEvent_t ev0, hipEvent_t ev1) {
   const long tasks = 2L * g.nframes * g.h;
   const unsigned blocks = (unsigned)((tasks + 3) / 4);
-  if (g.bpc == 8) hipLaunchKernelGGL(k_pairs<uint8_t>, dim3(blocks), dim3(256), 0, st, g, ra, dbg);
-  else hipLaunchKernelGGL(k_pairs<uint16_t>, dim3(blocks), dim3(256), 0, st, g, ra, dbg);
+  if (g.bpc == 8) hipExtLaunchKernelGGL(k_pairs<uint8_t>, dim3(blocks), dim3(256), 0, st, ev0, ev1, 0, g, ra, dbg);
+  else hipExtLaunchKernelGGL(k_pairs<uint16_t>, dim3(blocks), dim3(256), 0, st, ev0, ev1, 0, g, ra, dbg);
   return hipGetLastError();
 }
 
 hipError_t launch_walk(const Geometry& g, const RowArrays& ra, double* results, uint64_t* units,
-                       unsigned dbg, hipStream_t st) {
-  hipLaunchKernelGGL(k_walk, dim3(3 * g.nframes), dim3(kT), 0, st, g, ra, results, units, dbg);
+                       unsigned dbg, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+  hipExtLaunchKernelGGL(k_walk, dim3(3 * g.nframes), dim3(kT), 0, st, ev0, ev1, 0, g, ra, results, units, dbg);
   return hipGetLastError();
 }
 
