@@ -587,177 +587,236 @@ struct Walker {
 // across [x2, x3), 54 [x3, x4), beyond [x4, n); empty ones are skipped.
 
 constexpr int kEdges = 5;
+constexpr int kFastRows = 9;  // rows per thread in the fast walk: h <= kFastRows * kT
 
 struct FastLds {
-  uint64_t P[kEdges + 2], PC[kEdges + 2];  // exact prefixes at the edges (and at n)
-  int x[kEdges + 2];
-  int xw[kEdges][kWaves];  // per-wave edge minima
-  uint16_t rowbuf[kStage];
-  uint64_t runE[kT];
+  uint64_t P[kEdges + 1];   // exact prefix at each edge (entry kEdges: the total)
+  uint32_t PC[kEdges + 1];  // odd terms before each edge
+  int x[kEdges + 1];        // the edges (entry kEdges: n)
+  uint64_t runE[kT];        // a crossing row's run sums
+  uint32_t term[kStage];    // a crossing row's terms
 };
 
-// Edges of n items (thread t owns items [t*c, t*c + c)); base is the sum
-// before item 0.  Fills fl.x / fl.P / fl.PC (entries 0..4 the edges, 5 = n),
-// the edges made non-decreasing so that the segments tile [0, n).
-template <class EAt, class CAt>
-__device__ __forceinline__ void fast_edges(int n, uint64_t base, uint64_t M, EAt e_at, CAt c_at,
-                                           FastLds& fl, BlockScratch& sm) {
-  const int c = (n + kT - 1) / kT;
-  const int a = min((int)threadIdx.x * c, n), b = min(a + c, n);
-  uint64_t le = 0, lc = 0;
-  for (int k = a; k < b; ++k) {
-    le += e_at(k);
-    lc += c_at(k);
-  }
-  uint64_t P, PC, TE, TC;
-  block_excl_scan2(le, lc, &P, &PC, &TE, &TC, sm);
-  constexpr uint64_t T53 = 1ull << 53, T54 = 1ull << 54, T55 = 1ull << 55;
-  int x[kEdges] = {n, n, n, n, n};
-  {
-    uint64_t q = base + P;
-    for (int k = a; k < b; ++k) {
-      const uint64_t e = e_at(k);
-      const uint64_t lo = q > M ? q - M : 0, hi = q + e + M;
-      if (x[0] == n && q + e > T53) x[0] = k;
-      if (x[1] == n && lo >= T53) x[1] = k;
-      if (x[2] == n && hi >= T54) x[2] = k;
-      if (x[3] == n && lo >= T54) x[3] = k;
-      if (x[4] == n && hi >= T55) x[4] = k;
-      q += e;
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < kEdges; ++j) x[j] = (int)wave_min_u32((uint32_t)x[j]);
-  if ((threadIdx.x & 63) == 0)
-#pragma unroll
-    for (int j = 0; j < kEdges; ++j) fl.xw[j][threadIdx.x >> 6] = x[j];
+// Exclusive block scan of (v, u), their totals, and the block total of z.
+__device__ __forceinline__ void block_scan_vuz(uint64_t v, uint32_t u, uint64_t z, uint64_t* ev,
+                                               uint32_t* eu, uint64_t* tv, uint32_t* tu,
+                                               uint64_t* tz, BlockScratch& sm) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const uint64_t iv = wave_incl_scan_u64(v);
+  const uint32_t iu = wave_incl_scan_u32(u);
+  const uint64_t sz = wave_sum_u64(z);
   __syncthreads();
-#pragma unroll
-  for (int j = 0; j < kEdges; ++j) {
-    int m = fl.xw[j][0];
-#pragma unroll
-    for (int q = 1; q < kWaves; ++q) m = min(m, fl.xw[j][q]);
-    x[j] = j ? max(m, x[j - 1]) : m;
+  if (lane == 63) {
+    sm.w64[2 * wv] = iv;
+    sm.w64[2 * wv + 1] = sz;
+    sm.iv[wv] = (int)iu;
   }
-  // the owners of the edge items record the exact prefixes there
-  {
-    uint64_t q = base + P, qc = PC;
-    for (int k = a; k < b; ++k) {
+  __syncthreads();
+  uint64_t bv = 0, av = 0, az = 0;
+  uint32_t bu = 0, au = 0;
 #pragma unroll
-      for (int j = 0; j < kEdges; ++j)
-        if (x[j] == k) {
-          fl.P[j] = q;
-          fl.PC[j] = qc;
-        }
-      q += e_at(k);
-      qc += c_at(k);
+  for (int k = 0; k < kWaves; ++k) {
+    const uint64_t x = sm.w64[2 * k], y = sm.w64[2 * k + 1];
+    const uint32_t c = (uint32_t)sm.iv[k];
+    bv += k < wv ? x : 0;
+    bu += k < wv ? c : 0;
+    av += x;
+    au += c;
+    az += y;
+  }
+  *ev = bv + iv - v;
+  *eu = bu + iu - u;
+  *tv = av;
+  *tu = au;
+  *tz = az;
+}
+
+// The edges of n items whose values are in registers: thread t owns items
+// [a, a + c) with sums e[] and odd counts cnt[]; eprev() gives the sum of
+// item a - 1 (called after the scan's barriers, only when a > 0); base is
+// the sum before item 0 and M the margin.  With every sum below 2^55 an item's plan follows from where its
+// exact interval [P - M, P + E + M] lies against 2^53, 2^54 and 2^55, and
+// each edge of a plan is the first item at which a non-decreasing quantity
+// reaches a threshold:
+//   x0: P + E > 2^53        (end of the exact items)
+//   x1: P - M >= 2^53       (first item inside the binade of 2^53)
+//   x2: P + E + M >= 2^54   (first item that may leave it)
+//   x3: P - M >= 2^54       (first item inside the binade of 2^54)
+//   x4: P + E + M >= 2^55   (first item that may leave that one)
+// Since each condition is monotone in the item index, exactly one thread
+// sees its edge (the condition false before the item, true at it) and
+// writes it; the thread holding the last item writes the edges that never
+// occur.  Fills fl (entry kEdges: n and the totals); *ztot = block total of
+// z.  Ends with a barrier.
+template <int CMAX, class EPrev>
+__device__ __forceinline__ void edges_reg(int n, int a, int c, const uint64_t (&e)[CMAX],
+                                          const uint32_t (&cnt)[CMAX], EPrev eprev,
+                                          uint64_t base, uint64_t M, uint64_t z, uint64_t* ztot,
+                                          FastLds& fl, BlockScratch& sm) {
+  uint64_t le = 0;
+  uint32_t lc = 0;
+#pragma unroll
+  for (int k = 0; k < CMAX; ++k)
+    if (k < c) {
+      le += e[k];
+      lc += cnt[k];
     }
+  uint64_t P, TE;
+  uint32_t PC, TC;
+  block_scan_vuz(le, lc, z, &P, &PC, &TE, &TC, ztot, sm);
+  constexpr uint64_t T53 = 1ull << 53, T54 = 1ull << 54, T55 = 1ull << 55;
+  uint64_t q = base + P;
+  uint32_t qc = PC;
+  bool p0 = false, p1 = false, p2 = false, p3 = false, p4 = false;  // conditions at item a - 1
+  if (a > 0) {
+    const uint64_t pm = q - eprev(), lo = pm > M ? pm - M : 0;
+    p0 = q > T53;
+    p1 = lo >= T53;
+    p2 = q + M >= T54;
+    p3 = lo >= T54;
+    p4 = q + M >= T55;
   }
-  if (threadIdx.x == 0) {
 #pragma unroll
-    for (int j = 0; j < kEdges; ++j) {
-      fl.x[j] = x[j];
-      if (x[j] == n) {
-        fl.P[j] = base + TE;
-        fl.PC[j] = TC;
+  for (int k = 0; k < CMAX; ++k) {
+    if (k < c) {
+      const uint64_t qn = q + e[k], lo = q > M ? q - M : 0;
+      const bool c0 = qn > T53, c1 = lo >= T53, c2 = qn + M >= T54, c3 = lo >= T54,
+                 c4 = qn + M >= T55;
+      if ((c0 && !p0) | (c1 && !p1) | (c2 && !p2) | (c3 && !p3) | (c4 && !p4)) {
+        const int i = a + k;
+        if (c0 && !p0) fl.x[0] = i, fl.P[0] = q, fl.PC[0] = qc;
+        if (c1 && !p1) fl.x[1] = i, fl.P[1] = q, fl.PC[1] = qc;
+        if (c2 && !p2) fl.x[2] = i, fl.P[2] = q, fl.PC[2] = qc;
+        if (c3 && !p3) fl.x[3] = i, fl.P[3] = q, fl.PC[3] = qc;
+        if (c4 && !p4) fl.x[4] = i, fl.P[4] = q, fl.PC[4] = qc;
       }
+      p0 = c0, p1 = c1, p2 = c2, p3 = c3, p4 = c4;
+      q = qn;
+      qc += cnt[k];
     }
-    fl.x[kEdges] = n;
-    fl.P[kEdges] = base + TE;
-    fl.PC[kEdges] = TC;
+  }
+  if (c > 0 && a + c == n) {
+    const uint64_t T = base + TE;
+    if (!p0) fl.x[0] = n, fl.P[0] = T, fl.PC[0] = TC;
+    if (!p1) fl.x[1] = n, fl.P[1] = T, fl.PC[1] = TC;
+    if (!p2) fl.x[2] = n, fl.P[2] = T, fl.PC[2] = TC;
+    if (!p3) fl.x[3] = n, fl.P[3] = T, fl.PC[3] = TC;
+    if (!p4) fl.x[4] = n, fl.P[4] = T, fl.PC[4] = TC;
+    fl.x[kEdges] = n, fl.P[kEdges] = T, fl.PC[kEdges] = TC;
   }
   __syncthreads();
 }
 
-// The segments of fast_edges, in order: plan of segment g (0 exact, 1
-// across, 2 the binade of 2^53, 3 across, 4 the binade of 2^54, 5 beyond).
+// Segment g of the edges (0 exact, 1 across, 2 the binade of 2^53, 3 across,
+// 4 the binade of 2^54, 5 beyond): its plan.
 __device__ __forceinline__ int fast_plan(int g) {
   return g == 0 ? kPlanExact : g == 2 ? 53 : g == 4 ? 54 : (g == 5 ? -2 : kPlanCross);
 }
 
-// s + t1 + t2 + ... with the CPU's double adds (exact integers in units).
-__device__ __forceinline__ uint64_t add_terms_f64(uint64_t s, const uint16_t* x, int j0, int j1) {
-  double d = (double)s;  // s is a double the CPU could hold: exact
-  for (int j = j0; j < j1; ++j) d = d + (double)fsq_units(x[j]);
-  return (uint64_t)d;
+// Applies segment g's exact, closed-form or beyond plan to s (Eg, Cg its
+// exact sum and odd count); returns false when it does not apply.
+__device__ __forceinline__ bool fast_apply(uint64_t* s, int g, uint64_t Eg, uint64_t Cg) {
+  const int e = fast_plan(g);
+  if (e == kPlanExact) return try_exact(s, Eg);
+  if (e == 53 || e == 54) return try_apply(s, closed_pair(Eg, Cg, e), e);
+  return false;
 }
 
-// Row i planned across an edge, from S: kT runs, closed forms, the runs
-// across an edge term by term.  Returns false when it needs the general walk.
+// Row i planned across an edge, from S = *sp: one run of L consecutive
+// terms per thread, the runs' edges, closed forms, and the runs across an
+// edge term by term with the double add (the CPU's step).  Returns false
+// when the row needs the general walk.
 __device__ bool fast_cross_row(uint64_t* sp, int i, const void* plane, long stride, int w,
                                int bpc8, FastLds& fl, BlockScratch& sm) {
+  constexpr int LMAX = kStage / kT;
   if (w > kStage) return false;
   const uint64_t s0 = *sp;
-  __syncthreads();
-  {
-    const long base = (long)i * stride;
-    constexpr int U = kStage / kT;
-    uint32_t v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = threadIdx.x + u * kT;
-      v[u] = j < w ? (bpc8 ? ((const uint8_t*)plane)[base + j] : ((const uint16_t*)plane)[base + j]) : 0u;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = threadIdx.x + u * kT;
-      if (j < w) fl.rowbuf[j] = (uint16_t)v[u];
-    }
-  }
   const int L = (w + kT - 1) / kT;
   const int t = threadIdx.x;
-  const int j0 = min(t * L, w), j1 = min(j0 + L, w);
-  __syncthreads();
-  uint32_t c = 0;
-  uint64_t E = 0;
-  for (int j = j0; j < j1; ++j) {
-    const uint32_t x = fsq_units(fl.rowbuf[j]);
-    E += x;
-    c += x & 1u;
+  const int j0 = min(t * L, w), n = min(j0 + L, w) - j0;
+  const long base = (long)i * stride + j0;
+  uint32_t x[LMAX];
+#pragma unroll
+  for (int k = 0; k < LMAX; ++k)  // every load issued before the first use
+    x[k] = k < n ? (bpc8 ? ((const uint8_t*)plane)[base + k] : ((const uint16_t*)plane)[base + k])
+                 : 0u;
+  uint32_t tk[LMAX];
+  uint64_t E[1] = {0};
+  uint32_t c[1] = {0};
+#pragma unroll
+  for (int k = 0; k < LMAX; ++k) {
+    tk[k] = fsq_units(x[k]);  // 0 past the run's end
+    E[0] += tk[k];
+    c[0] += tk[k] & 1u;
   }
+  __syncthreads();  // every read of the previous row's terms and run sums is done
+#pragma unroll
+  for (int k = 0; k < LMAX; ++k)
+    if (k < n) fl.term[j0 + k] = tk[k];
+  fl.runE[t] = E[0];  // visible after the scan's barriers
   const int eB = (s0 < kTwo53 ? 53 : binade(s0)) + 1;
   const uint64_t Mr = (uint64_t)w << (eB - 53);
-  fast_edges(
-      kT, s0, Mr, [&](int) { return E; }, [&](int) { return (uint64_t)c; }, fl, sm);
+  uint64_t unused;
+  edges_reg<1>(
+      kT, t, 1, E, c, [&] { return fl.runE[t - 1]; }, s0, Mr, 0, &unused, fl, sm);
   uint64_t s = s0;
   int a = 0;
+  uint64_t Pa = s0, PCa = 0;
+#pragma unroll
   for (int g = 0; g <= kEdges; ++g) {
-    const int b = fl.x[g] > a ? fl.x[g] : a;  // edges are non-decreasing
+    const int b = fl.x[g];
+    const uint64_t Pb = fl.P[g], PCb = fl.PC[g];
+    if (b < a) return false;  // edges out of order: not the premise
     if (b > a) {
-      const int e = fast_plan(g);
-      const uint64_t Pa = g == 0 ? s0 : fl.P[g - 1], PCa = g == 0 ? 0 : fl.PC[g - 1];
-      const uint64_t Eg = fl.P[g] - Pa, Cg = fl.PC[g] - PCa;
-      if (e == kPlanExact) {
-        if (!try_exact(&s, Eg)) return false;
-      } else if (e == 53 || e == 54) {
-        if (!try_apply(&s, closed_pair(Eg, Cg, e), e)) return false;
-      } else if (e == kPlanCross) {
-        s = add_terms_f64(s, fl.rowbuf, min(a * L, w), min(b * L, w));
-      } else {
+      if (g == 1 || g == 3) {
+        double d = (double)s;  // a value the CPU's double holds: exact
+        const int t1 = min(b * L, w);
+        for (int j = min(a * L, w); j < t1; ++j) d = d + (double)fl.term[j];
+        s = (uint64_t)d;
+      } else if (!fast_apply(&s, g, Pb - Pa, PCb - PCa)) {
         return false;
       }
     }
     a = b;
+    Pa = Pb;
+    PCa = PCb;
   }
   *sp = s;
   return true;
 }
 
-// The plane's rows are in rows.R / rows.C (h <= kChunk).  Returns false when
-// the plane needs the general walk.  Margin: with every sum below 2^55 the
-// CPU's sum strays from the exact prefix by at most 2 units per term added
-// past 2^53.
-__device__ bool fast_walk(uint64_t* out, uint64_t* exact, int h, const void* plane, long stride,
-                          int w, int bpc8, RowLds& rows, FastLds& fl, BlockScratch& sm) {
+// The fast walk of one plane (h <= kFastRows * kT, every sum below 2^55):
+// thread t holds rows [t*c, t*c + c) in registers.  Margin: with every sum
+// below 2^55 the CPU's sum strays from the exact prefix by at most 2 units
+// per term added past 2^53.  Returns false when the plane needs the general
+// walk; *exact and *s1 are set either way.
+__device__ bool fast_walk(uint64_t* out, uint64_t* exact, uint64_t* s1, const uint64_t* R,
+                          const uint32_t* C, const uint32_t* R1, int h, const void* plane,
+                          long stride, int w, int bpc8, FastLds& fl, BlockScratch& sm) {
+  const int cr = (h + kT - 1) / kT;
+  const int a = min((int)threadIdx.x * cr, h), c = min(cr, h - a);
+  uint64_t e[kFastRows];
+  uint32_t cnt[kFastRows];
+  uint64_t z = 0;
+  uint32_t z1[kFastRows];
+#pragma unroll
+  for (int k = 0; k < kFastRows; ++k) {  // every load issued before the first use
+    e[k] = k < c ? R[a + k] : 0;
+    cnt[k] = k < c ? C[a + k] : 0;
+    z1[k] = k < c ? R1[a + k] : 0;
+  }
+  const uint64_t eprev = a > 0 ? R[a - 1] : 0;
+#pragma unroll
+  for (int k = 0; k < kFastRows; ++k) z += z1[k];
   const uint64_t M = 2ull * (uint64_t)w * (uint64_t)h;
-  fast_edges(
-      h, 0, M, [&](int k) { return rows.R[k]; }, [&](int k) { return (uint64_t)rows.C[k]; },
-      fl, sm);
+  edges_reg<kFastRows>(
+      h, a, c, e, cnt, [&] { return eprev; }, 0, M, z, s1, fl, sm);
   const uint64_t E = fl.P[kEdges];
   *exact = E;
   if (E >= (1ull << 55)) return false;
   int x[kEdges + 1];
-  uint64_t P[kEdges + 1], PC[kEdges + 1];
+  uint64_t P[kEdges + 1];
+  uint32_t PC[kEdges + 1];
 #pragma unroll
   for (int j = 0; j <= kEdges; ++j) {
     x[j] = fl.x[j];
@@ -765,25 +824,23 @@ __device__ bool fast_walk(uint64_t* out, uint64_t* exact, int h, const void* pla
     PC[j] = fl.PC[j];
   }
   uint64_t s = 0;
-  int a = 0;
+  int ia = 0;
+  uint64_t Pa = 0, PCa = 0;
+#pragma unroll
   for (int g = 0; g <= kEdges; ++g) {
-    const int b = x[g] > a ? x[g] : a;
-    if (b > a) {
-      const int e = fast_plan(g);
-      const uint64_t Pa = g == 0 ? 0 : P[g - 1], PCa = g == 0 ? 0 : PC[g - 1];
-      const uint64_t Eg = P[g] - Pa, Cg = PC[g] - PCa;
-      if (e == kPlanExact) {
-        if (!try_exact(&s, Eg)) return false;
-      } else if (e == 53 || e == 54) {
-        if (!try_apply(&s, closed_pair(Eg, Cg, e), e)) return false;
-      } else if (e == kPlanCross) {
-        for (int i = a; i < b; ++i)
+    const int b = x[g];
+    if (b < ia) return false;  // edges out of order: not the premise
+    if (b > ia) {
+      if (g == 1 || g == 3) {
+        for (int i = ia; i < b; ++i)
           if (!fast_cross_row(&s, i, plane, stride, w, bpc8, fl, sm)) return false;
-      } else {
+      } else if (!fast_apply(&s, g, P[g] - Pa, PC[g] - PCa)) {
         return false;
       }
     }
-    a = b;
+    ia = b;
+    Pa = P[g];
+    PCa = PC[g];
   }
   *out = s;
   return true;
@@ -894,40 +951,18 @@ __global__ void __launch_bounds__(kT) k_walk(Geometry g, RowArrays ra, double* r
     E = S = block_sum_u64(b, sm);
   } else {
     bool fast = false;
-    if (dbg == 0 && g.h <= kChunk) {
-      uint64_t a = 0;
-      {
-        constexpr int U = (kChunk + kT - 1) / kT;
-        uint64_t rv[U];
-        uint32_t cv[U], sv[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {  // every load issued before the first use
-          const int i = threadIdx.x + u * kT;
-          rv[u] = i < g.h ? ra.r2[off + i] : 0;
-          cv[u] = i < g.h ? ra.codd[off + i] : 0;
-          sv[u] = i < g.h ? ra.r1[off + i] : 0;
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int i = threadIdx.x + u * kT;
-          if (i < g.h) {
-            rows.R[i] = rv[u];
-            rows.C[i] = (uint16_t)cv[u];
-          }
-          a += sv[u];
-        }
-      }
-      s1 = block_sum_u64(a, sm);  // also the barrier before the rows are read
+    if (dbg == 0 && g.h <= kFastRows * kT) {
       const char* plane = (const char*)(pl == 0 ? g.ref : g.dis) +
                           (long)f * g.pitch * (g.bpc == 8 ? 1 : 2);
-      fast = fast_walk(&S, &E, g.h, plane, g.stride, g.w, g.bpc == 8, rows, fl, sm);
+      fast = fast_walk(&S, &E, &s1, ra.r2 + off, ra.codd + off, ra.r1 + off, g.h, plane,
+                       g.stride, g.w, g.bpc == 8, fl, sm);
     }
     if (!fast) {
       const char* plane = (const char*)(pl == 0 ? g.ref : g.dis) +
                           (long)f * g.pitch * (g.bpc == 8 ? 1 : 2);
       general_walk(plane, g.stride, g.w, g.h, g.bpc == 8, ra.r2 + off, ra.codd + off,
                    ra.r1 + off, ra.plan + off, ra.pairs + 2 * off, dbg, sm, rows, runs, rseg,
-                   useg, fl.rowbuf, &staged, res);
+                   useg, reinterpret_cast<uint16_t*>(fl.term), &staged, res);
       S = res[0];
       E = res[1];
       s1 = res[2];

@@ -80,6 +80,11 @@ __device__ __forceinline__ uint64_t dpp64_or0(uint64_t v) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ uint32_t dpp32_or0(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWMASK, 0xF, false);
+}
+
 // Inclusive prefix sum over the 64 lanes: row_shr 1, 2, 4, 8 inside each row
 // of 16 lanes, then row_bcast:15 into rows 1 and 3 and row_bcast:31 into
 // rows 2 and 3.
@@ -90,6 +95,16 @@ __device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v) {
   v += dpp64_or0<0x118, 0xF>(v);
   v += dpp64_or0<0x142, 0xA>(v);
   v += dpp64_or0<0x143, 0xC>(v);
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
+  v += dpp32_or0<0x111, 0xF>(v);
+  v += dpp32_or0<0x112, 0xF>(v);
+  v += dpp32_or0<0x114, 0xF>(v);
+  v += dpp32_or0<0x118, 0xF>(v);
+  v += dpp32_or0<0x142, 0xA>(v);
+  v += dpp32_or0<0x143, 0xC>(v);
   return v;
 }
 
