@@ -665,43 +665,48 @@ __device__ __forceinline__ void edges_reg(int n, int a, int c, const uint64_t (&
   uint32_t PC, TC;
   block_scan_vuz(le, lc, z, &P, &PC, &TE, &TC, ztot, sm);
   constexpr uint64_t T53 = 1ull << 53, T54 = 1ull << 54, T55 = 1ull << 55;
-  uint64_t q = base + P;
-  uint32_t qc = PC;
-  bool p0 = false, p1 = false, p2 = false, p3 = false, p4 = false;  // conditions at item a - 1
-  if (a > 0) {
-    const uint64_t pm = q - eprev(), lo = pm > M ? pm - M : 0;
-    p0 = q > T53;
-    p1 = lo >= T53;
-    p2 = q + M >= T54;
-    p3 = lo >= T54;
-    p4 = q + M >= T55;
-  }
+  // The five conditions of item k, from P_k (lo side) and P_{k+1} (hi side).
+  auto conds = [&](uint64_t pk, uint64_t pk1) {
+    const uint64_t lo = pk > M ? pk - M : 0;
+    return (unsigned)(pk1 > T53) | (unsigned)(lo >= T53) << 1 | (unsigned)(pk1 + M >= T54) << 2 |
+           (unsigned)(lo >= T54) << 3 | (unsigned)(pk1 + M >= T55) << 4;
+  };
+  const uint64_t q0 = base + P, qend = q0 + le;
+  uint64_t elast = 0;
 #pragma unroll
-  for (int k = 0; k < CMAX; ++k) {
-    if (k < c) {
-      const uint64_t qn = q + e[k], lo = q > M ? q - M : 0;
-      const bool c0 = qn > T53, c1 = lo >= T53, c2 = qn + M >= T54, c3 = lo >= T54,
-                 c4 = qn + M >= T55;
-      if ((c0 && !p0) | (c1 && !p1) | (c2 && !p2) | (c3 && !p3) | (c4 && !p4)) {
-        const int i = a + k;
-        if (c0 && !p0) fl.x[0] = i, fl.P[0] = q, fl.PC[0] = qc;
-        if (c1 && !p1) fl.x[1] = i, fl.P[1] = q, fl.PC[1] = qc;
-        if (c2 && !p2) fl.x[2] = i, fl.P[2] = q, fl.PC[2] = qc;
-        if (c3 && !p3) fl.x[3] = i, fl.P[3] = q, fl.PC[3] = qc;
-        if (c4 && !p4) fl.x[4] = i, fl.P[4] = q, fl.PC[4] = qc;
+  for (int k = 0; k < CMAX; ++k)
+    if (k == c - 1) elast = e[k];
+  // Conditions at item a - 1 and at the chunk's last item; an edge lies in
+  // this chunk when it is false before the chunk and true at its end.
+  const unsigned before = a > 0 ? conds(q0 - eprev(), q0) : 0u;
+  const unsigned last = c > 0 ? conds(qend - elast, qend) : before;
+  const unsigned own = last & ~before;
+  if (own) {  // a few threads: find each owned edge's item
+    uint64_t q = q0;
+    uint32_t qc = PC;
+    unsigned seen = before;
+#pragma unroll
+    for (int k = 0; k < CMAX; ++k) {
+      if (k < c) {
+        const uint64_t qn = q + e[k];
+        const unsigned now = conds(q, qn), fresh = now & ~seen;
+        if (fresh) {
+          const int i = a + k;
+#pragma unroll
+          for (int j = 0; j < kEdges; ++j)
+            if (fresh >> j & 1u) fl.x[j] = i, fl.P[j] = q, fl.PC[j] = qc;
+        }
+        seen = now;
+        q = qn;
+        qc += cnt[k];
       }
-      p0 = c0, p1 = c1, p2 = c2, p3 = c3, p4 = c4;
-      q = qn;
-      qc += cnt[k];
     }
   }
   if (c > 0 && a + c == n) {
     const uint64_t T = base + TE;
-    if (!p0) fl.x[0] = n, fl.P[0] = T, fl.PC[0] = TC;
-    if (!p1) fl.x[1] = n, fl.P[1] = T, fl.PC[1] = TC;
-    if (!p2) fl.x[2] = n, fl.P[2] = T, fl.PC[2] = TC;
-    if (!p3) fl.x[3] = n, fl.P[3] = T, fl.PC[3] = TC;
-    if (!p4) fl.x[4] = n, fl.P[4] = T, fl.PC[4] = TC;
+#pragma unroll
+    for (int j = 0; j < kEdges; ++j)
+      if (!(last >> j & 1u)) fl.x[j] = n, fl.P[j] = T, fl.PC[j] = TC;
     fl.x[kEdges] = n, fl.P[kEdges] = T, fl.PC[kEdges] = TC;
   }
   __syncthreads();
@@ -722,36 +727,42 @@ __device__ __forceinline__ bool fast_apply(uint64_t* s, int g, uint64_t Eg, uint
   return false;
 }
 
-// Row i planned across an edge, from S = *sp: one run of L consecutive
-// terms per thread, the runs' edges, closed forms, and the runs across an
-// edge term by term with the double add (the CPU's step).  Returns false
-// when the row needs the general walk.
-__device__ bool fast_cross_row(uint64_t* sp, int i, const void* plane, long stride, int w,
-                               int bpc8, FastLds& fl, BlockScratch& sm) {
-  constexpr int LMAX = kStage / kT;
-  if (w > kStage) return false;
+constexpr int kRunMax = kStage / kT;  // terms per run in a crossing row
+
+// The L consecutive samples of thread t's run of row i, into registers.
+__device__ __forceinline__ void load_run(uint32_t (&x)[kRunMax], int i, const void* plane,
+                                         long stride, int w, int bpc8) {
+  const int L = (w + kT - 1) / kT;
+  const int j0 = min((int)threadIdx.x * L, w), n = min(j0 + L, w) - j0;
+  const long base = (long)i * stride + j0;
+#pragma unroll
+  for (int k = 0; k < kRunMax; ++k)  // every load issued before the first use
+    x[k] = k < n ? (bpc8 ? ((const uint8_t*)plane)[base + k] : ((const uint16_t*)plane)[base + k])
+                 : 0u;
+}
+
+// Row i planned across an edge, from S = *sp, its run samples in x: one run
+// of L consecutive terms per thread, the runs' edges, closed forms, and the
+// runs across an edge term by term with the double add (the CPU's step).
+// Returns false when the row needs the general walk (w <= kStage).
+__device__ bool fast_cross_row(uint64_t* sp, const uint32_t (&x)[kRunMax], int w, FastLds& fl,
+                               BlockScratch& sm) {
   const uint64_t s0 = *sp;
   const int L = (w + kT - 1) / kT;
   const int t = threadIdx.x;
   const int j0 = min(t * L, w), n = min(j0 + L, w) - j0;
-  const long base = (long)i * stride + j0;
-  uint32_t x[LMAX];
-#pragma unroll
-  for (int k = 0; k < LMAX; ++k)  // every load issued before the first use
-    x[k] = k < n ? (bpc8 ? ((const uint8_t*)plane)[base + k] : ((const uint16_t*)plane)[base + k])
-                 : 0u;
-  uint32_t tk[LMAX];
+  uint32_t tk[kRunMax];
   uint64_t E[1] = {0};
   uint32_t c[1] = {0};
 #pragma unroll
-  for (int k = 0; k < LMAX; ++k) {
+  for (int k = 0; k < kRunMax; ++k) {
     tk[k] = fsq_units(x[k]);  // 0 past the run's end
     E[0] += tk[k];
     c[0] += tk[k] & 1u;
   }
   __syncthreads();  // every read of the previous row's terms and run sums is done
 #pragma unroll
-  for (int k = 0; k < LMAX; ++k)
+  for (int k = 0; k < kRunMax; ++k)
     if (k < n) fl.term[j0 + k] = tk[k];
   fl.runE[t] = E[0];  // visible after the scan's barriers
   const int eB = (s0 < kTwo53 ? 53 : binade(s0)) + 1;
@@ -770,8 +781,17 @@ __device__ bool fast_cross_row(uint64_t* sp, int i, const void* plane, long stri
     if (b > a) {
       if (g == 1 || g == 3) {
         double d = (double)s;  // a value the CPU's double holds: exact
-        const int t1 = min(b * L, w);
-        for (int j = min(a * L, w); j < t1; ++j) d = d + (double)fl.term[j];
+        const int t0 = min(a * L, w), t1 = min(b * L, w);
+        if (t1 - t0 <= kRunMax) {  // one run: its terms first, then the adds
+          uint32_t v[kRunMax];
+#pragma unroll
+          for (int k = 0; k < kRunMax; ++k) v[k] = t0 + k < t1 ? fl.term[t0 + k] : 0u;
+#pragma unroll
+          for (int k = 0; k < kRunMax; ++k)
+            if (t0 + k < t1) d = d + (double)v[k];
+        } else {
+          for (int j = t0; j < t1; ++j) d = d + (double)fl.term[j];
+        }
         s = (uint64_t)d;
       } else if (!fast_apply(&s, g, Pb - Pa, PCb - PCa)) {
         return false;
@@ -823,6 +843,14 @@ __device__ bool fast_walk(uint64_t* out, uint64_t* exact, uint64_t* s1, const ui
     P[j] = fl.P[j];
     PC[j] = fl.PC[j];
   }
+  if (w > kStage) {
+    if (x[0] < x[1] || x[2] < x[3]) return false;  // rows across an edge, too wide
+  }
+  // the first row of each stretch across an edge, loaded before it is needed
+  uint32_t xa[kRunMax], xb[kRunMax];
+  const int ra = x[0] < x[1] ? x[0] : -1, rb = x[2] < x[3] ? x[2] : -1;
+  if (ra >= 0) load_run(xa, ra, plane, stride, w, bpc8);
+  if (rb >= 0) load_run(xb, rb, plane, stride, w, bpc8);
   uint64_t s = 0;
   int ia = 0;
   uint64_t Pa = 0, PCa = 0;
@@ -832,8 +860,17 @@ __device__ bool fast_walk(uint64_t* out, uint64_t* exact, uint64_t* s1, const ui
     if (b < ia) return false;  // edges out of order: not the premise
     if (b > ia) {
       if (g == 1 || g == 3) {
-        for (int i = ia; i < b; ++i)
-          if (!fast_cross_row(&s, i, plane, stride, w, bpc8, fl, sm)) return false;
+        for (int i = ia; i < b; ++i) {
+          bool ok;
+          if (i == (g == 1 ? ra : rb)) {
+            ok = fast_cross_row(&s, g == 1 ? xa : xb, w, fl, sm);
+          } else {
+            uint32_t xi[kRunMax];
+            load_run(xi, i, plane, stride, w, bpc8);
+            ok = fast_cross_row(&s, xi, w, fl, sm);
+          }
+          if (!ok) return false;
+        }
       } else if (!fast_apply(&s, g, P[g] - Pa, PC[g] - PCa)) {
         return false;
       }
@@ -843,6 +880,90 @@ __device__ bool fast_walk(uint64_t* out, uint64_t* exact, uint64_t* s1, const ui
     PCa = PC[g];
   }
   *out = s;
+  return true;
+}
+
+// Pair of one noise row t inside binade e (sh = e - 52, u = 2^sh): the
+// double add moves S by t rounded to a multiple of u, ties to the even
+// multiple, which depends on S only through its parity p = (S / u) mod 2.
+// With v = p * u standing in for S: RNE_u(v + t) - v for p = 0 and 1.
+__device__ __forceinline__ Pair64 noise_row_pair(uint64_t t, int sh) {
+  const uint64_t u = 1ull << sh, half = u >> 1;
+  const uint64_t z0 = t, z1 = u + t;
+  const uint64_t r0 = (z0 + (half - 1) + ((z0 >> sh) & 1)) & ~(u - 1);
+  const uint64_t r1 = (z1 + (half - 1) + ((z1 >> sh) & 1)) & ~(u - 1);
+  return Pair64{r0, r1 - u};
+}
+
+// The fast PSNR noise (h <= kChunk, every sum below 2^55): rows in
+// registers and in stash[], the same edges as the moment walk with margin
+// 2 per row (each add past 2^53 rounds by at most u/2 <= 2 units below
+// 2^55), exact rows added as integers, rows across an edge added with the
+// double add, and each stretch of rows inside one binade applied as one
+// pair composed in row order.  Returns false when it does not apply.
+__device__ bool fast_noise(double* out, uint64_t* exact, const uint64_t* RN, int h,
+                           uint64_t* stash, FastLds& fl, BlockScratch& sm) {
+  const int cr = (h + kT - 1) / kT;
+  const int a = min((int)threadIdx.x * cr, h), c = min(cr, h - a);
+  constexpr int CM = (kChunk + kT - 1) / kT;
+  uint64_t e[CM];
+  uint32_t cnt[CM];
+#pragma unroll
+  for (int k = 0; k < CM; ++k) {  // every load issued before the first use
+    e[k] = k < c ? RN[a + k] : 0;
+    cnt[k] = 0;
+  }
+  const uint64_t eprev = a > 0 ? RN[a - 1] : 0;
+  __syncthreads();  // earlier readers of stash are done
+#pragma unroll
+  for (int k = 0; k < CM; ++k)
+    if (k < c) stash[a + k] = e[k];  // visible after the scan's barriers
+  uint64_t unused;
+  edges_reg<CM>(
+      h, a, c, e, cnt, [&] { return eprev; }, 0, 2ull * (uint64_t)h, 0, &unused, fl, sm);
+  const uint64_t E = fl.P[kEdges];
+  *exact = E;
+  if (E >= (1ull << 55)) return false;
+  int x[kEdges + 1];
+  uint64_t P[kEdges + 1];
+#pragma unroll
+  for (int j = 0; j <= kEdges; ++j) {
+    x[j] = fl.x[j];
+    P[j] = fl.P[j];
+  }
+  uint64_t s = 0;
+  int ia = 0;
+  uint64_t Pa = 0;
+#pragma unroll
+  for (int g = 0; g <= kEdges; ++g) {
+    const int b = x[g];
+    if (b < ia) return false;  // edges out of order: not the premise
+    if (b > ia) {
+      const int ep = fast_plan(g);
+      if (ep == kPlanExact) {
+        if (!try_exact(&s, P[g] - Pa)) return false;
+      } else if (ep == kPlanCross) {
+        double d = (double)s;  // a value the CPU's double holds: exact
+        for (int i = ia; i < b; ++i) d = d + (double)stash[i];
+        s = (uint64_t)d;
+      } else if (ep == 53 || ep == 54) {
+        const int sh = ep - 52;
+        Pair64 acc = pair64_id();
+#pragma unroll
+        for (int k = 0; k < CM; ++k) {
+          const int i = a + k;
+          if (k < c && i >= ia && i < b) acc = then64(acc, noise_row_pair(e[k], sh), sh);
+        }
+        const Pair64 pr = block_then(acc, sh, sm);
+        if (!try_apply(&s, pr, ep)) return false;
+      } else {
+        return false;
+      }
+    }
+    ia = b;
+    Pa = P[g];
+  }
+  *out = (double)s;  // an integer the CPU's double holds: exact
   return true;
 }
 
@@ -928,7 +1049,10 @@ __global__ void __launch_bounds__(kT) k_walk(Geometry g, RowArrays ra, double* r
   const double n = (double)g.w * (double)g.h;
   if (job == 2) {
     uint64_t ex;
-    const double d = noise_chain(ra.rn + (long)f * g.h, g.h, sm, rows.R, &ex);
+    double d;
+    const uint64_t* RN = ra.rn + (long)f * g.h;
+    if (!(dbg == 0 && g.may_round && g.h <= kChunk && fast_noise(&d, &ex, RN, g.h, rows.R, fl, sm)))
+      d = noise_chain(RN, g.h, sm, rows.R, &ex);
     if (threadIdx.x == 0) {
       const double noise = d * (1.0 / (double)(1u << (2 * k)));
       results[6 * f + 4] = noise;

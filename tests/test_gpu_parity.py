@@ -175,6 +175,18 @@ def test_past_2_55_4096x2560(api, orc):
     check_batch(api, orc, ref, dis, 16, label="4096x2560 past 2^55")
 
 
+def test_noise_past_2_54(api, orc):
+    """ref high, dis low: the PSNR noise passes 2^54 units below 2^55, so its
+    row adds round in the binades of 2^53 and 2^54 (ADR-1499, Decision:
+    every rounding past 2^53, ties included, is the CPU's)."""
+    rng = np.random.Generator(np.random.PCG64(5454))
+    ref = rng.integers(48000, 65536, size=(2, 2160, 3840)).astype(np.uint16)
+    dis = rng.integers(0, 16000, size=(2, 2160, 3840)).astype(np.uint16)
+    units = api.bef_frames_units(dev(ref), dev(dis), 16)
+    assert ((units[:, 6] >= 1 << 54) & (units[:, 6] < 1 << 55)).all(), units[:, 6]
+    check_batch(api, orc, ref, dis, 16, label="noise past 2^54")
+
+
 def test_async_matches_sync(api, orc):
     import torch
     ref, dis = synth.make_frames(5, frames=3)
