@@ -111,9 +111,10 @@ const char *bef_last_error(void);
 #define BEF_DBG_NO_CLOSED_FORM 32u
 unsigned bef_debug_set(unsigned flags);
 
-/* Kernel timing: when enabled, the library records HIP events around each
- * kernel it launches (on the stream it launches on) and accumulates their
- * durations.  kernel: 0 row sums, 1 plan, 2 row pairs, 3 walk.
+/* Kernel timing: when enabled, each kernel the library launches carries a
+ * start and a stop HIP event recorded by its own dispatch (on the stream
+ * it is launched on), and the library accumulates their durations.
+ * kernel: 0 row sums, 1 plan, 2 row pairs, 3 walk.
  * bef_timing_read returns the summed milliseconds and launch count since
  * the last reset (0 / -EINVAL). */
 int bef_timing_enable(int on);
