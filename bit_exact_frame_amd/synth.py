@@ -114,3 +114,54 @@ def uniform_planes(seed: int, frames: int, h: int, w: int, stride: int,
     ref[:, :, :w] = rng.integers(lo, top, size=(frames, h, w))
     dis[:, :, :w] = rng.integers(lo, top, size=(frames, h, w))
     return ref, dis
+
+
+# ---------------------------------------------------------------------------
+# Smooth 8-bit content widened to 16 bits (stand-in for real footage widened
+# three ways: ADR-1497, Consequences).  The 8-bit picture is a seeded sum of
+# a few low-frequency waves and a gradient, plus a little noise, with a
+# brightness that steps by frame so that the widened frames' second-moment
+# sums fall on both sides of 2^53 units, and a dark band in the bottom rows
+# (small codewords: odd float squares once the sum is past 2^53); the
+# distorted picture is the same scene shifted by one pixel with its own
+# noise.  Widening: "shift" x << 8, "x257" x * 257 (full range), "dither"
+# x << 8 plus a seeded uniform low byte.
+
+WIDEN_MODES = ("shift", "x257", "dither")
+
+
+def smooth_8bit(seed: int, h: int, w: int, shift: int = 0) -> np.ndarray:
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([SEED, 313, seed])))
+    yy, xx = np.mgrid[0:h, 0:w].astype(np.float64)
+    xx = xx + shift
+    img = 40.0 + 30.0 * (seed // 2 % 4) + 120.0 * (xx / w) * (1.0 - 0.5 * yy / h)
+    for _ in range(4):
+        fx, fy = rng.uniform(0.5, 6.0, size=2)
+        ph = rng.uniform(0, 2 * np.pi)
+        amp = rng.uniform(10.0, 35.0)
+        img += amp * np.sin(2 * np.pi * (fx * xx / w + fy * yy / h) + ph)
+    img += rng.normal(0.0, 2.0, size=(h, w))
+    img[int(0.85 * h):] *= 0.06  # a dark band at the bottom (codewords below 16)
+    return np.clip(np.rint(img), 0, 255).astype(np.int64)
+
+
+def widened_frames(mode: str, frames: int, h: int = 2160, w: int = 3840):
+    """(ref, dis) uint16 arrays (frames, h, w) of smooth content widened by
+    ``mode`` (one of WIDEN_MODES)."""
+    if mode not in WIDEN_MODES:
+        raise KeyError(mode)
+    ref = np.empty((frames, h, w), np.uint16)
+    dis = np.empty((frames, h, w), np.uint16)
+    for k in range(frames):
+        r8 = smooth_8bit(2 * k, h, w)
+        d8 = smooth_8bit(2 * k + 1, h, w, shift=1)
+        if mode == "shift":
+            r, d = r8 << 8, d8 << 8
+        elif mode == "x257":
+            r, d = r8 * 257, d8 * 257
+        else:
+            rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([SEED, 314, k])))
+            r = (r8 << 8) | rng.integers(0, 256, size=(h, w))
+            d = (d8 << 8) | rng.integers(0, 256, size=(h, w))
+        ref[k], dis[k] = r, d
+    return ref, dis

@@ -187,6 +187,18 @@ def test_noise_past_2_54(api, orc):
     check_batch(api, orc, ref, dis, 16, label="noise past 2^54")
 
 
+@pytest.mark.parametrize("mode", synth.WIDEN_MODES)
+def test_widened_smooth_content(api, orc, mode):
+    """Smooth 8-bit content widened to 16 bits three ways (ADR-1497,
+    Consequences): by a shift (every square exact past 2^53), by 257 and
+    with a dithered low byte (odd squares in a dark band past 2^53).  Four
+    frames whose sums fall on both sides of 2^53 units."""
+    ref, dis = synth.widened_frames(mode, 4)
+    units = api.bef_frames_units(dev(ref), dev(dis), 16)
+    assert (units[:, 2] > 1 << 53).any() and (units[:, 2] < 1 << 53).any()
+    check_batch(api, orc, ref, dis, 16, label=f"widened {mode}")
+
+
 def test_async_matches_sync(api, orc):
     import torch
     ref, dis = synth.make_frames(5, frames=3)
