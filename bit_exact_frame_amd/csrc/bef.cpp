@@ -176,6 +176,37 @@ hipError_t timed(int kernel, F launch) {
   return e;
 }
 
+// Load shape of the 16-bit row kernel: bytes per load (16, 8 or 4, as the
+// row starts allow) and load slots per lane per group (4, 5 or 8).  A wave
+// spreads a row's whole chunks over its 64 lanes in groups of 64 * ng; the
+// shape that leaves the fewest idle bytes in the last group wins, then the
+// one with wider loads.
+void load_shape(const void* ref, const void* dis, int w, ptrdiff_t stride, ptrdiff_t pitch,
+                int nframes, int* cb_out, int* ng_out) {
+  uint64_t al = 16;
+  auto limit = [&](uint64_t v) {
+    while (al > 1 && v % al) al >>= 1;
+  };
+  limit((uintptr_t)ref);
+  limit((uintptr_t)dis);
+  limit((uint64_t)stride * 2);
+  if (nframes > 1) limit((uint64_t)pitch * 2);
+  int best_cb = 0, best_ng = 1;
+  uint64_t best_idle = ~0ull;
+  for (int cb = 16; cb >= 4; cb >>= 1) {
+    if ((uint64_t)cb > al) continue;
+    const uint64_t nc = (uint64_t)w * 2 / cb;
+    if (nc == 0) continue;
+    const uint64_t nper = (nc + 63) / 64;
+    for (int ng : {8, 5, 4}) {
+      const uint64_t idle = (((nper + ng - 1) / ng) * ng * 64 - nc) * cb;
+      if (idle < best_idle) best_cb = cb, best_ng = ng, best_idle = idle;
+    }
+  }
+  *cb_out = best_cb;
+  *ng_out = best_ng;
+}
+
 struct Call {
   Geometry g;
   int dev;
@@ -206,6 +237,9 @@ int prepare(Call& c, const void* ref, const void* dis, int w, int h, ptrdiff_t s
   g.bpc = bpc;
   g.vec = ((uintptr_t)ref % 16 == 0) && ((uintptr_t)dis % 16 == 0) &&
           ((long)stride * B) % 16 == 0 && (nframes == 1 || ((long)pitch * B) % 16 == 0);
+  g.cb = 0;
+  g.ng = 1;
+  if (bpc != 8) load_shape(ref, dis, w, stride, pitch, nframes, &g.cb, &g.ng);
   // Largest possible exact plane sum: every sample at the container's top.
   const uint64_t tmax = bpc == 8 ? 65025ull : 0xFFFE0000ull;
   const uint64_t maxsum = (uint64_t)w * (uint64_t)h * tmax;

@@ -25,7 +25,8 @@ namespace {
 struct Acc16 {
   double m2r0, m2r1, m2d0, m2d1, mn0, mn1;  // float squares, exact in f64
   uint32_t s1r, s1d;                        // first-moment sums
-  us2 oddr, oddd;                           // odd squares (per half-word)
+  uint32_t ob;          // odd squares, per byte: ref even, ref odd, dis even, dis odd
+  uint32_t oddr, oddd;  // odd squares, flushed from ob
 };
 
 // Two 16-bit samples of each plane.
@@ -44,12 +45,24 @@ __device__ __forceinline__ void take_dword16(uint32_t a, uint32_t b, Acc16& q) {
   q.s1r = __builtin_amdgcn_udot2(__builtin_bit_cast(us2, a), (us2){1, 1}, q.s1r, false);
   q.s1d = __builtin_amdgcn_udot2(__builtin_bit_cast(us2, b), (us2){1, 1}, q.s1d, false);
   if (ODD) {
-    // A float square is odd exactly when x is odd and below 4096:
-    // min(x, 4096) & 1.
-    const us2 cap = {4096, 4096}, one = {1, 1};
-    q.oddr += __builtin_elementwise_min(__builtin_bit_cast(us2, a), cap) & one;
-    q.oddd += __builtin_elementwise_min(__builtin_bit_cast(us2, b), cap) & one;
+    // A float square is odd exactly when x is odd and below 4096, i.e. when
+    // min(x, 4096) is odd.  The low bytes of the four capped samples go to
+    // one word (a byte permute) and their low bits into byte counters.
+    const us2 cap = {4096, 4096};
+    const uint32_t ma = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(us2, a), cap));
+    const uint32_t mb = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(us2, b), cap));
+    // v_perm_b32 picks bytes of {mb, ma} (ma = bytes 0-3): the low bytes of
+    // ma's two halves, then of mb's
+    const uint32_t lo = __builtin_amdgcn_perm(mb, ma, 0x06040200u);
+    q.ob += lo & 0x01010101u;
   }
+}
+
+// Byte counters into the plane counts (before any byte can reach 256).
+__device__ __forceinline__ void flush_odd(Acc16& q) {
+  q.oddr = __builtin_amdgcn_udot4(q.ob, 0x00000101u, q.oddr, false);
+  q.oddd = __builtin_amdgcn_udot4(q.ob, 0x01010000u, q.oddd, false);
+  q.ob = 0;
 }
 
 template <bool ODD>
@@ -62,18 +75,37 @@ __device__ __forceinline__ void take_sample16(uint32_t a, uint32_t b, Acc16& q) 
   q.s1r += a;
   q.s1d += b;
   if (ODD) {
-    q.oddr.x += (unsigned short)((a < 4096u ? a : 4096u) & 1u);
-    q.oddd.x += (unsigned short)((b < 4096u ? b : 4096u) & 1u);
+    q.oddr += (a < 4096u ? a : 4096u) & 1u;
+    q.oddd += (b < 4096u ? b : 4096u) & 1u;
   }
 }
 
-constexpr int kRowsU = 4;  // 16-byte loads in flight per lane per plane
+// Loads of CB bytes (16, 8 or 4): 16 dwords per plane per lane per group.
+template <int CB>
+struct Chunk;
+template <>
+struct Chunk<16> {
+  typedef v4u T;
+  static __device__ __forceinline__ uint32_t dw(const T& v, int k) { return v[k]; }
+};
+template <>
+struct Chunk<8> {
+  typedef uint32_t T __attribute__((ext_vector_type(2)));
+  static __device__ __forceinline__ uint32_t dw(const T& v, int k) { return v[k]; }
+};
+template <>
+struct Chunk<4> {
+  typedef uint32_t T;
+  static __device__ __forceinline__ uint32_t dw(const T& v, int) { return v; }
+};
 
-template <bool ODD, bool VEC>
+template <bool ODD, int CB, int NG>
 __device__ __forceinline__ void rows16_body(const Geometry& g, const RowArrays& ra, int i, int f,
                                             int lane);
 
-template <bool ODD, bool VEC>
+// CB bytes per load (16, 8, 4; 0 = sample by sample, for rows not aligned
+// to 4 bytes), NG load slots per lane per group.
+template <bool ODD, int CB, int NG>
 __global__ void __launch_bounds__(256) k_rows16(Geometry g, RowArrays ra) {
   const int lane = threadIdx.x & 63;
   const long task = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -82,44 +114,49 @@ __global__ void __launch_bounds__(256) k_rows16(Geometry g, RowArrays ra) {
   // The odd-square count is only read for rows past 2^53; a row whose
   // prefix cannot reach 2^53 even with every sample at 65535 skips it.
   if (ODD && (uint64_t)(i + 1) * (uint64_t)g.w * 0xFFFE0000ull > kTwo53)
-    rows16_body<true, VEC>(g, ra, i, f, lane);
+    rows16_body<true, CB, NG>(g, ra, i, f, lane);
   else
-    rows16_body<false, VEC>(g, ra, i, f, lane);
+    rows16_body<false, CB, NG>(g, ra, i, f, lane);
 }
 
-template <bool ODD, bool VEC>
+template <bool ODD, int CB, int NG>
 __device__ __forceinline__ void rows16_body(const Geometry& g, const RowArrays& ra, int i, int f,
                                             int lane) {
   const uint16_t* rr = (const uint16_t*)g.ref + (long)f * g.pitch + (long)i * g.stride;
   const uint16_t* dr = (const uint16_t*)g.dis + (long)f * g.pitch + (long)i * g.stride;
-  Acc16 q = {0, 0, 0, 0, 0, 0, 0u, 0u, {0, 0}, {0, 0}};
+  Acc16 q = {0, 0, 0, 0, 0, 0, 0u, 0u, 0u, 0u, 0u};
   int j0 = 0;
-  if (VEC) {
-    const int nv = g.w >> 3;  // 8 samples per 16-byte vector
-    const v4u* rv = (const v4u*)rr;
-    const v4u* dv = (const v4u*)dr;
-    for (int base = 0; base < nv; base += 64 * kRowsU) {
-      v4u a[kRowsU], b[kRowsU];
+  if constexpr (CB > 0) {
+    typedef typename Chunk<CB>::T T;
+    const int nc = (g.w * 2) / CB;     // whole chunks in the row
+    const int nper = (nc + 63) >> 6;   // chunk slots per lane
+    const T* rv = (const T*)rr;
+    const T* dv = (const T*)dr;
+    for (int g0 = 0; g0 < nper; g0 += NG) {
+      T a[NG], b[NG];
+      if ((g0 + NG) * 64 <= nc) {  // uniform: a full group, every load unconditional
 #pragma unroll
-      for (int u = 0; u < kRowsU; ++u) {
-        const int c = base + u * 64 + lane;
-        if (c < nv) {
-          a[u] = __builtin_nontemporal_load(rv + c);
-          b[u] = __builtin_nontemporal_load(dv + c);
-        } else {
-          a[u] = (v4u){0u, 0u, 0u, 0u};  // zero samples add nothing
-          b[u] = (v4u){0u, 0u, 0u, 0u};
+        for (int u = 0; u < NG; ++u) {
+          a[u] = __builtin_nontemporal_load(rv + (g0 + u) * 64 + lane);
+          b[u] = __builtin_nontemporal_load(dv + (g0 + u) * 64 + lane);
+        }
+      } else {  // the row's last group: clamped loads, zeroed past the end
+#pragma unroll
+        for (int u = 0; u < NG; ++u) {
+          const int c = (g0 + u) * 64 + lane, cc = c < nc ? c : nc - 1;
+          const T x = __builtin_nontemporal_load(rv + cc), y = __builtin_nontemporal_load(dv + cc);
+          a[u] = c < nc ? x : T{};  // zero samples add nothing
+          b[u] = c < nc ? y : T{};
         }
       }
 #pragma unroll
-      for (int u = 0; u < kRowsU; ++u) {
-        take_dword16<ODD>(a[u].x, b[u].x, q);
-        take_dword16<ODD>(a[u].y, b[u].y, q);
-        take_dword16<ODD>(a[u].z, b[u].z, q);
-        take_dword16<ODD>(a[u].w, b[u].w, q);
-      }
+      for (int u = 0; u < NG; ++u)
+#pragma unroll
+        for (int k = 0; k < CB / 4; ++k)
+          take_dword16<ODD>(Chunk<CB>::dw(a[u], k), Chunk<CB>::dw(b[u], k), q);
+      if (ODD) flush_odd(q);
     }
-    j0 = nv << 3;
+    j0 = nc * (CB / 2);
   }
   for (int j = j0 + lane; j < g.w; j += 64) take_sample16<ODD>(rr[j], dr[j], q);
 
@@ -129,8 +166,10 @@ __device__ __forceinline__ void rows16_body(const Geometry& g, const RowArrays& 
   const uint32_t s1r = wave_sum_u32(q.s1r), s1d = wave_sum_u32(q.s1d);
   uint32_t odr = 0, odd = 0;
   if (ODD) {
-    odr = wave_sum_u32((uint32_t)q.oddr.x + q.oddr.y);
-    odd = wave_sum_u32((uint32_t)q.oddd.x + q.oddd.y);
+    // both counts in one word: each is at most w <= 32768 < 2^16
+    const uint32_t both = wave_sum_u32(q.oddr | (q.oddd << 16));
+    odr = both & 0xFFFFu;
+    odd = both >> 16;
   }
   if (lane == 0) {
     const long k = (long)f * g.h + i, k2 = (long)(g.nframes + f) * g.h + i;
@@ -205,12 +244,27 @@ hipError_t launch_rows(const Geometry& g, const RowArrays& ra, hipStream_t st, h
   const unsigned blocks = (unsigned)((tasks + 3) / 4);
   if (g.bpc == 8) {
     hipExtLaunchKernelGGL(k_rows8, dim3(blocks), dim3(256), 0, st, ev0, ev1, 0, g, ra);
-  } else if (g.need_odd) {
-    if (g.vec) hipExtLaunchKernelGGL((k_rows16<true, true>), dim3(blocks), dim3(256), 0, st, ev0, ev1, 0, g, ra);
-    else hipExtLaunchKernelGGL((k_rows16<true, false>), dim3(blocks), dim3(256), 0, st, ev0, ev1, 0, g, ra);
   } else {
-    if (g.vec) hipExtLaunchKernelGGL((k_rows16<false, true>), dim3(blocks), dim3(256), 0, st, ev0, ev1, 0, g, ra);
-    else hipExtLaunchKernelGGL((k_rows16<false, false>), dim3(blocks), dim3(256), 0, st, ev0, ev1, 0, g, ra);
+#define BEF_ROWS16(CB, NG)                                                                  \
+  if (g.need_odd)                                                                             \
+    hipExtLaunchKernelGGL((k_rows16<true, CB, NG>), dim3(blocks), dim3(256), 0, st, ev0, ev1, \
+                          0, g, ra);                                                          \
+  else                                                                                        \
+    hipExtLaunchKernelGGL((k_rows16<false, CB, NG>), dim3(blocks), dim3(256), 0, st, ev0, ev1, \
+                          0, g, ra)
+    switch (g.cb * 16 + g.ng) {
+      case 16 * 16 + 4: BEF_ROWS16(16, 4); break;
+      case 16 * 16 + 5: BEF_ROWS16(16, 5); break;
+      case 16 * 16 + 8: BEF_ROWS16(16, 8); break;
+      case 8 * 16 + 4: BEF_ROWS16(8, 4); break;
+      case 8 * 16 + 5: BEF_ROWS16(8, 5); break;
+      case 8 * 16 + 8: BEF_ROWS16(8, 8); break;
+      case 4 * 16 + 4: BEF_ROWS16(4, 4); break;
+      case 4 * 16 + 5: BEF_ROWS16(4, 5); break;
+      case 4 * 16 + 8: BEF_ROWS16(4, 8); break;
+      default: BEF_ROWS16(0, 1); break;
+    }
+#undef BEF_ROWS16
   }
   return hipGetLastError();
 }
