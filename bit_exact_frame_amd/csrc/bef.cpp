@@ -177,10 +177,10 @@ hipError_t timed(int kernel, F launch) {
 }
 
 // Load shape of the 16-bit row kernel: bytes per load (16, 8 or 4, as the
-// row starts allow) and load slots per lane per group (4, 5 or 8).  A wave
-// spreads a row's whole chunks over its 64 lanes in groups of 64 * ng; the
-// shape that leaves the fewest idle bytes in the last group wins, then the
-// one with wider loads.
+// row starts allow) and load slots per lane per group (15, 8, 5 or 4).  A
+// wave spreads a row's whole chunks over its 64 lanes in groups of 64 * ng;
+// the shape that leaves the fewest idle bytes in the last group wins, then
+// the one with wider loads, then the larger group (more loads in flight).
 void load_shape(const void* ref, const void* dis, int w, ptrdiff_t stride, ptrdiff_t pitch,
                 int nframes, int* cb_out, int* ng_out) {
   uint64_t al = 16;
@@ -198,7 +198,8 @@ void load_shape(const void* ref, const void* dis, int w, ptrdiff_t stride, ptrdi
     const uint64_t nc = (uint64_t)w * 2 / cb;
     if (nc == 0) continue;
     const uint64_t nper = (nc + 63) / 64;
-    for (int ng : {8, 5, 4}) {
+    for (int ng : {15, 8, 5, 4}) {
+      if (ng == 15 && cb == 16) continue;  // (60 registers of loads: too many)
       const uint64_t idle = (((nper + ng - 1) / ng) * ng * 64 - nc) * cb;
       if (idle < best_idle) best_cb = cb, best_ng = ng, best_idle = idle;
     }

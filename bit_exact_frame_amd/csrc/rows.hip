@@ -104,13 +104,16 @@ __device__ __forceinline__ void rows16_body(const Geometry& g, const RowArrays& 
                                             int lane);
 
 // CB bytes per load (16, 8, 4; 0 = sample by sample, for rows not aligned
-// to 4 bytes), NG load slots per lane per group.
+// to 4 bytes), NG load slots per lane per group (4, 5, 8; 15 for 8- and
+// 4-byte loads).
 template <bool ODD, int CB, int NG>
 __global__ void __launch_bounds__(256) k_rows16(Geometry g, RowArrays ra) {
   const int lane = threadIdx.x & 63;
-  const long task = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (task >= (long)g.nframes * g.h) return;  // whole wave leaves together
-  const int i = (int)(task / g.nframes), f = (int)(task % g.nframes);
+  // grid (ceil(h / 4), frames): wave w of block x takes row 4x + w of frame y
+  // (row and frame are wave-uniform scalars)
+  const int i = (int)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int f = (int)blockIdx.y;
+  if (i >= g.h) return;  // whole wave leaves together
   // The odd-square count is only read for rows past 2^53; a row whose
   // prefix cannot reach 2^53 even with every sample at 65535 skips it.
   if (ODD && (uint64_t)(i + 1) * (uint64_t)g.w * 0xFFFE0000ull > kTwo53)
@@ -187,9 +190,10 @@ __device__ __forceinline__ void rows16_body(const Geometry& g, const RowArrays& 
 // byte dot products; the noise is r^2 + d^2 - 2rd per pixel, exactly.
 __global__ void __launch_bounds__(256) k_rows8(Geometry g, RowArrays ra) {
   const int lane = threadIdx.x & 63;
-  const long task = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (task >= (long)g.nframes * g.h) return;
-  const int i = (int)(task / g.nframes), f = (int)(task % g.nframes);
+  // grid (ceil(h / 4), frames), as the 16-bit kernel
+  const int i = (int)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int f = (int)blockIdx.y;
+  if (i >= g.h) return;
   const uint8_t* rr = (const uint8_t*)g.ref + (long)f * g.pitch + (long)i * g.stride;
   const uint8_t* dr = (const uint8_t*)g.dis + (long)f * g.pitch + (long)i * g.stride;
   uint32_t s1r = 0, s1d = 0, s2r = 0, s2d = 0, x = 0;
@@ -240,17 +244,16 @@ namespace bef {
 
 hipError_t launch_rows(const Geometry& g, const RowArrays& ra, hipStream_t st, hipEvent_t ev0,
                        hipEvent_t ev1) {
-  const long tasks = (long)g.nframes * g.h;
-  const unsigned blocks = (unsigned)((tasks + 3) / 4);
+  const dim3 grid16((unsigned)((g.h + 3) / 4), (unsigned)g.nframes);
   if (g.bpc == 8) {
-    hipExtLaunchKernelGGL(k_rows8, dim3(blocks), dim3(256), 0, st, ev0, ev1, 0, g, ra);
+    hipExtLaunchKernelGGL(k_rows8, grid16, dim3(256), 0, st, ev0, ev1, 0, g, ra);
   } else {
 #define BEF_ROWS16(CB, NG)                                                                  \
   if (g.need_odd)                                                                             \
-    hipExtLaunchKernelGGL((k_rows16<true, CB, NG>), dim3(blocks), dim3(256), 0, st, ev0, ev1, \
+    hipExtLaunchKernelGGL((k_rows16<true, CB, NG>), grid16, dim3(256), 0, st, ev0, ev1,       \
                           0, g, ra);                                                          \
   else                                                                                        \
-    hipExtLaunchKernelGGL((k_rows16<false, CB, NG>), dim3(blocks), dim3(256), 0, st, ev0, ev1, \
+    hipExtLaunchKernelGGL((k_rows16<false, CB, NG>), grid16, dim3(256), 0, st, ev0, ev1,      \
                           0, g, ra)
     switch (g.cb * 16 + g.ng) {
       case 16 * 16 + 4: BEF_ROWS16(16, 4); break;
@@ -259,9 +262,11 @@ hipError_t launch_rows(const Geometry& g, const RowArrays& ra, hipStream_t st, h
       case 8 * 16 + 4: BEF_ROWS16(8, 4); break;
       case 8 * 16 + 5: BEF_ROWS16(8, 5); break;
       case 8 * 16 + 8: BEF_ROWS16(8, 8); break;
+      case 8 * 16 + 15: BEF_ROWS16(8, 15); break;
       case 4 * 16 + 4: BEF_ROWS16(4, 4); break;
       case 4 * 16 + 5: BEF_ROWS16(4, 5); break;
       case 4 * 16 + 8: BEF_ROWS16(4, 8); break;
+      case 4 * 16 + 15: BEF_ROWS16(4, 15); break;
       default: BEF_ROWS16(0, 1); break;
     }
 #undef BEF_ROWS16
