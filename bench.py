@@ -177,6 +177,23 @@ def main():
     torch.cuda.synchronize()
     clean_ms = ev0.elapsed_time(ev1)
 
+    # context, outside the timed steps: the row pass's access pattern read
+    # with no arithmetic (the practical ceiling of its memory side)
+    ceiling = None
+    if wl.bpc != 8:
+        cout = torch.empty(F * wl.h, dtype=torch.int32, device="cuda")
+        for k in range(10):
+            api.bef_read_ceiling(refs[k % ring], diss[k % ring], cout, w=wl.w, stream=stream)
+        torch.cuda.synchronize()
+        api.bef_timing_enable(True)
+        api.bef_timing_reset()
+        for k in range(max(20, args.steps // 2)):
+            api.bef_read_ceiling(refs[k % ring], diss[k % ring], cout, w=wl.w, stream=stream)
+        torch.cuda.synchronize()
+        api.bef_timing_enable(False)
+        c_ms, c_n = api.bef_timing_read("ceiling")
+        ceiling = batch_bytes / (c_ms / c_n / 1e3) / 1e9
+
     ms_per_step = clean_ms / args.steps
     fps = F * args.steps / (clean_ms / 1e3)
     rows_avg_ms = rows_ms / max(rows_n, 1)
@@ -204,6 +221,8 @@ def main():
                    "whole_path_frac": round(batch_bytes * args.steps / (clean_ms / 1e3) / 1e9
                                             / PEAK_HBM_GBS, 4),
                    "walk_avg_us": round(1e3 * walk_ms / max(walk_n, 1), 2),
+                   "read_ceiling_GBps": None if ceiling is None else round(ceiling, 1),
+                   "rows_over_read_ceiling": None if ceiling is None else round(achieved / ceiling, 4),
                    "timed_with_events_ms_per_step": round(total_ms / args.steps, 5)},
         "roofline": {"bound": "hbm", "kernel": "k_rows16", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",

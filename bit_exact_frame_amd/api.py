@@ -40,8 +40,9 @@ _lib.psnr_noise.argtypes = [_vp, _vp, _i, _i, _pd, _i, _dp]
 _lib.bef_frames.argtypes = [_vp, _vp, _i, _i, _pd, _pd, _i, _i, _vp, _dp, _dp]
 _lib.bef_frames_async.argtypes = [_vp, _vp, _i, _i, _pd, _pd, _i, _i, _vp, _vp]
 _lib.bef_frames_units.argtypes = [_vp, _vp, _i, _i, _pd, _pd, _i, _i, _vp, _u64p]
+_lib.bef_read_ceiling.argtypes = [_vp, _vp, _i, _i, _pd, _pd, _i, _vp, _vp]
 for _n in ("moment_frame", "psnr_noise", "bef_frames", "bef_frames_async",
-           "bef_frames_units"):
+           "bef_frames_units", "bef_read_ceiling"):
     getattr(_lib, _n).restype = _i
 _lib.bef_last_error.restype = ctypes.c_char_p
 _lib.bef_debug_set.argtypes = [_u]
@@ -65,7 +66,7 @@ DBG_FORCE_ROUND = 8
 DBG_NO_STRETCH = 16
 DBG_NO_CLOSED_FORM = 32
 
-KERNELS = {"rows": 0, "plan": 1, "pairs": 2, "walk": 3}
+KERNELS = {"rows": 0, "plan": 1, "pairs": 2, "walk": 3, "ceiling": 4}
 
 
 class BefError(RuntimeError):
@@ -156,6 +157,20 @@ def bef_frames_units(ref, dis, bpc: int, w: int | None = None, stream=None):
                                  f, bpc, _stream_ptr(stream), units.ctypes.data_as(_u64p)),
            "bef_frames_units")
     return units
+
+
+def bef_read_ceiling(ref, dis, out, w: int | None = None, stream=None):
+    """Diagnostic read-only pass over 16-bit planes (the row pass's memory
+    side); ``out`` is a uint32 device tensor of at least F*h words."""
+    import torch
+    f, h, stride, w = _geom(ref, 16, w)
+    if out.dtype != torch.int32 and out.dtype != torch.uint32:
+        raise BefError("out must be a 32-bit integer device tensor")
+    if not out.is_cuda or out.numel() < f * h:
+        raise BefError("out must be a device tensor of at least F*h words")
+    _check(_lib.bef_read_ceiling(ref.data_ptr(), dis.data_ptr(), w, h, stride, h * stride, f,
+                                 _stream_ptr(stream), ctypes.c_void_p(out.data_ptr())),
+           "bef_read_ceiling")
 
 
 def bef_debug_set(flags: int) -> int:

@@ -41,8 +41,8 @@ struct EvPair {
 bool g_timing = false;
 std::vector<EvPair> g_ev_live;
 std::vector<hipEvent_t> g_ev_pool;
-double g_ms[4] = {0, 0, 0, 0};
-long g_n[4] = {0, 0, 0, 0};
+double g_ms[5] = {0, 0, 0, 0, 0};
+long g_n[5] = {0, 0, 0, 0, 0};
 
 int fail(int rc, const char* fmt, ...) {
   char buf[512];
@@ -351,6 +351,23 @@ int bef_frames_async(const void* ref, const void* dis, int w, int h, ptrdiff_t s
   return enqueue(c, (hipStream_t)stream, dev_results);
 }
 
+int bef_read_ceiling(const void* ref, const void* dis, int w, int h, ptrdiff_t stride,
+                     ptrdiff_t frame_pitch, int nframes, void* stream, uint32_t* dev_out) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_err.clear();
+  if (!dev_out) return fail(-EINVAL, "NULL dev_out");
+  DevGuard dg;
+  Call c;
+  int rc = prepare(c, ref, dis, w, h, stride, frame_pitch, nframes, 16);
+  if (rc) return rc;
+  if (c.g.cb == 0) return fail(-EINVAL, "rows hold no whole 4-byte chunks at this alignment");
+  const hipStream_t st = (hipStream_t)stream;
+  BEF_HIP(timed(4, [&](hipEvent_t a, hipEvent_t b) {
+    return launch_read_ceiling(c.g, dev_out, st, a, b);
+  }));
+  return 0;
+}
+
 int moment_frame(const void* ref, const void* dis, int w, int h, ptrdiff_t stride, int bpc,
                  double out[4]) {
   if (!out) return -EINVAL;
@@ -380,7 +397,7 @@ int bef_timing_enable(int on) {
 
 int bef_timing_read(int kernel, double* ms, long* launches) {
   std::lock_guard<std::mutex> lk(g_mu);
-  if (kernel < 0 || kernel > 3 || !ms || !launches) return -EINVAL;
+  if (kernel < 0 || kernel > 4 || !ms || !launches) return -EINVAL;
   ev_collect();
   *ms = g_ms[kernel];
   *launches = g_n[kernel];

@@ -186,6 +186,38 @@ __device__ __forceinline__ void rows16_body(const Geometry& g, const RowArrays& 
   }
 }
 
+// The memory side of the 16-bit row pass alone: the same grid, load shape
+// and nontemporal loads, with the arithmetic replaced by an XOR of the
+// loaded words (one word per row written to out[frame][row]).  A
+// diagnostic: the practical read ceiling of this access pattern.
+template <int CB, int NG>
+__global__ void __launch_bounds__(256) k_read_ceiling(Geometry g, uint32_t* out) {
+  typedef typename Chunk<CB>::T T;
+  const int lane = threadIdx.x & 63;
+  const int i = (int)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int f = (int)blockIdx.y;
+  if (i >= g.h) return;
+  const T* rv = (const T*)((const uint16_t*)g.ref + (long)f * g.pitch + (long)i * g.stride);
+  const T* dv = (const T*)((const uint16_t*)g.dis + (long)f * g.pitch + (long)i * g.stride);
+  const int nc = (g.w * 2) / CB, nper = (nc + 63) >> 6;
+  uint32_t acc = 0;
+  for (int g0 = 0; g0 < nper; g0 += NG) {
+    T a[NG], b[NG];
+#pragma unroll
+    for (int u = 0; u < NG; ++u) {
+      const int c = (g0 + u) * 64 + lane, cc = c < nc ? c : nc - 1;
+      a[u] = __builtin_nontemporal_load(rv + cc);
+      b[u] = __builtin_nontemporal_load(dv + cc);
+    }
+#pragma unroll
+    for (int u = 0; u < NG; ++u)
+#pragma unroll
+      for (int k = 0; k < CB / 4; ++k) acc ^= Chunk<CB>::dw(a[u], k) + Chunk<CB>::dw(b[u], k);
+  }
+  acc = wave_sum_u32(acc);
+  if (lane == 0) out[(long)f * g.h + i] = acc;
+}
+
 // 8-bit planes: squares are exact integers (x <= 255), summed with 4-way
 // byte dot products; the noise is r^2 + d^2 - 2rd per pixel, exactly.
 __global__ void __launch_bounds__(256) k_rows8(Geometry g, RowArrays ra) {
@@ -271,6 +303,29 @@ hipError_t launch_rows(const Geometry& g, const RowArrays& ra, hipStream_t st, h
     }
 #undef BEF_ROWS16
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_read_ceiling(const Geometry& g, uint32_t* out, hipStream_t st, hipEvent_t ev0,
+                               hipEvent_t ev1) {
+  const dim3 grid((unsigned)((g.h + 3) / 4), (unsigned)g.nframes);
+#define BEF_CEIL(CB, NG)                                                                       \
+  hipExtLaunchKernelGGL((k_read_ceiling<CB, NG>), grid, dim3(256), 0, st, ev0, ev1, 0, g, out)
+  switch (g.cb * 16 + g.ng) {
+    case 16 * 16 + 4: BEF_CEIL(16, 4); break;
+    case 16 * 16 + 5: BEF_CEIL(16, 5); break;
+    case 16 * 16 + 8: BEF_CEIL(16, 8); break;
+    case 8 * 16 + 4: BEF_CEIL(8, 4); break;
+    case 8 * 16 + 5: BEF_CEIL(8, 5); break;
+    case 8 * 16 + 8: BEF_CEIL(8, 8); break;
+    case 8 * 16 + 15: BEF_CEIL(8, 15); break;
+    case 4 * 16 + 4: BEF_CEIL(4, 4); break;
+    case 4 * 16 + 5: BEF_CEIL(4, 5); break;
+    case 4 * 16 + 8: BEF_CEIL(4, 8); break;
+    case 4 * 16 + 15: BEF_CEIL(4, 15); break;
+    default: return hipErrorInvalidValue;  // no whole chunks: nothing to measure
+  }
+#undef BEF_CEIL
   return hipGetLastError();
 }
 

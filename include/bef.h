@@ -111,10 +111,22 @@ const char *bef_last_error(void);
 #define BEF_DBG_NO_CLOSED_FORM 32u
 unsigned bef_debug_set(unsigned flags);
 
+/* Diagnostic, not part of the reductions: the memory side of the 16-bit
+ * row pass alone.  Reads both planes (16-bit, same arguments and limits as
+ * bef_frames) with the row pass's grid, load width and nontemporal loads,
+ * replacing the arithmetic by an XOR of the loaded words, and writes one
+ * word per row to dev_out (DEVICE, [nframes][h] uint32_t, caller-owned).
+ * Asynchronous on stream.  Its duration (timing kernel 4) is the practical
+ * read ceiling of the row pass's access pattern.  -EINVAL also when no
+ * whole 4-byte chunk fits the rows' alignment. */
+int bef_read_ceiling(const void *ref, const void *dis, int w, int h,
+                     ptrdiff_t stride, ptrdiff_t frame_pitch, int nframes,
+                     void *stream, uint32_t *dev_out);
+
 /* Kernel timing: when enabled, each kernel the library launches carries a
  * start and a stop HIP event recorded by its own dispatch (on the stream
  * it is launched on), and the library accumulates their durations.
- * kernel: 0 row sums, 1 plan, 2 row pairs, 3 walk.
+ * kernel: 0 row sums, 1 plan, 2 row pairs, 3 walk, 4 read ceiling.
  * bef_timing_read returns the summed milliseconds and launch count since
  * the last reset (0 / -EINVAL). */
 int bef_timing_enable(int on);

@@ -219,6 +219,24 @@ def test_deterministic(api):
     assert (a == b).all()
 
 
+def test_read_ceiling_diagnostic(api):
+    """The read-only diagnostic pass runs on the row pass's shapes, gives
+    the same words twice, and rejects rows with no whole 4-byte chunk."""
+    import torch
+    ref, dis = synth.make_frames(5, frames=2)
+    r, d = dev(ref), dev(dis)
+    out1 = torch.zeros(2 * ref.shape[1], dtype=torch.int32, device="cuda")
+    out2 = torch.ones_like(out1)
+    api.bef_read_ceiling(r, d, out1)
+    api.bef_read_ceiling(r, d, out2)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2)
+    buf = torch.zeros(8 * 33 + 1, dtype=torch.uint16, device="cuda")
+    odd = buf[1:].view(1, 8, 33)  # contiguous, starts 2 bytes past an aligned address
+    with pytest.raises(api.BefError):
+        api.bef_read_ceiling(odd, odd, out1, w=32)
+
+
 def test_bad_arguments(api):
     import torch
     r = torch.zeros((4, 4), dtype=torch.uint16, device="cuda")
