@@ -587,129 +587,103 @@ struct Walker {
 // across [x2, x3), 54 [x3, x4), beyond [x4, n); empty ones are skipped.
 
 constexpr int kEdges = 5;
-constexpr int kFastRows = 9;  // rows per thread in the fast walk: h <= kFastRows * kT
+constexpr int kRowsPer = (kChunk + kT - 1) / kT;  // rows per thread when loading a plane's sums
 
-struct FastLds {
-  uint64_t P[kEdges + 1];   // exact prefix at each edge (entry kEdges: the total)
-  uint32_t PC[kEdges + 1];  // odd terms before each edge
-  int x[kEdges + 1];        // the edges (entry kEdges: n)
-  uint64_t runE[kT];        // a crossing row's run sums
-  uint32_t term[kStage];    // a crossing row's terms
-};
-
-// Exclusive block scan of (v, u), their totals, and the block total of z.
-__device__ __forceinline__ void block_scan_vuz(uint64_t v, uint32_t u, uint64_t z, uint64_t* ev,
-                                               uint32_t* eu, uint64_t* tv, uint32_t* tu,
-                                               uint64_t* tz, BlockScratch& sm) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const uint64_t iv = wave_incl_scan_u64(v);
-  const uint32_t iu = wave_incl_scan_u32(u);
-  const uint64_t sz = wave_sum_u64(z);
-  __syncthreads();
-  if (lane == 63) {
-    sm.w64[2 * wv] = iv;
-    sm.w64[2 * wv + 1] = sz;
-    sm.iv[wv] = (int)iu;
-  }
-  __syncthreads();
-  uint64_t bv = 0, av = 0, az = 0;
-  uint32_t bu = 0, au = 0;
-#pragma unroll
-  for (int k = 0; k < kWaves; ++k) {
-    const uint64_t x = sm.w64[2 * k], y = sm.w64[2 * k + 1];
-    const uint32_t c = (uint32_t)sm.iv[k];
-    bv += k < wv ? x : 0;
-    bu += k < wv ? c : 0;
-    av += x;
-    au += c;
-    az += y;
-  }
-  *ev = bv + iv - v;
-  *eu = bu + iu - u;
-  *tv = av;
-  *tu = au;
-  *tz = az;
-}
-
-// The edges of n items whose values are in registers: thread t owns items
-// [a, a + c) with sums e[] and odd counts cnt[]; eprev() gives the sum of
-// item a - 1 (called after the scan's barriers, only when a > 0); base is
-// the sum before item 0 and M the margin.  With every sum below 2^55 an item's plan follows from where its
-// exact interval [P - M, P + E + M] lies against 2^53, 2^54 and 2^55, and
-// each edge of a plan is the first item at which a non-decreasing quantity
-// reaches a threshold:
+// ---------------------------------------------------------------------------
+// The fast path: one wave (64 lanes, no block barrier) per plane.
+//
+// With every sum below 2^55 a stretch's plan follows from where its exact
+// interval [P - M, P + E + M] lies against 2^53, 2^54 and 2^55 (P the exact
+// sum before it, E its exact sum, M a bound on how far the CPU's rounded
+// sum can stray from P).  Each edge of a plan is the first item at which a
+// non-decreasing quantity reaches a threshold:
 //   x0: P + E > 2^53        (end of the exact items)
 //   x1: P - M >= 2^53       (first item inside the binade of 2^53)
 //   x2: P + E + M >= 2^54   (first item that may leave it)
 //   x3: P - M >= 2^54       (first item inside the binade of 2^54)
 //   x4: P + E + M >= 2^55   (first item that may leave that one)
-// Since each condition is monotone in the item index, exactly one thread
-// sees its edge (the condition false before the item, true at it) and
-// writes it; the thread holding the last item writes the edges that never
-// occur.  Fills fl (entry kEdges: n and the totals); *ztot = block total of
-// z.  Ends with a barrier.
-template <int CMAX, class EPrev>
-__device__ __forceinline__ void edges_reg(int n, int a, int c, const uint64_t (&e)[CMAX],
-                                          const uint32_t (&cnt)[CMAX], EPrev eprev,
-                                          uint64_t base, uint64_t M, uint64_t z, uint64_t* ztot,
-                                          FastLds& fl, BlockScratch& sm) {
-  uint64_t le = 0;
-  uint32_t lc = 0;
-#pragma unroll
-  for (int k = 0; k < CMAX; ++k)
-    if (k < c) {
-      le += e[k];
-      lc += cnt[k];
-    }
-  uint64_t P, TE;
-  uint32_t PC, TC;
-  block_scan_vuz(le, lc, z, &P, &PC, &TE, &TC, ztot, sm);
+// The segments, in order: exact [0, x0), across [x0, x1), 53 [x1, x2),
+// across [x2, x3), 54 [x3, x4), beyond [x4, n).
+
+__device__ __forceinline__ unsigned edge_conds(uint64_t pk, uint64_t pk1, uint64_t M) {
   constexpr uint64_t T53 = 1ull << 53, T54 = 1ull << 54, T55 = 1ull << 55;
-  // The five conditions of item k, from P_k (lo side) and P_{k+1} (hi side).
-  auto conds = [&](uint64_t pk, uint64_t pk1) {
-    const uint64_t lo = pk > M ? pk - M : 0;
-    return (unsigned)(pk1 > T53) | (unsigned)(lo >= T53) << 1 | (unsigned)(pk1 + M >= T54) << 2 |
-           (unsigned)(lo >= T54) << 3 | (unsigned)(pk1 + M >= T55) << 4;
-  };
-  const uint64_t q0 = base + P, qend = q0 + le;
-  uint64_t elast = 0;
-#pragma unroll
-  for (int k = 0; k < CMAX; ++k)
-    if (k == c - 1) elast = e[k];
-  // Conditions at item a - 1 and at the chunk's last item; an edge lies in
-  // this chunk when it is false before the chunk and true at its end.
-  const unsigned before = a > 0 ? conds(q0 - eprev(), q0) : 0u;
-  const unsigned last = c > 0 ? conds(qend - elast, qend) : before;
+  const uint64_t lo = pk > M ? pk - M : 0;
+  return (unsigned)(pk1 > T53) | (unsigned)(lo >= T53) << 1 | (unsigned)(pk1 + M >= T54) << 2 |
+         (unsigned)(lo >= T54) << 3 | (unsigned)(pk1 + M >= T55) << 4;
+}
+
+// Edges of n items (uniform over the wave): x[j], the exact prefix P[j]
+// (base included) and odd count PC[j] before each edge; entry kEdges is n
+// and the totals.
+struct WEdges {
+  int x[kEdges + 1];
+  uint64_t P[kEdges + 1];
+  uint32_t PC[kEdges + 1];
+  bool ok;
+};
+
+// Lane l owns items [l*c, l*c + c) with sum le, odd count lc and last item
+// value elast; item_at(k, &e, &cnt) gives any single item.  Each condition
+// is monotone in the item index, so an edge lies in the one lane whose
+// chunk starts false and ends true; that lane's items are then spread one
+// per lane (c <= 64) and scanned again to find the edge's item.
+template <class ItemAt>
+__device__ __forceinline__ WEdges wave_edges(int n, int c, uint64_t le, uint32_t lc,
+                                             uint64_t elast, uint64_t base, uint64_t M,
+                                             ItemAt item_at) {
+  const int lane = threadIdx.x & 63;
+  const int a = min(lane * c, n), cl = min(c, n - a);
+  const uint64_t P = base + wave_excl_scan_u64(le);
+  const uint32_t PC = wave_excl_scan_u32(lc);
+  const uint64_t T = rdl64(P + le, 63);
+  const uint32_t TC = rdl32(PC + lc, 63);
+  const uint64_t ep = lane_before_u64(elast);
+  const unsigned before = (cl > 0 && a > 0) ? edge_conds(P - ep, P, M) : 0u;
+  const unsigned last = cl > 0 ? edge_conds(P + le - elast, P + le, M) : 0u;
   const unsigned own = last & ~before;
-  if (own) {  // a few threads: find each owned edge's item
-    uint64_t q = q0;
-    uint32_t qc = PC;
-    unsigned seen = before;
+  const unsigned occurs = rdl32(last, (n - 1) / c);  // conditions at item n - 1
+  WEdges r;
+  r.ok = true;
 #pragma unroll
-    for (int k = 0; k < CMAX; ++k) {
-      if (k < c) {
-        const uint64_t qn = q + e[k];
-        const unsigned now = conds(q, qn), fresh = now & ~seen;
-        if (fresh) {
-          const int i = a + k;
+  for (int j = 0; j <= kEdges; ++j) {
+    r.x[j] = n;
+    r.P[j] = T;
+    r.PC[j] = TC;
+  }
+  unsigned pending = occurs & 31u;
+  while (pending) {
+    const int j0 = __builtin_ctz(pending);
+    const uint64_t om = wave_ballot((own >> j0) & 1u);
+    if (om == 0) {  // not monotone: not the premise
+      r.ok = false;
+      return r;
+    }
+    const int owner = __builtin_ctzll(om);
+    const unsigned owned = rdl32(own, owner) & pending;
+    const int b0 = owner * c, cnt = min(c, n - b0);
+    uint64_t e = 0;
+    uint32_t cc = 0;
+    if (lane < cnt) item_at(b0 + lane, &e, &cc);
+    const uint64_t q = rdl64(P, owner) + wave_excl_scan_u64(e);
+    const uint32_t qc = rdl32(PC, owner) + wave_excl_scan_u32(cc);
+    const unsigned now = lane < cnt ? edge_conds(q, q + e, M) : 0u;
 #pragma unroll
-          for (int j = 0; j < kEdges; ++j)
-            if (fresh >> j & 1u) fl.x[j] = i, fl.P[j] = q, fl.PC[j] = qc;
+    for (int j = 0; j < kEdges; ++j) {
+      if ((owned >> j) & 1u) {
+        const uint64_t m = wave_ballot((now >> j) & 1u);
+        if (m == 0) {
+          r.ok = false;
+          return r;
         }
-        seen = now;
-        q = qn;
-        qc += cnt[k];
+        const int k = __builtin_ctzll(m);
+        r.x[j] = b0 + k;
+        r.P[j] = rdl64(q, k);
+        r.PC[j] = rdl32(qc, k);
       }
     }
+    pending &= ~owned;
   }
-  if (c > 0 && a + c == n) {
-    const uint64_t T = base + TE;
-#pragma unroll
-    for (int j = 0; j < kEdges; ++j)
-      if (!(last >> j & 1u)) fl.x[j] = n, fl.P[j] = T, fl.PC[j] = TC;
-    fl.x[kEdges] = n, fl.P[kEdges] = T, fl.PC[kEdges] = TC;
-  }
-  __syncthreads();
+  return r;
 }
 
 // Segment g of the edges (0 exact, 1 across, 2 the binade of 2^53, 3 across,
@@ -727,157 +701,186 @@ __device__ __forceinline__ bool fast_apply(uint64_t* s, int g, uint64_t Eg, uint
   return false;
 }
 
-constexpr int kRunMax = kStage / kT;  // terms per run in a crossing row
+// A crossing row staged in LDS by one wave: samples (zeros from w up to
+// the lanes' last run), and per 8-sample chunk the exact sum of the float
+// squares (units) and their odd count.
+struct RowStage {
+  uint16_t x[kStage];
+  uint64_t chE[kStage / 8];
+  uint8_t chC[kStage / 8];
+};
 
-// The L consecutive samples of thread t's run of row i, into registers.
-__device__ __forceinline__ void load_run(uint32_t (&x)[kRunMax], int i, const void* plane,
-                                         long stride, int w, int bpc8) {
-  const int L = (w + kT - 1) / kT;
-  const int j0 = min((int)threadIdx.x * L, w), n = min(j0 + L, w) - j0;
-  const long base = (long)i * stride + j0;
+// Samples of a row's term run: lane l takes chunks [l*cpl, l*cpl + cpl) of
+// 8 samples, cpl = ceil(ceil(w / 8) / 64).
+__device__ __forceinline__ int run_chunks(int w) { return (((w + 7) >> 3) + 63) >> 6; }
+
+// Loads row i of the plane into st by one wave (16-byte loads when the row
+// allows them, then every chunk's term sums from the loaded registers).
+__device__ void wave_stage_row(RowStage& st, int i, const void* plane, long stride, int w,
+                               int bpc8) {
+  const int lane = threadIdx.x & 63;
+  const int nch = 64 * run_chunks(w);  // chunks through the last lane's run
+  if (!bpc8) {
+    const uint16_t* row = (const uint16_t*)plane + (long)i * stride;
+    if (((uintptr_t)row & 15) == 0 && (w & 7) == 0) {
+      const int nv = w >> 3;
+      constexpr int U = kStage / 8 / 64;
+      v4u v[U];
 #pragma unroll
-  for (int k = 0; k < kRunMax; ++k)  // every load issued before the first use
-    x[k] = k < n ? (bpc8 ? ((const uint8_t*)plane)[base + k] : ((const uint16_t*)plane)[base + k])
-                 : 0u;
+      for (int u = 0; u < U; ++u) {  // every load issued before the first use
+        const int cidx = lane + 64 * u;
+        v[u] = cidx < nv ? ((const v4u*)row)[cidx] : (v4u){0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int cidx = lane + 64 * u;
+        if (cidx < nch) {
+          ((v4u*)st.x)[cidx] = v[u];
+          uint64_t e = 0;
+          uint32_t c = 0;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const uint32_t t = fsq_units((v[u][q >> 1] >> (16 * (q & 1))) & 0xFFFFu);
+            e += t;
+            c += t & 1u;
+          }
+          st.chE[cidx] = e;
+          st.chC[cidx] = (uint8_t)c;
+        }
+      }
+      return;
+    }
+    for (int j = lane; j < nch * 8; j += 64) st.x[j] = j < w ? row[j] : (uint16_t)0;
+  } else {
+    const uint8_t* row = (const uint8_t*)plane + (long)i * stride;
+    for (int j = lane; j < nch * 8; j += 64) st.x[j] = j < w ? row[j] : (uint16_t)0;
+  }
+  wave_lds_sync();
+  for (int cidx = lane; cidx < nch; cidx += 64) {
+    uint64_t e = 0;
+    uint32_t c = 0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const uint32_t t = fsq_units(st.x[8 * cidx + q]);
+      e += t;
+      c += t & 1u;
+    }
+    st.chE[cidx] = e;
+    st.chC[cidx] = (uint8_t)c;
+  }
 }
 
-// Row i planned across an edge, from S = *sp, its run samples in x: one run
-// of L consecutive terms per thread, the runs' edges, closed forms, and the
-// runs across an edge term by term with the double add (the CPU's step).
-// Returns false when the row needs the general walk (w <= kStage).
-__device__ bool fast_cross_row(uint64_t* sp, const uint32_t (&x)[kRunMax], int w, FastLds& fl,
-                               BlockScratch& sm) {
+// Row (staged in st) planned across an edge, from S = *sp: lane l takes
+// the terms of its run_chunks(w) chunks, the terms' edges with margin
+// w * u/2 (u the last place of the binade above S), closed forms, and the
+// terms across an edge added with the double add (the CPU's step).
+__device__ bool wave_cross_row(uint64_t* sp, const RowStage& st, int w) {
+  const int lane = threadIdx.x & 63;
   const uint64_t s0 = *sp;
-  const int L = (w + kT - 1) / kT;
-  const int t = threadIdx.x;
-  const int j0 = min(t * L, w), n = min(j0 + L, w) - j0;
-  uint32_t tk[kRunMax];
-  uint64_t E[1] = {0};
-  uint32_t c[1] = {0};
+  const int cpl = run_chunks(w), L = 8 * cpl;
+  const int a = min(lane * L, w), cl = min(L, w - a);
+  uint64_t le = 0;
+  uint32_t lc = 0;
+  constexpr int CMAXR = kStage / 8 / 64;
 #pragma unroll
-  for (int k = 0; k < kRunMax; ++k) {
-    tk[k] = fsq_units(x[k]);  // 0 past the run's end
-    E[0] += tk[k];
-    c[0] += tk[k] & 1u;
-  }
-  __syncthreads();  // every read of the previous row's terms and run sums is done
-#pragma unroll
-  for (int k = 0; k < kRunMax; ++k)
-    if (k < n) fl.term[j0 + k] = tk[k];
-  fl.runE[t] = E[0];  // visible after the scan's barriers
+  for (int q = 0; q < CMAXR; ++q)
+    if (q < cpl) {  // zeros past w add nothing
+      le += st.chE[lane * cpl + q];
+      lc += st.chC[lane * cpl + q];
+    }
+  const uint64_t elast = cl > 0 ? fsq_units(st.x[a + cl - 1]) : 0;
   const int eB = (s0 < kTwo53 ? 53 : binade(s0)) + 1;
   const uint64_t Mr = (uint64_t)w << (eB - 53);
-  uint64_t unused;
-  edges_reg<1>(
-      kT, t, 1, E, c, [&] { return fl.runE[t - 1]; }, s0, Mr, 0, &unused, fl, sm);
+  const WEdges ed = wave_edges(w, L, le, lc, elast, s0, Mr, [&](int k, uint64_t* e, uint32_t* c) {
+    const uint32_t x = fsq_units(st.x[k]);
+    *e = x;
+    *c = x & 1u;
+  });
+  if (!ed.ok) return false;
   uint64_t s = s0;
-  int a = 0;
+  int ia = 0;
   uint64_t Pa = s0, PCa = 0;
 #pragma unroll
   for (int g = 0; g <= kEdges; ++g) {
-    const int b = fl.x[g];
-    const uint64_t Pb = fl.P[g], PCb = fl.PC[g];
-    if (b < a) return false;  // edges out of order: not the premise
-    if (b > a) {
+    const int b = ed.x[g];
+    if (b < ia) return false;  // edges out of order: not the premise
+    if (b > ia) {
       if (g == 1 || g == 3) {
         double d = (double)s;  // a value the CPU's double holds: exact
-        const int t0 = min(a * L, w), t1 = min(b * L, w);
-        if (t1 - t0 <= kRunMax) {  // one run: its terms first, then the adds
-          uint32_t v[kRunMax];
-#pragma unroll
-          for (int k = 0; k < kRunMax; ++k) v[k] = t0 + k < t1 ? fl.term[t0 + k] : 0u;
-#pragma unroll
-          for (int k = 0; k < kRunMax; ++k)
-            if (t0 + k < t1) d = d + (double)v[k];
-        } else {
-          for (int j = t0; j < t1; ++j) d = d + (double)fl.term[j];
-        }
+        for (int k = ia; k < b; ++k) d = d + (double)fsq_units(st.x[k]);
         s = (uint64_t)d;
-      } else if (!fast_apply(&s, g, Pb - Pa, PCb - PCa)) {
+      } else if (!fast_apply(&s, g, ed.P[g] - Pa, ed.PC[g] - PCa)) {
         return false;
       }
     }
-    a = b;
-    Pa = Pb;
-    PCa = PCb;
+    ia = b;
+    Pa = ed.P[g];
+    PCa = ed.PC[g];
   }
   *sp = s;
   return true;
 }
 
-// The fast walk of one plane (h <= kFastRows * kT, every sum below 2^55):
-// thread t holds rows [t*c, t*c + c) in registers.  Margin: with every sum
-// below 2^55 the CPU's sum strays from the exact prefix by at most 2 units
-// per term added past 2^53.  Returns false when the plane needs the general
-// walk; *exact and *s1 are set either way.
-__device__ bool fast_walk(uint64_t* out, uint64_t* exact, uint64_t* s1, const uint64_t* R,
-                          const uint32_t* C, const uint32_t* R1, int h, const void* plane,
-                          long stride, int w, int bpc8, FastLds& fl, BlockScratch& sm) {
-  const int cr = (h + kT - 1) / kT;
-  const int a = min((int)threadIdx.x * cr, h), c = min(cr, h - a);
-  uint64_t e[kFastRows];
-  uint32_t cnt[kFastRows];
-  uint64_t z = 0;
-  uint32_t z1[kFastRows];
+// The fast walk of one plane by one wave: rows' exact sums and odd counts
+// in lE / lC (LDS, h <= kChunk), and per block thread t the sums of rows
+// [t*cs, t*cs + cs) in pe / pc; lane l takes the rows of threads
+// [8l, 8l + 8).  Samples are read only for rows across an edge (w <=
+// kStage).  Margin: with every sum below 2^55 the CPU's sum strays from the
+// exact prefix by at most 2 units per term added past 2^53.  Returns false
+// when the plane needs the general walk; *exact is set either way.
+__device__ bool wave_walk(uint64_t* out, uint64_t* exact, const uint64_t* lE, const uint16_t* lC,
+                          const uint64_t* pe, const uint32_t* pc, int cs, int h,
+                          const void* plane, long stride, int w, int bpc8, RowStage& st0,
+                          RowStage& st1) {
+  const int lane = threadIdx.x & 63;
+  constexpr int PER = kT / 64;
+  const int c = PER * cs;
+  const int a = min(lane * c, h), cl = min(c, h - a);
+  uint64_t le = 0;
+  uint32_t lc = 0;
 #pragma unroll
-  for (int k = 0; k < kFastRows; ++k) {  // every load issued before the first use
-    e[k] = k < c ? R[a + k] : 0;
-    cnt[k] = k < c ? C[a + k] : 0;
-    z1[k] = k < c ? R1[a + k] : 0;
+  for (int q = 0; q < PER; ++q) {
+    le += pe[lane * PER + q];
+    lc += pc[lane * PER + q];
   }
-  const uint64_t eprev = a > 0 ? R[a - 1] : 0;
-#pragma unroll
-  for (int k = 0; k < kFastRows; ++k) z += z1[k];
+  const uint64_t elast = cl > 0 ? lE[a + cl - 1] : 0;
   const uint64_t M = 2ull * (uint64_t)w * (uint64_t)h;
-  edges_reg<kFastRows>(
-      h, a, c, e, cnt, [&] { return eprev; }, 0, M, z, s1, fl, sm);
-  const uint64_t E = fl.P[kEdges];
-  *exact = E;
-  if (E >= (1ull << 55)) return false;
-  int x[kEdges + 1];
-  uint64_t P[kEdges + 1];
-  uint32_t PC[kEdges + 1];
-#pragma unroll
-  for (int j = 0; j <= kEdges; ++j) {
-    x[j] = fl.x[j];
-    P[j] = fl.P[j];
-    PC[j] = fl.PC[j];
-  }
-  if (w > kStage) {
-    if (x[0] < x[1] || x[2] < x[3]) return false;  // rows across an edge, too wide
-  }
-  // the first row of each stretch across an edge, loaded before it is needed
-  uint32_t xa[kRunMax], xb[kRunMax];
-  const int ra = x[0] < x[1] ? x[0] : -1, rb = x[2] < x[3] ? x[2] : -1;
-  if (ra >= 0) load_run(xa, ra, plane, stride, w, bpc8);
-  if (rb >= 0) load_run(xb, rb, plane, stride, w, bpc8);
+  const WEdges ed = wave_edges(h, c, le, lc, elast, 0, M, [&](int k, uint64_t* e, uint32_t* cc) {
+    *e = lE[k];
+    *cc = lC[k];
+  });
+  *exact = ed.P[kEdges];
+  if (!ed.ok || ed.P[kEdges] >= (1ull << 55)) return false;
+  // the first row of each stretch across an edge, staged before its turn
+  const int ra = ed.x[0] < ed.x[1] ? ed.x[0] : -1, rb = ed.x[2] < ed.x[3] ? ed.x[2] : -1;
+  if (ra >= 0) wave_stage_row(st0, ra, plane, stride, w, bpc8);
+  if (rb >= 0) wave_stage_row(st1, rb, plane, stride, w, bpc8);
+  wave_lds_sync();
   uint64_t s = 0;
   int ia = 0;
   uint64_t Pa = 0, PCa = 0;
 #pragma unroll
   for (int g = 0; g <= kEdges; ++g) {
-    const int b = x[g];
+    const int b = ed.x[g];
     if (b < ia) return false;  // edges out of order: not the premise
     if (b > ia) {
       if (g == 1 || g == 3) {
         for (int i = ia; i < b; ++i) {
-          bool ok;
-          if (i == (g == 1 ? ra : rb)) {
-            ok = fast_cross_row(&s, g == 1 ? xa : xb, w, fl, sm);
-          } else {
-            uint32_t xi[kRunMax];
-            load_run(xi, i, plane, stride, w, bpc8);
-            ok = fast_cross_row(&s, xi, w, fl, sm);
+          RowStage& sg = g == 1 ? st0 : st1;
+          if (i != (g == 1 ? ra : rb)) {  // a further row of the stretch
+            wave_lds_sync();
+            wave_stage_row(sg, i, plane, stride, w, bpc8);
+            wave_lds_sync();
           }
-          if (!ok) return false;
+          if (!wave_cross_row(&s, sg, w)) return false;
         }
-      } else if (!fast_apply(&s, g, P[g] - Pa, PC[g] - PCa)) {
+      } else if (!fast_apply(&s, g, ed.P[g] - Pa, ed.PC[g] - PCa)) {
         return false;
       }
     }
     ia = b;
-    Pa = P[g];
-    PCa = PC[g];
+    Pa = ed.P[g];
+    PCa = ed.PC[g];
   }
   *out = s;
   return true;
@@ -895,73 +898,59 @@ __device__ __forceinline__ Pair64 noise_row_pair(uint64_t t, int sh) {
   return Pair64{r0, r1 - u};
 }
 
-// The fast PSNR noise (h <= kChunk, every sum below 2^55): rows in
-// registers and in stash[], the same edges as the moment walk with margin
-// 2 per row (each add past 2^53 rounds by at most u/2 <= 2 units below
-// 2^55), exact rows added as integers, rows across an edge added with the
-// double add, and each stretch of rows inside one binade applied as one
-// pair composed in row order.  Returns false when it does not apply.
-__device__ bool fast_noise(double* out, uint64_t* exact, const uint64_t* RN, int h,
-                           uint64_t* stash, FastLds& fl, BlockScratch& sm) {
-  const int cr = (h + kT - 1) / kT;
-  const int a = min((int)threadIdx.x * cr, h), c = min(cr, h - a);
-  constexpr int CM = (kChunk + kT - 1) / kT;
-  uint64_t e[CM];
-  uint32_t cnt[CM];
+// The fast PSNR noise by one wave: rows' exact sums in lR (LDS, h <=
+// kChunk) and per block thread t the sum of rows [t*cs, t*cs + cs) in pe
+// (lane l takes the rows of threads [8l, 8l + 8)), the same edges as the moment walk with margin 2 per row (each
+// add past 2^53 rounds by at most u/2 <= 2 units below 2^55), exact rows
+// added as integers, rows across an edge added with the double add, and
+// each stretch of rows inside one binade applied as one pair composed in
+// row order (the stretch spread evenly over the lanes, then an ordered
+// tree).  Returns false when it does not apply.
+__device__ bool wave_noise(double* out, uint64_t* exact, const uint64_t* lR, const uint64_t* pe,
+                           int cs, int h) {
+  const int lane = threadIdx.x & 63;
+  constexpr int PER = kT / 64;
+  const int c = PER * cs;
+  const int a = min(lane * c, h), cl = min(c, h - a);
+  uint64_t le = 0;
 #pragma unroll
-  for (int k = 0; k < CM; ++k) {  // every load issued before the first use
-    e[k] = k < c ? RN[a + k] : 0;
-    cnt[k] = 0;
-  }
-  const uint64_t eprev = a > 0 ? RN[a - 1] : 0;
-  __syncthreads();  // earlier readers of stash are done
-#pragma unroll
-  for (int k = 0; k < CM; ++k)
-    if (k < c) stash[a + k] = e[k];  // visible after the scan's barriers
-  uint64_t unused;
-  edges_reg<CM>(
-      h, a, c, e, cnt, [&] { return eprev; }, 0, 2ull * (uint64_t)h, 0, &unused, fl, sm);
-  const uint64_t E = fl.P[kEdges];
-  *exact = E;
-  if (E >= (1ull << 55)) return false;
-  int x[kEdges + 1];
-  uint64_t P[kEdges + 1];
-#pragma unroll
-  for (int j = 0; j <= kEdges; ++j) {
-    x[j] = fl.x[j];
-    P[j] = fl.P[j];
-  }
+  for (int q = 0; q < PER; ++q) le += pe[lane * PER + q];
+  const uint64_t elast = cl > 0 ? lR[a + cl - 1] : 0;
+  const WEdges ed = wave_edges(h, c, le, 0u, elast, 0, 2ull * (uint64_t)h,
+                               [&](int k, uint64_t* e, uint32_t* cc) {
+                                 *e = lR[k];
+                                 *cc = 0;
+                               });
+  *exact = ed.P[kEdges];
+  if (!ed.ok || ed.P[kEdges] >= (1ull << 55)) return false;
   uint64_t s = 0;
   int ia = 0;
   uint64_t Pa = 0;
 #pragma unroll
   for (int g = 0; g <= kEdges; ++g) {
-    const int b = x[g];
+    const int b = ed.x[g];
     if (b < ia) return false;  // edges out of order: not the premise
     if (b > ia) {
       const int ep = fast_plan(g);
       if (ep == kPlanExact) {
-        if (!try_exact(&s, P[g] - Pa)) return false;
+        if (!try_exact(&s, ed.P[g] - Pa)) return false;
       } else if (ep == kPlanCross) {
         double d = (double)s;  // a value the CPU's double holds: exact
-        for (int i = ia; i < b; ++i) d = d + (double)stash[i];
+        for (int i = ia; i < b; ++i) d = d + (double)lR[i];
         s = (uint64_t)d;
       } else if (ep == 53 || ep == 54) {
         const int sh = ep - 52;
+        const int cs = (b - ia + 63) >> 6;
+        const int r0 = min(ia + lane * cs, b), r1 = min(r0 + cs, b);
         Pair64 acc = pair64_id();
-#pragma unroll
-        for (int k = 0; k < CM; ++k) {
-          const int i = a + k;
-          if (k < c && i >= ia && i < b) acc = then64(acc, noise_row_pair(e[k], sh), sh);
-        }
-        const Pair64 pr = block_then(acc, sh, sm);
-        if (!try_apply(&s, pr, ep)) return false;
+        for (int i = r0; i < r1; ++i) acc = then64(acc, noise_row_pair(lR[i], sh), sh);
+        if (!try_apply(&s, wave_then(acc, sh), ep)) return false;
       } else {
         return false;
       }
     }
     ia = b;
-    Pa = P[g];
+    Pa = ed.P[g];
   }
   *out = (double)s;  // an integer the CPU's double holds: exact
   return true;
@@ -1035,24 +1024,54 @@ __device__ __noinline__ void general_walk(const char* plane, long stride, int w,
   __syncthreads();
 }
 
+// One 512-thread block per (frame, job): jobs 0 and 1 the moments of ref and
+// dis, job 2 the PSNR noise.  Fast path: every thread loads the rows' sums
+// into LDS (coalesced), then wave 0 alone walks the plane while the other
+// waves wait at the next barrier (the wave's code has no block barrier);
+// when it does not apply, the whole block takes the general walk.
 __global__ void __launch_bounds__(kT) k_walk(Geometry g, RowArrays ra, double* results,
                                              uint64_t* units, unsigned dbg) {
   __shared__ BlockScratch sm;
   __shared__ RowLds rows;
   __shared__ RunLds runs;
   __shared__ Seg rseg[kMaxSeg + 1], useg[kMaxSeg + 1];
-  __shared__ FastLds fl;
-  __shared__ int staged;
+  __shared__ __attribute__((aligned(16))) RowStage stage[2];
+  __shared__ uint64_t pe[kT], pz[kT];
+  __shared__ uint32_t pc[kT];
+  __shared__ int staged, fast_ok;
   __shared__ uint64_t res[3];
   const int f = blockIdx.x / 3, job = blockIdx.x % 3;
   const int k = g.bpc - 8;
   const double n = (double)g.w * (double)g.h;
+  const int wave = threadIdx.x >> 6;
+  const bool try_fast = dbg == 0 && g.may_round && g.h <= kChunk && g.w <= kStage;
   if (job == 2) {
-    uint64_t ex;
-    double d;
+    uint64_t ex = 0;
+    double d = 0.0;
     const uint64_t* RN = ra.rn + (long)f * g.h;
-    if (!(dbg == 0 && g.may_round && g.h <= kChunk && fast_noise(&d, &ex, RN, g.h, rows.R, fl, sm)))
-      d = noise_chain(RN, g.h, sm, rows.R, &ex);
+    bool fast = false;
+    if (try_fast) {
+      const int cs = (g.h + kT - 1) / kT, i0 = (int)threadIdx.x * cs;
+      uint64_t v[kRowsPer];
+#pragma unroll
+      for (int q = 0; q < kRowsPer; ++q)  // every load issued before the first use
+        v[q] = q < cs && i0 + q < g.h ? RN[i0 + q] : 0;
+      uint64_t e = 0;
+#pragma unroll
+      for (int q = 0; q < kRowsPer; ++q) {
+        if (q < cs && i0 + q < g.h) rows.R[i0 + q] = v[q];
+        e += v[q];
+      }
+      pe[threadIdx.x] = e;
+      __syncthreads();
+      if (wave == 0) {
+        const bool ok = wave_noise(&d, &ex, rows.R, pe, cs, g.h);
+        if (threadIdx.x == 0) fast_ok = ok;
+      }
+      __syncthreads();
+      fast = fast_ok != 0;
+    }
+    if (!fast) d = noise_chain(RN, g.h, sm, rows.R, &ex);
     if (threadIdx.x == 0) {
       const double noise = d * (1.0 / (double)(1u << (2 * k)));
       results[6 * f + 4] = noise;
@@ -1064,6 +1083,8 @@ __global__ void __launch_bounds__(kT) k_walk(Geometry g, RowArrays ra, double* r
   }
   const int pl = job;
   const long off = (long)(pl * g.nframes + f) * g.h;
+  const char* plane =
+      (const char*)(pl == 0 ? g.ref : g.dis) + (long)f * g.pitch * (g.bpc == 8 ? 1 : 2);
   uint64_t S = 0, E = 0, s1 = 0;
   if (!g.may_round) {
     uint64_t a = 0, b = 0;
@@ -1075,18 +1096,49 @@ __global__ void __launch_bounds__(kT) k_walk(Geometry g, RowArrays ra, double* r
     E = S = block_sum_u64(b, sm);
   } else {
     bool fast = false;
-    if (dbg == 0 && g.h <= kFastRows * kT) {
-      const char* plane = (const char*)(pl == 0 ? g.ref : g.dis) +
-                          (long)f * g.pitch * (g.bpc == 8 ? 1 : 2);
-      fast = fast_walk(&S, &E, &s1, ra.r2 + off, ra.codd + off, ra.r1 + off, g.h, plane,
-                       g.stride, g.w, g.bpc == 8, fl, sm);
+    if (try_fast) {
+      const int cs = (g.h + kT - 1) / kT, i0 = (int)threadIdx.x * cs;
+      uint64_t v[kRowsPer];
+      uint32_t cv[kRowsPer], zv[kRowsPer];
+#pragma unroll
+      for (int q = 0; q < kRowsPer; ++q) {  // every load issued before the first use
+        const bool in = q < cs && i0 + q < g.h;
+        v[q] = in ? ra.r2[off + i0 + q] : 0;
+        cv[q] = in ? ra.codd[off + i0 + q] : 0;
+        zv[q] = in ? ra.r1[off + i0 + q] : 0;
+      }
+      uint64_t e = 0, z = 0;
+      uint32_t c = 0;
+#pragma unroll
+      for (int q = 0; q < kRowsPer; ++q) {
+        if (q < cs && i0 + q < g.h) {
+          rows.R[i0 + q] = v[q];
+          rows.C[i0 + q] = (uint16_t)cv[q];  // at most w <= kStage
+        }
+        e += v[q];
+        c += cv[q];
+        z += zv[q];
+      }
+      pe[threadIdx.x] = e;
+      pc[threadIdx.x] = c;
+      pz[threadIdx.x] = z;
+      __syncthreads();
+      if (wave == 0) {
+        uint64_t zz = 0;
+#pragma unroll
+        for (int q = 0; q < kT / 64; ++q) zz += pz[(threadIdx.x & 63) * (kT / 64) + q];
+        s1 = wave_sum_u64(zz);
+        const bool ok = wave_walk(&S, &E, rows.R, rows.C, pe, pc, cs, g.h, plane, g.stride, g.w,
+                                  g.bpc == 8, stage[0], stage[1]);
+        if (threadIdx.x == 0) fast_ok = ok;
+      }
+      __syncthreads();
+      fast = fast_ok != 0;
     }
     if (!fast) {
-      const char* plane = (const char*)(pl == 0 ? g.ref : g.dis) +
-                          (long)f * g.pitch * (g.bpc == 8 ? 1 : 2);
       general_walk(plane, g.stride, g.w, g.h, g.bpc == 8, ra.r2 + off, ra.codd + off,
                    ra.r1 + off, ra.plan + off, ra.pairs + 2 * off, dbg, sm, rows, runs, rseg,
-                   useg, reinterpret_cast<uint16_t*>(fl.term), &staged, res);
+                   useg, stage[0].x, &staged, res);
       S = res[0];
       E = res[1];
       s1 = res[2];

@@ -108,4 +108,32 @@ __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
   return v;
 }
 
+__device__ __forceinline__ uint64_t wave_excl_scan_u64(uint64_t v) {
+  return wave_incl_scan_u64(v) - v;
+}
+__device__ __forceinline__ uint32_t wave_excl_scan_u32(uint32_t v) {
+  return wave_incl_scan_u32(v) - v;
+}
+
+// Lanes whose predicate holds (bit l = lane l); uniform.
+__device__ __forceinline__ uint64_t wave_ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+
+// The value held by lane (l - 1) (lane 0 reads its own).
+__device__ __forceinline__ uint64_t lane_before_u64(uint64_t v) {
+  const int lane = threadIdx.x & 63;
+  const int addr = (lane > 0 ? lane - 1 : 0) << 2;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)(uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Orders this wave's earlier LDS writes before its later LDS reads (LDS
+// serves one wave's accesses in order; this keeps the compiler from
+// moving them).  No other wave is involved.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 }  // namespace
