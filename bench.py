@@ -106,6 +106,8 @@ def main():
     ap.add_argument("--workload", type=int, default=4)
     ap.add_argument("--ring", type=int, default=0, help="device copies of the batch (0 = auto)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
+    ap.add_argument("--no-host", action="store_true",
+                    help="skip the host-memory pipeline figure (PCIe-inclusive context)")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="only run device-to-device copies of MIB MiB (HBM counter "
                          "calibration) and exit")
@@ -194,6 +196,18 @@ def main():
         c_ms, c_n = api.bef_timing_read("ceiling")
         ceiling = batch_bytes / (c_ms / c_n / 1e3) / 1e9
 
+    # context: the same frames from pinned host memory through the library's
+    # two-slot upload pipeline (PCIe-inclusive rate; never the value)
+    host_fps = None
+    if not args.no_host:
+        rp, dp = torch.from_numpy(ref_h).pin_memory(), torch.from_numpy(dis_h).pin_memory()
+        api.bef_frames_host(rp, dp, wl.bpc, w=wl.w)
+        t0 = time.perf_counter()
+        for _ in range(3):
+            api.bef_frames_host(rp, dp, wl.bpc, w=wl.w)
+        host_fps = 3 * F / (time.perf_counter() - t0)
+        del rp, dp
+
     ms_per_step = clean_ms / args.steps
     fps = F * args.steps / (clean_ms / 1e3)
     rows_avg_ms = rows_ms / max(rows_n, 1)
@@ -222,6 +236,7 @@ def main():
                                             / PEAK_HBM_GBS, 4),
                    "walk_avg_us": round(1e3 * walk_ms / max(walk_n, 1), 2),
                    "read_ceiling_GBps": None if ceiling is None else round(ceiling, 1),
+                   "host_pipeline_fps_pcie_inclusive": None if host_fps is None else round(host_fps, 1),
                    "rows_over_read_ceiling": None if ceiling is None else round(achieved / ceiling, 4),
                    "timed_with_events_ms_per_step": round(total_ms / args.steps, 5)},
         "roofline": {"bound": "hbm", "kernel": "k_rows16", "achieved": round(achieved, 1),

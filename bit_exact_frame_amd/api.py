@@ -41,8 +41,9 @@ _lib.bef_frames.argtypes = [_vp, _vp, _i, _i, _pd, _pd, _i, _i, _vp, _dp, _dp]
 _lib.bef_frames_async.argtypes = [_vp, _vp, _i, _i, _pd, _pd, _i, _i, _vp, _vp]
 _lib.bef_frames_units.argtypes = [_vp, _vp, _i, _i, _pd, _pd, _i, _i, _vp, _u64p]
 _lib.bef_read_ceiling.argtypes = [_vp, _vp, _i, _i, _pd, _pd, _i, _vp, _vp]
+_lib.bef_frames_host.argtypes = [_vp, _vp, _i, _i, _pd, _pd, _i, _i, _i, _dp, _dp]
 for _n in ("moment_frame", "psnr_noise", "bef_frames", "bef_frames_async",
-           "bef_frames_units", "bef_read_ceiling"):
+           "bef_frames_units", "bef_read_ceiling", "bef_frames_host"):
     getattr(_lib, _n).restype = _i
 _lib.bef_last_error.restype = ctypes.c_char_p
 _lib.bef_debug_set.argtypes = [_u]
@@ -135,6 +136,39 @@ def bef_frames(ref, dis, bpc: int, w: int | None = None, stream=None):
     _check(_lib.bef_frames(ref.data_ptr(), dis.data_ptr(), w, h, stride, h * stride, f,
                            bpc, _stream_ptr(stream), mom.ctypes.data_as(_dp),
                            ps.ctypes.data_as(_dp)), "bef_frames")
+    return mom, ps
+
+
+def _host_geom(t, bpc, w):
+    want = np.uint8 if bpc == 8 else np.uint16
+    if isinstance(t, np.ndarray):
+        if t.dtype != want or not t.flags.c_contiguous:
+            raise BefError(f"bpc {bpc} needs C-contiguous {want.__name__} host planes")
+        ptr = t.ctypes.data
+    else:  # a CPU torch tensor (pinned or not)
+        import torch
+        if t.is_cuda or not t.is_contiguous():
+            raise BefError("host planes must be contiguous CPU tensors or arrays")
+        if t.dtype != (torch.uint8 if bpc == 8 else torch.uint16):
+            raise BefError(f"bpc {bpc} needs {want.__name__} host planes")
+        ptr = t.data_ptr()
+    h, stride = t.shape[-2], t.shape[-1]
+    f = t.shape[0] if t.ndim == 3 else 1
+    return ptr, f, h, stride, (stride if w is None else int(w))
+
+
+def bef_frames_host(ref, dis, bpc: int, w: int | None = None, device: int = 0):
+    """Batch from HOST planes (numpy arrays or CPU tensors, (F, h, stride) or
+    (h, stride)): returns (moments float64[F,4], psnr float64[F,2])."""
+    pr, f, h, stride, w = _host_geom(ref, bpc, w)
+    pd, f2, h2, stride2, _ = _host_geom(dis, bpc, w)
+    if (f2, h2, stride2) != (f, h, stride):
+        raise BefError("ref and dis shapes differ")
+    mom = np.zeros((f, 4), np.float64)
+    ps = np.zeros((f, 2), np.float64)
+    _check(_lib.bef_frames_host(ctypes.c_void_p(pr), ctypes.c_void_p(pd), w, h, stride,
+                                h * stride, f, bpc, int(device), mom.ctypes.data_as(_dp),
+                                ps.ctypes.data_as(_dp)), "bef_frames_host")
     return mom, ps
 
 

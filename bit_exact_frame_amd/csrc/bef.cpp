@@ -9,6 +9,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -30,6 +31,11 @@ struct Arena {
   size_t cap = 0;
   void* host = nullptr;  // pinned read-back staging
   size_t host_cap = 0;
+  // frames from host memory: two device slots, two streams, their events
+  void* pipe = nullptr;
+  size_t pipe_cap = 0;
+  hipStream_t copy_st = nullptr, comp_st = nullptr;
+  hipEvent_t copied[2] = {nullptr, nullptr}, done[2] = {nullptr, nullptr};
 };
 Arena g_arena[kMaxDev];
 
@@ -314,6 +320,100 @@ struct DevGuard {
   }
 };
 
+// Frames from host memory, streamed in chunks through two device slots:
+// the upload of chunk n (copy stream) overlaps the reductions of chunk
+// n - 1 (compute stream); a slot is reloaded only after the chunk before
+// last has been reduced from it.
+constexpr size_t kPipeChunkBytes = 64ull << 20;  // per plane and chunk
+
+int pipe_setup(int dev, size_t slot_bytes, size_t res_bytes) {
+  Arena& a = g_arena[dev];
+  if (!a.copy_st) {
+    BEF_HIP(hipStreamCreateWithFlags(&a.copy_st, hipStreamNonBlocking));
+    BEF_HIP(hipStreamCreateWithFlags(&a.comp_st, hipStreamNonBlocking));
+    for (int k = 0; k < 2; ++k) {
+      BEF_HIP(hipEventCreateWithFlags(&a.copied[k], hipEventDisableTiming));
+      BEF_HIP(hipEventCreateWithFlags(&a.done[k], hipEventDisableTiming));
+    }
+  }
+  const size_t need = 4 * slot_bytes + up256(res_bytes);  // 2 slots x 2 planes, results
+  if (a.pipe_cap < need) {
+    if (a.pipe) BEF_HIP(hipFree(a.pipe));
+    a.pipe = nullptr;
+    a.pipe_cap = 0;
+    if (hipMalloc(&a.pipe, need) != hipSuccess) {
+      (void)hipGetLastError();
+      a.pipe = nullptr;
+      return fail(-ENOMEM, "hipMalloc of %zu bytes of frame slots failed", need);
+    }
+    a.pipe_cap = need;
+  }
+  return 0;
+}
+
+int run_host(const void* ref, const void* dis, int w, int h, ptrdiff_t stride, ptrdiff_t pitch,
+             int nframes, int bpc, int dev, double* moments, double* psnr) {
+  if (!ref || !dis) return fail(-EINVAL, "NULL plane pointer");
+  int ndev = 0;
+  BEF_HIP(hipGetDeviceCount(&ndev));
+  if (dev < 0 || dev >= ndev || dev >= kMaxDev) return fail(-EINVAL, "device %d out of range", dev);
+  // geometry checks on the host side (device pointers are checked per chunk)
+  int rc = validate(ref, dis, w, h, stride, pitch, nframes, bpc);
+  if (rc) return rc;
+  BEF_HIP(hipSetDevice(dev));
+  const size_t B = bpc == 8 ? 1 : 2;
+  const size_t fbytes = (size_t)h * (size_t)stride * B;  // one plane of one frame
+  const int K = (int)std::max<size_t>(1, std::min<size_t>((size_t)nframes, kPipeChunkBytes / fbytes));
+  const size_t slot = up256((size_t)K * fbytes);
+  if ((rc = pipe_setup(dev, slot, (size_t)nframes * 6 * 8))) return rc;
+  Arena& a = g_arena[dev];
+  double* d_res = (double*)((char*)a.pipe + 4 * slot);  // every frame's results
+  const bool contiguous = (size_t)pitch * B == fbytes || nframes == 1;
+  const int nchunks = (nframes + K - 1) / K;
+  for (int ci = 0; ci < nchunks; ++ci) {
+    const int k0 = ci * K, kn = std::min(K, nframes - k0), sl = ci & 1;
+    char* dref = (char*)a.pipe + (size_t)sl * 2 * slot;
+    char* ddis = dref + slot;
+    if (ci >= 2) BEF_HIP(hipStreamWaitEvent(a.copy_st, a.done[sl], 0));
+    for (int pl = 0; pl < 2; ++pl) {
+      const char* src = (const char*)(pl == 0 ? ref : dis) + (size_t)k0 * (size_t)pitch * B;
+      char* dst = pl == 0 ? dref : ddis;
+      if (contiguous) {
+        BEF_HIP(hipMemcpyAsync(dst, src, (size_t)kn * fbytes, hipMemcpyHostToDevice, a.copy_st));
+      } else {
+        for (int f = 0; f < kn; ++f)
+          BEF_HIP(hipMemcpyAsync(dst + (size_t)f * fbytes, src + (size_t)f * (size_t)pitch * B,
+                                 fbytes, hipMemcpyHostToDevice, a.copy_st));
+      }
+    }
+    BEF_HIP(hipEventRecord(a.copied[sl], a.copy_st));
+    BEF_HIP(hipStreamWaitEvent(a.comp_st, a.copied[sl], 0));
+    Call c;
+    if ((rc = prepare(c, dref, ddis, w, h, stride, (ptrdiff_t)(h * stride), kn, bpc))) break;
+    if ((rc = enqueue(c, a.comp_st, d_res + 6 * (size_t)k0))) break;
+    BEF_HIP(hipEventRecord(a.done[sl], a.comp_st));
+  }
+  if (rc == 0) {
+    double* hres = (double*)g_arena[dev].host;
+    const size_t rb = (size_t)nframes * 6 * 8;
+    if ((rc = ensure(dev, 0, rb + 256)) == 0) {
+      hres = (double*)g_arena[dev].host;
+      BEF_HIP(hipMemcpyAsync(hres, d_res, rb, hipMemcpyDeviceToHost, a.comp_st));
+      BEF_HIP(hipStreamSynchronize(a.comp_st));
+      for (int f = 0; f < nframes; ++f) {
+        if (moments)
+          for (int k = 0; k < 4; ++k) moments[4 * f + k] = hres[6 * f + k];
+        if (psnr)
+          for (int k = 0; k < 2; ++k) psnr[2 * f + k] = hres[6 * f + 4 + k];
+      }
+    }
+  }
+  (void)hipStreamSynchronize(a.comp_st);
+  (void)hipStreamSynchronize(a.copy_st);
+  if (g_timing) ev_collect();
+  return rc;
+}
+
 }  // namespace
 
 extern "C" {
@@ -366,6 +466,15 @@ int bef_read_ceiling(const void* ref, const void* dis, int w, int h, ptrdiff_t s
     return launch_read_ceiling(c.g, dev_out, st, a, b);
   }));
   return 0;
+}
+
+int bef_frames_host(const void* ref, const void* dis, int w, int h, ptrdiff_t stride,
+                    ptrdiff_t frame_pitch, int nframes, int bpc, int device, double* moments,
+                    double* psnr) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_err.clear();
+  DevGuard dg;
+  return run_host(ref, dis, w, h, stride, frame_pitch, nframes, bpc, device, moments, psnr);
 }
 
 int moment_frame(const void* ref, const void* dis, int w, int h, ptrdiff_t stride, int bpc,
@@ -425,6 +534,13 @@ void bef_release(void) {
     (void)hipSetDevice(d);
     if (a.base) (void)hipFree(a.base);
     if (a.host) (void)hipHostFree(a.host);
+    if (a.pipe) (void)hipFree(a.pipe);
+    for (int k = 0; k < 2; ++k) {
+      if (a.copied[k]) (void)hipEventDestroy(a.copied[k]);
+      if (a.done[k]) (void)hipEventDestroy(a.done[k]);
+    }
+    if (a.copy_st) (void)hipStreamDestroy(a.copy_st);
+    if (a.comp_st) (void)hipStreamDestroy(a.comp_st);
     a = Arena();
   }
 }

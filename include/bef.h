@@ -82,6 +82,19 @@ int bef_frames_async(const void *ref, const void *dis, int w, int h,
                      ptrdiff_t stride, ptrdiff_t frame_pitch, int nframes,
                      int bpc, void *stream, double *dev_results);
 
+/* As bef_frames, for frames in HOST memory (ref, dis: host pointers, same
+ * layout and limits), on device `device`, synchronously.  The library
+ * streams the frames through two device slots of up to 64 MiB per plane:
+ * the upload of one chunk of frames (on a library copy stream) overlaps
+ * the reductions of the previous chunk (on a library compute stream).
+ * Pinned host memory (hipHostMalloc, torch pin_memory) lets the uploads run
+ * at the link's rate; pageable memory is staged by the HIP runtime.  The
+ * slots are kept until bef_release().  moments / psnr: HOST, as in
+ * bef_frames (either may be NULL). */
+int bef_frames_host(const void *ref, const void *dis, int w, int h,
+                    ptrdiff_t stride, ptrdiff_t frame_pitch, int nframes,
+                    int bpc, int device, double *moments, double *psnr);
+
 /* Diagnostics: per-frame integer sums in units, synchronously.
  * units (HOST, [nframes][8]) = {S1_ref, S1_dis, S2_ref_exact, S2_dis_exact,
  * S2_ref_cpu, S2_dis_cpu, noise_exact, bits of the noise double in units}.

@@ -219,6 +219,26 @@ def test_deterministic(api):
     assert (a == b).all()
 
 
+@pytest.mark.parametrize("key,pinned", [(5, False), (5, True), (3, True)])
+def test_host_pipeline_matches_device(api, orc, key, pinned):
+    """Frames from host memory, streamed through the two device slots (the
+    12-bit workload takes four chunks, so both slots are reloaded), give the
+    same bits as the device entry point and the oracle."""
+    import torch
+    wl = synth.WORKLOADS[key]
+    ref, dis = synth.make_frames(key)
+    say(f"[gpu] host pipeline workload {key} pinned={pinned}")
+    if pinned:
+        r, d = torch.from_numpy(ref).pin_memory(), torch.from_numpy(dis).pin_memory()
+    else:
+        r, d = ref, dis
+    hmom, hps = api.bef_frames_host(r, d, wl.bpc, w=wl.w)
+    mom, ps = api.bef_frames(dev(ref), dev(dis), wl.bpc, w=wl.w)
+    assert (bits(hmom) == bits(mom)).all() and (bits(hps) == bits(ps)).all()
+    emom, eps = expect(orc, ref[:2], dis[:2], wl.bpc, wl.w)
+    assert (bits(hmom[:2]) == bits(emom)).all() and (bits(hps[:2]) == bits(eps)).all()
+
+
 def test_read_ceiling_diagnostic(api):
     """The read-only diagnostic pass runs on the row pass's shapes, gives
     the same words twice, and rejects rows with no whole 4-byte chunk."""
