@@ -866,6 +866,13 @@ __device__ bool wave_walk(uint64_t* out, uint64_t* exact, const uint64_t* lE, co
     if (b > ia) {
       if (g == 1 || g == 3) {
         for (int i = ia; i < b; ++i) {
+          // a row that, from the actual S, adds exactly or stays inside its
+          // binade needs no samples (rows of zeros after a crossing, say)
+          if (try_exact(&s, lE[i])) continue;
+          if (s >= kTwo53) {
+            const int e = binade(s);
+            if (e <= 54 && try_apply(&s, closed_pair(lE[i], lC[i], e), e)) continue;
+          }
           RowStage& sg = g == 1 ? st0 : st1;
           if (i != (g == 1 ? ra : rb)) {  // a further row of the stretch
             wave_lds_sync();

@@ -118,6 +118,11 @@ SHAPES = [
     (176, 144, 192, 8, 2),     # 8-bit with stride padding
     (1000, 37, 1000, 8, 2),    # 8-bit ragged
     (32768, 2, 32768, 16, 1),  # widest row
+    (97, 11, 97, 9, 2),        # every bit depth from 9 to 15
+    (130, 7, 132, 11, 2),
+    (256, 5, 256, 13, 2),
+    (300, 6, 304, 14, 2),
+    (33, 40, 40, 15, 3),
 ]
 
 
@@ -173,6 +178,37 @@ def test_past_2_55_4096x2560(api, orc):
     ref[mask] = rng.integers(0, 8192, size=int(mask.sum())).astype(np.uint16)
     dis = rng.integers(0, 65536, size=ref.shape).astype(np.uint16)
     check_batch(api, orc, ref, dis, 16, label="4096x2560 past 2^55")
+
+
+def test_wide_rows_past_2_53(api, orc):
+    """7680x1100 full-range noise crosses 2^53 in a row wider than the fast
+    path stages (the general walk reads such rows from memory)."""
+    ref, dis = synth.uniform_planes(7681, 1, 1100, 7680, 7680, 16)
+    units = api.bef_frames_units(dev(ref), dev(dis), 16)
+    assert (units[:, 2] > 1 << 53).all()
+    check_batch(api, orc, ref, dis, 16, label="7680x1100")
+
+
+def test_tall_plane_past_2_53(api, orc):
+    """1024x8192 full-range noise: more rows than the walk holds in LDS."""
+    ref, dis = synth.uniform_planes(8193, 1, 8192, 1024, 1024, 16)
+    units = api.bef_frames_units(dev(ref), dev(dis), 16)
+    assert (units[:, 2] > 1 << 53).all()
+    check_batch(api, orc, ref, dis, 16, label="1024x8192")
+
+
+def test_letterbox_rows_of_zeros_after_2_53(api, orc):
+    """Bright rows take the exact sum to 2^53 + 5000, then rows of zeros (a
+    black band) follow while the sum sits within the walk's margin of the
+    edge: every such row is checked against the actual running sum."""
+    ref = np.zeros((2, 2160, 3840), np.uint16)
+    for f in range(2):
+        boundary._fill_to(ref[f].reshape(-1), 0, (1 << 53) + 5000, 40000, 65536,
+                          np.random.Generator(np.random.PCG64(1653 + f)), False)
+    dis = synth.uniform_planes(1653, 2, 2160, 3840, 3840, 16)[1]
+    units = api.bef_frames_units(dev(ref), dev(dis), 16)
+    assert (units[:, 2] == (1 << 53) + 5000).all()
+    check_batch(api, orc, ref, dis, 16, label="letterbox")
 
 
 def test_noise_past_2_54(api, orc):
