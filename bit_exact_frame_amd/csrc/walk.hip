@@ -702,24 +702,27 @@ __device__ __forceinline__ bool fast_apply(uint64_t* s, int g, uint64_t Eg, uint
 }
 
 // A crossing row staged in LDS by one wave: samples (zeros from w up to
-// the lanes' last run), and per 8-sample chunk the exact sum of the float
-// squares (units) and their odd count.
+// the lanes' last run), and each lane's run sums: the exact sum of its
+// terms (float squares in units) and their odd count.
 struct RowStage {
   uint16_t x[kStage];
-  uint64_t chE[kStage / 8];
-  uint8_t chC[kStage / 8];
+  uint64_t runE[64];
+  uint32_t runC[64];
 };
 
 // Samples of a row's term run: lane l takes chunks [l*cpl, l*cpl + cpl) of
 // 8 samples, cpl = ceil(ceil(w / 8) / 64).
 __device__ __forceinline__ int run_chunks(int w) { return (((w + 7) >> 3) + 63) >> 6; }
 
-// Loads row i of the plane into st by one wave (16-byte loads when the row
-// allows them, then every chunk's term sums from the loaded registers).
+// Loads row i of the plane into st by one wave: each lane loads its own
+// run (16-byte loads when the row allows them) and sums its terms from the
+// loaded registers.
 __device__ void wave_stage_row(RowStage& st, int i, const void* plane, long stride, int w,
                                int bpc8) {
   const int lane = threadIdx.x & 63;
-  const int nch = 64 * run_chunks(w);  // chunks through the last lane's run
+  const int cpl = run_chunks(w);
+  uint64_t e = 0;
+  uint32_t c = 0;
   if (!bpc8) {
     const uint16_t* row = (const uint16_t*)plane + (long)i * stride;
     if (((uintptr_t)row & 15) == 0 && (w & 7) == 0) {
@@ -728,66 +731,57 @@ __device__ void wave_stage_row(RowStage& st, int i, const void* plane, long stri
       v4u v[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {  // every load issued before the first use
-        const int cidx = lane + 64 * u;
-        v[u] = cidx < nv ? ((const v4u*)row)[cidx] : (v4u){0u, 0u, 0u, 0u};
+        const int cidx = lane * cpl + u;
+        v[u] = u < cpl && cidx < nv ? ((const v4u*)row)[cidx] : (v4u){0u, 0u, 0u, 0u};
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int cidx = lane + 64 * u;
-        if (cidx < nch) {
-          ((v4u*)st.x)[cidx] = v[u];
-          uint64_t e = 0;
-          uint32_t c = 0;
+        if (u < cpl) {
+          ((v4u*)st.x)[lane * cpl + u] = v[u];
 #pragma unroll
           for (int q = 0; q < 8; ++q) {
             const uint32_t t = fsq_units((v[u][q >> 1] >> (16 * (q & 1))) & 0xFFFFu);
             e += t;
             c += t & 1u;
           }
-          st.chE[cidx] = e;
-          st.chC[cidx] = (uint8_t)c;
         }
       }
+      st.runE[lane] = e;
+      st.runC[lane] = c;
       return;
     }
-    for (int j = lane; j < nch * 8; j += 64) st.x[j] = j < w ? row[j] : (uint16_t)0;
-  } else {
-    const uint8_t* row = (const uint8_t*)plane + (long)i * stride;
-    for (int j = lane; j < nch * 8; j += 64) st.x[j] = j < w ? row[j] : (uint16_t)0;
-  }
-  wave_lds_sync();
-  for (int cidx = lane; cidx < nch; cidx += 64) {
-    uint64_t e = 0;
-    uint32_t c = 0;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const uint32_t t = fsq_units(st.x[8 * cidx + q]);
+    for (int j = lane * 8 * cpl, k = 0; k < 8 * cpl; ++j, ++k) {
+      const uint32_t x = j < w ? row[j] : 0u;
+      st.x[j] = (uint16_t)x;
+      const uint32_t t = fsq_units(x);
       e += t;
       c += t & 1u;
     }
-    st.chE[cidx] = e;
-    st.chC[cidx] = (uint8_t)c;
+  } else {
+    const uint8_t* row = (const uint8_t*)plane + (long)i * stride;
+    for (int j = lane * 8 * cpl, k = 0; k < 8 * cpl; ++j, ++k) {
+      const uint32_t x = j < w ? row[j] : 0u;
+      st.x[j] = (uint16_t)x;
+      const uint32_t t = fsq_units(x);
+      e += t;
+      c += t & 1u;
+    }
   }
+  st.runE[lane] = e;
+  st.runC[lane] = c;
 }
 
 // Row (staged in st) planned across an edge, from S = *sp: lane l takes
-// the terms of its run_chunks(w) chunks, the terms' edges with margin
-// w * u/2 (u the last place of the binade above S), closed forms, and the
-// terms across an edge added with the double add (the CPU's step).
+// the terms of its run, the terms' edges with margin w * u/2 (u the last
+// place of the binade above S), closed forms, and the terms across an edge
+// added with the double add (the CPU's step).
 __device__ bool wave_cross_row(uint64_t* sp, const RowStage& st, int w) {
   const int lane = threadIdx.x & 63;
   const uint64_t s0 = *sp;
-  const int cpl = run_chunks(w), L = 8 * cpl;
+  const int L = 8 * run_chunks(w);
   const int a = min(lane * L, w), cl = min(L, w - a);
-  uint64_t le = 0;
-  uint32_t lc = 0;
-  constexpr int CMAXR = kStage / 8 / 64;
-#pragma unroll
-  for (int q = 0; q < CMAXR; ++q)
-    if (q < cpl) {  // zeros past w add nothing
-      le += st.chE[lane * cpl + q];
-      lc += st.chC[lane * cpl + q];
-    }
+  const uint64_t le = st.runE[lane];
+  const uint32_t lc = st.runC[lane];
   const uint64_t elast = cl > 0 ? fsq_units(st.x[a + cl - 1]) : 0;
   const int eB = (s0 < kTwo53 ? 53 : binade(s0)) + 1;
   const uint64_t Mr = (uint64_t)w << (eB - 53);
@@ -1131,12 +1125,12 @@ __global__ void __launch_bounds__(kT) k_walk(Geometry g, RowArrays ra, double* r
       pz[threadIdx.x] = z;
       __syncthreads();
       if (wave == 0) {
-        uint64_t zz = 0;
+        const bool ok = wave_walk(&S, &E, rows.R, rows.C, pe, pc, cs, g.h, plane, g.stride, g.w,
+                                  g.bpc == 8, stage[0], stage[1]);
+        uint64_t zz = 0;  // the first-moment sum, off the walk's path
 #pragma unroll
         for (int q = 0; q < kT / 64; ++q) zz += pz[(threadIdx.x & 63) * (kT / 64) + q];
         s1 = wave_sum_u64(zz);
-        const bool ok = wave_walk(&S, &E, rows.R, rows.C, pe, pc, cs, g.h, plane, g.stride, g.w,
-                                  g.bpc == 8, stage[0], stage[1]);
         if (threadIdx.x == 0) fast_ok = ok;
       }
       __syncthreads();
