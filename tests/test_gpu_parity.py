@@ -275,6 +275,29 @@ def test_host_pipeline_matches_device(api, orc, key, pinned):
     assert (bits(hmom[:2]) == bits(emom)).all() and (bits(hps[:2]) == bits(eps)).all()
 
 
+def test_host_pipeline_frame_pitch(api, orc):
+    """Host frames that are not contiguous (a frame pitch above h * stride)
+    are uploaded frame by frame; same bits as the device path."""
+    import ctypes
+    wl = synth.WORKLOADS[3]
+    ref, dis = synth.make_frames(3, frames=5)
+    F, h, stride = ref.shape
+    gap = 3  # rows of padding between frames
+    rbig = np.full((F, h + gap, stride), 0xFFFF, np.uint16)
+    dbig = np.full((F, h + gap, stride), 0xFFFF, np.uint16)
+    rbig[:, :h] = ref
+    dbig[:, :h] = dis
+    mom = np.zeros((F, 4), np.float64)
+    ps = np.zeros((F, 2), np.float64)
+    dp = ctypes.POINTER(ctypes.c_double)
+    rc = api.lib().bef_frames_host(rbig.ctypes.data, dbig.ctypes.data, wl.w, h, stride,
+                                   (h + gap) * stride, F, wl.bpc, 0, mom.ctypes.data_as(dp),
+                                   ps.ctypes.data_as(dp))
+    assert rc == 0, api.last_error()
+    dmom, dps = api.bef_frames(dev(ref), dev(dis), wl.bpc, w=wl.w)
+    assert (bits(mom) == bits(dmom)).all() and (bits(ps) == bits(dps)).all()
+
+
 def test_read_ceiling_diagnostic(api):
     """The read-only diagnostic pass runs on the row pass's shapes, gives
     the same words twice, and rejects rows with no whole 4-byte chunk."""
