@@ -59,6 +59,7 @@ _lib.bef_host_noise_units.argtypes = [_vp, _vp, _i, _i, _pd, _i, _u64p, _u64p]
 _lib.bef_host_rne53_add.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
 _lib.bef_host_rne53_add.restype = ctypes.c_uint64
 _lib.bef_host_run_pair.argtypes = [_vp, _i, _i, _u64p]
+_lib.bef_host_load_shape.argtypes = [_vp, _vp, _i, _pd, _pd, _i, ctypes.POINTER(ctypes.c_int)]
 
 DBG_PLAN_WRONG = 1
 DBG_PLAN_NONE = 2
@@ -262,3 +263,13 @@ def bef_host_run_pair(terms: np.ndarray, e: int):
     out = (ctypes.c_uint64 * 2)()
     _check(_lib.bef_host_run_pair(t.ctypes.data, t.size, e, out), "bef_host_run_pair")
     return list(out)
+
+
+def bef_host_load_shape(ref_addr: int, dis_addr: int, w: int, stride: int, frame_pitch: int,
+                        nframes: int):
+    """(bytes per load, load slots per group) the row kernel uses for planes
+    at these addresses (alignment only; nothing is read)."""
+    out = (ctypes.c_int * 2)()
+    _check(_lib.bef_host_load_shape(ctypes.c_void_p(ref_addr), ctypes.c_void_p(dis_addr), w,
+                                    stride, frame_pitch, nframes, out), "bef_host_load_shape")
+    return out[0], out[1]

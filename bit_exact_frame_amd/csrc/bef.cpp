@@ -522,6 +522,13 @@ void bef_timing_reset(void) {
   }
 }
 
+int bef_host_load_shape(const void* ref, const void* dis, int w, ptrdiff_t stride,
+                        ptrdiff_t frame_pitch, int nframes, int out[2]) {
+  if (!out || w <= 0 || nframes <= 0) return -EINVAL;
+  load_shape(ref, dis, w, stride, frame_pitch, nframes, &out[0], &out[1]);
+  return 0;
+}
+
 void bef_release(void) {
   std::lock_guard<std::mutex> lk(g_mu);
   ev_collect();

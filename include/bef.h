@@ -164,6 +164,12 @@ int bef_host_noise_units(const void *ref, const void *dis, int w, int h,
                          uint64_t *exact);
 /* The one-term step: fl64(s + t) in units. */
 uint64_t bef_host_rne53_add(uint64_t s, uint64_t t);
+/* The 16-bit row kernel's load shape for planes at these addresses (only
+ * their alignment is used; nothing is read): out = {bytes per load (16, 8,
+ * 4, or 0 for sample by sample), load slots per lane per group}. */
+int bef_host_load_shape(const void *ref, const void *dis, int w,
+                        ptrdiff_t stride, ptrdiff_t frame_pitch, int nframes,
+                        int out[2]);
 /* Pair of a run of terms inside binade e: out = {inc_even, inc_odd}. */
 int bef_host_run_pair(const uint32_t *terms, int n, int e, uint64_t out[2]);
 

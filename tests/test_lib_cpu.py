@@ -201,6 +201,44 @@ def test_host_noise_matches_oracle(api, orc):
         assert ex == checkers.psnr_units(r[0], d[0])[1]
 
 
+# ------------------------------------------------------ row kernel shape --
+
+# (bytes per load, slots per group) the row kernel's launcher instantiates
+LAUNCHED = {(16, 4), (16, 5), (16, 8), (8, 4), (8, 5), (8, 8), (8, 15), (4, 4), (4, 5),
+            (4, 8), (4, 15), (0, 1)}
+
+
+def test_load_shape_choice(api):
+    """For many widths and alignments the host picks a load width that the
+    rows allow, a shape the launcher has a kernel for, and no more idle lane
+    slots than any allowed shape would leave."""
+    rng = np.random.Generator(np.random.PCG64(44))
+    widths = [1, 3, 4, 7, 8, 64, 100, 176, 511, 512, 520, 1000, 1280, 1920, 2560, 3840,
+              4096, 4100, 7680, 32768] + [int(x) for x in rng.integers(1, 32769, size=60)]
+    for w in widths:
+        for base_align in (2, 4, 8, 16, 256):
+            for extra in (0, 1, 3):
+                stride = w + extra
+                ref = 0x100000 + base_align
+                cb, ng = api.bef_host_load_shape(ref, ref + 0x4000000, w, stride, stride * 9, 2)
+                assert (cb, ng) in LAUNCHED, (w, base_align, extra, cb, ng)
+                align = 16
+                for v in (ref, ref + 0x4000000, stride * 2, stride * 18):
+                    while align > 1 and v % align:
+                        align //= 2
+                if cb:
+                    assert cb <= align and cb in (4, 8, 16), (w, cb, align)
+                    nc = w * 2 // cb
+                    nper = -(-nc // 64)
+                    idle = (-(-nper // ng) * ng * 64 - nc) * cb
+                    best = min(((-(-(-(-(w * 2 // c) // 64)) // g) * g * 64 - w * 2 // c) * c)
+                               for c in (16, 8, 4) if c <= align and w * 2 // c > 0
+                               for g in (15, 8, 5, 4) if not (g == 15 and c == 16))
+                    assert idle == best, (w, align, cb, ng, idle, best)
+                else:
+                    assert align < 4 or w * 2 < 4, (w, align)
+
+
 # ------------------------------------------------ planted breaks (header) --
 
 MUTANTS = {
