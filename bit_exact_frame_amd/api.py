@@ -59,6 +59,8 @@ _lib.bef_host_noise_units.argtypes = [_vp, _vp, _i, _i, _pd, _i, _u64p, _u64p]
 _lib.bef_host_rne53_add.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
 _lib.bef_host_rne53_add.restype = ctypes.c_uint64
 _lib.bef_host_run_pair.argtypes = [_vp, _i, _i, _u64p]
+_lib.bef_host_fast_units.argtypes = [_vp, _i, _i, _pd, _i, _u64p]
+_lib.bef_host_fast_noise.argtypes = [_vp, _vp, _i, _i, _pd, _i, _u64p]
 _lib.bef_host_load_shape.argtypes = [_vp, _vp, _i, _pd, _pd, _i, ctypes.POINTER(ctypes.c_int)]
 
 DBG_PLAN_WRONG = 1
@@ -252,6 +254,26 @@ def bef_host_noise_units(ref: np.ndarray, dis: np.ndarray, bpc: int, w: int | No
                                      ctypes.byref(bits), ctypes.byref(ex)),
            "bef_host_noise_units")
     return bits.value, ex.value
+
+
+def bef_host_fast_units(plane: np.ndarray, bpc: int, w: int | None = None):
+    """[handled, S_cpu, S_exact] of the fast path's decisions on one plane."""
+    h, stride = plane.shape
+    w = stride if w is None else w
+    out = (ctypes.c_uint64 * 3)()
+    _check(_lib.bef_host_fast_units(plane.ctypes.data, w, h, stride, bpc, out),
+           "bef_host_fast_units")
+    return list(out)
+
+
+def bef_host_fast_noise(ref: np.ndarray, dis: np.ndarray, bpc: int, w: int | None = None):
+    """[handled, bits of the noise double in units, exact] of the fast noise."""
+    h, stride = ref.shape
+    w = stride if w is None else w
+    out = (ctypes.c_uint64 * 3)()
+    _check(_lib.bef_host_fast_noise(ref.ctypes.data, dis.ctypes.data, w, h, stride, bpc, out),
+           "bef_host_fast_noise")
+    return list(out)
 
 
 def bef_host_rne53_add(s: int, t: int) -> int:

@@ -1,7 +1,10 @@
 // host_emu.cpp -- the device algorithm's steps run serially on the host.
 //
 // Test entry points only (bef_host_*): they take HOST planes and follow the
-// same decomposition as the kernels -- exact per-row sums, a per-row plan
+// same decisions as the kernels, with the integer steps of ordsum.h.  The
+// fast path: the plan as five threshold edges, exact and closed-form
+// segments, rows and terms at an edge one by one, noise stretches as
+// composed row pairs.  The general walk: exact per-row sums, a per-row plan
 // from the exact prefix, row pairs from 64 lane runs joined by an ordered
 // tree, a walk over stretches of rows with the same plan, a fallback of
 // each unfit row to 256 runs (planned by their own exact prefix) and of
@@ -84,10 +87,7 @@ struct Emu {
   // 64 lane runs of ceil(w/64) terms, each a two-trajectory fold, joined by
   // an ordered tree and widened with R.
   Pair64 row_pair(int i, int e) const {
-    if (e <= 54 && !(dbg & BEF_DBG_NO_CLOSED_FORM)) {
-      const uint64_t a0 = R[i] - C[i];
-      return Pair64{a0, (e == 53 && C[i] > 0) ? a0 + 2 : a0};
-    }
+    if (e <= 54 && !(dbg & BEF_DBG_NO_CLOSED_FORM)) return closed_pair(R[i], C[i], e);
     const int sh = e - 52;
     const int L = (pl.w + 63) / 64;
     std::vector<Pair32> lanes(64);
@@ -211,6 +211,165 @@ struct Emu {
   }
 };
 
+// ---------------------------------------------------------------------------
+// The fast path's decisions, serially: each edge of the plan is the first
+// item meeting its condition (edge_conds), then the segments in order --
+// exact adds, closed-form pairs, and the items across an edge one by one.
+// The device finds the same first items with lane chunks and a second
+// scan; the decisions and every arithmetic step are these.
+
+struct Edges {
+  int x[kEdges + 1];
+  uint64_t P[kEdges + 1], PC[kEdges + 1];
+};
+
+template <class EAt, class CAt>
+Edges first_items(int n, uint64_t base, uint64_t M, EAt e_at, CAt c_at) {
+  Edges r;
+  uint64_t q = base, qc = 0;
+  unsigned seen = 0;
+  for (int j = 0; j <= kEdges; ++j) r.x[j] = n;
+  for (int k = 0; k < n; ++k) {
+    const uint64_t e = e_at(k);
+    const unsigned now = edge_conds(q, q + e, M), fresh = now & ~seen;
+    for (int j = 0; j < kEdges; ++j)
+      if ((fresh >> j) & 1u) r.x[j] = k, r.P[j] = q, r.PC[j] = qc;
+    seen |= now;
+    q += e;
+    qc += c_at(k);
+  }
+  for (int j = 0; j <= kEdges; ++j)
+    if (r.x[j] == n) r.P[j] = q, r.PC[j] = qc;
+  return r;
+}
+
+struct Fast {
+  Plane pl;
+  std::vector<uint64_t> R, C;
+
+  uint32_t T(int i, int j) const { return fsq_units(pl.x(i, j)); }
+
+  // A row across an edge: its terms' edges from the actual S with margin
+  // w * u/2, closed forms, and the terms at an edge by the one-term step.
+  bool cross_row(uint64_t* sp, int i) const {
+    const uint64_t s0 = *sp;
+    const int eB = (s0 < kTwo53 ? 53 : binade(s0)) + 1;
+    const uint64_t Mr = (uint64_t)pl.w << (eB - 53);
+    const Edges ed = first_items(
+        pl.w, s0, Mr, [&](int k) { return (uint64_t)T(i, k); },
+        [&](int k) { return (uint64_t)(T(i, k) & 1u); });
+    uint64_t s = s0, Pa = s0, PCa = 0;
+    int a = 0;
+    for (int g = 0; g <= kEdges; ++g) {
+      const int b = ed.x[g];
+      if (b < a) return false;
+      if (b > a) {
+        if (g == 1 || g == 3) {
+          for (int k = a; k < b; ++k) s = rne53_add(s, T(i, k));
+        } else if (!fast_apply(&s, g, ed.P[g] - Pa, ed.PC[g] - PCa)) {
+          return false;
+        }
+      }
+      a = b;
+      Pa = ed.P[g];
+      PCa = ed.PC[g];
+    }
+    *sp = s;
+    return true;
+  }
+
+  // out = {handled, S_cpu, S_exact}
+  void run(uint64_t out[3]) {
+    const int h = pl.h, w = pl.w;
+    R.assign(h, 0);
+    C.assign(h, 0);
+    for (int i = 0; i < h; ++i)
+      for (int j = 0; j < w; ++j) {
+        R[i] += T(i, j);
+        C[i] += T(i, j) & 1u;
+      }
+    const Edges ed = first_items(
+        h, 0, 2ull * (uint64_t)w * (uint64_t)h, [&](int k) { return R[k]; },
+        [&](int k) { return C[k]; });
+    out[0] = 0;
+    out[2] = ed.P[kEdges];
+    if (ed.P[kEdges] >= (1ull << 55)) return;
+    uint64_t s = 0, Pa = 0, PCa = 0;
+    int a = 0;
+    for (int g = 0; g <= kEdges; ++g) {
+      const int b = ed.x[g];
+      if (b < a) return;
+      if (b > a) {
+        if (g == 1 || g == 3) {
+          for (int i = a; i < b; ++i) {
+            if (try_exact(&s, R[i])) continue;
+            if (s >= kTwo53) {
+              const int e = binade(s);
+              if (e <= 54 && try_apply(&s, closed_pair(R[i], C[i], e), e)) continue;
+            }
+            if (!cross_row(&s, i)) return;
+          }
+        } else if (!fast_apply(&s, g, ed.P[g] - Pa, ed.PC[g] - PCa)) {
+          return;
+        }
+      }
+      a = b;
+      Pa = ed.P[g];
+      PCa = ed.PC[g];
+    }
+    out[0] = 1;
+    out[1] = s;
+  }
+};
+
+// The fast PSNR noise: rows' exact sums, the same edges with margin 2 per
+// row, exact rows as integers, rows at an edge by the one-term step, and
+// each stretch inside one binade as the composed pair of its rows (any
+// grouping: composition is associative).  out = {handled, bits of the
+// double in units, exact sum}.
+void fast_noise(const Plane& r, const Plane& d, uint64_t out[3]) {
+  const int h = r.h;
+  std::vector<uint64_t> RN(h, 0);
+  for (int i = 0; i < h; ++i)
+    for (int j = 0; j < r.w; ++j) {
+      const int32_t a = (int32_t)r.x(i, j) - (int32_t)d.x(i, j);
+      RN[i] += fsq_units((uint32_t)(a < 0 ? -a : a));
+    }
+  const Edges ed = first_items(
+      h, 0, 2ull * (uint64_t)h, [&](int k) { return RN[k]; }, [&](int) { return (uint64_t)0; });
+  out[0] = 0;
+  out[2] = ed.P[kEdges];
+  if (ed.P[kEdges] >= (1ull << 55)) return;
+  uint64_t s = 0, Pa = 0;
+  int a = 0;
+  for (int g = 0; g <= kEdges; ++g) {
+    const int b = ed.x[g];
+    if (b < a) return;
+    if (b > a) {
+      const int ep = fast_plan(g);
+      if (ep == kPlanExact) {
+        if (!try_exact(&s, ed.P[g] - Pa)) return;
+      } else if (ep == kPlanCross) {
+        for (int i = a; i < b; ++i) s = rne53_add(s, RN[i]);
+      } else if (ep == 53 || ep == 54) {
+        const int sh = ep - 52;
+        Pair64 acc = pair64_id();
+        for (int i = a; i < b; ++i) acc = then64(acc, noise_row_pair(RN[i], sh), sh);
+        if (!try_apply(&s, acc, ep)) return;
+      } else {
+        return;
+      }
+    }
+    a = b;
+    Pa = ed.P[g];
+  }
+  const double v = (double)s;
+  uint64_t bits;
+  __builtin_memcpy(&bits, &v, 8);
+  out[0] = 1;
+  out[1] = bits;
+}
+
 bool bad(const void* a, int w, int h, ptrdiff_t stride, int bpc) {
   return !a || w <= 0 || h <= 0 || w > 32768 || h > 32768 || stride < w || bpc < 8 || bpc > 16;
 }
@@ -245,6 +404,21 @@ extern "C" int bef_host_noise_units(const void* ref, const void* dis, int w, int
   __builtin_memcpy(&b, &v, 8);
   *bits = b;
   *exact = tot;
+  return 0;
+}
+
+extern "C" int bef_host_fast_units(const void* plane, int w, int h, ptrdiff_t stride, int bpc,
+                                   uint64_t out[3]) {
+  if (bad(plane, w, h, stride, bpc) || !out) return -EINVAL;
+  Fast f{Plane{plane, w, h, stride, bpc}, {}, {}};
+  f.run(out);
+  return 0;
+}
+
+extern "C" int bef_host_fast_noise(const void* ref, const void* dis, int w, int h,
+                                   ptrdiff_t stride, int bpc, uint64_t out[3]) {
+  if (bad(ref, w, h, stride, bpc) || !dis || !out) return -EINVAL;
+  fast_noise(Plane{ref, w, h, stride, bpc}, Plane{dis, w, h, stride, bpc}, out);
   return 0;
 }
 

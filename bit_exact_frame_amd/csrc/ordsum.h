@@ -199,6 +199,80 @@ BEF_HD int plan_of(uint64_t P, uint64_t E, uint64_t M) {
   return binade(hi) == e ? e : kPlanCross;
 }
 
+// Pair of a stretch of terms inside the binade of 2^53 or 2^54 from its
+// exact sum E and its count c of odd terms.  Every float square in units is
+// 0 or 1 modulo 4 (odd exactly when x is odd and below 4096).  In the
+// binade of 2^53 (u = 2) an even term moves S exactly and keeps its
+// parity, and an odd term is a tie: it moves by t - 1 + 2 * (parity before)
+// and leaves the parity even; so the stretch moves by E - c from an even
+// start and by E - c + 2 from an odd one when it holds an odd term.  In the
+// binade of 2^54 (u = 4) an odd term rounds down: E - c from either start.
+BEF_HD Pair64 closed_pair(uint64_t E, uint64_t c, int e) {
+  const uint64_t a0 = E - c;
+#if BEF_MUTANT == 8
+  (void)e;
+  return Pair64{a0, a0};  // mutant: the tie's +2 from an odd start forgotten
+#else
+  return Pair64{a0, (e == 53 && c > 0) ? a0 + 2 : a0};
+#endif
+}
+
+// Pair of one noise row t (any integer) inside binade e (sh = e - 52, u =
+// 2^sh): the double add moves S by t rounded to a multiple of u, ties to
+// the even multiple, which depends on S only through its parity p = (S /
+// u) mod 2.  With v = p * u standing in for S: RNE_u(v + t) - v for p = 0
+// and 1.
+BEF_HD Pair64 noise_row_pair(uint64_t t, int sh) {
+  const uint64_t u = 1ull << sh, half = u >> 1;
+  const uint64_t z0 = t, z1 = u + t;
+#if BEF_MUTANT == 9
+  const uint64_t r0 = (z0 + (half - 1) + (1 - ((z0 >> sh) & 1))) & ~(u - 1);  // mutant: ties to odd
+  const uint64_t r1 = (z1 + (half - 1) + (1 - ((z1 >> sh) & 1))) & ~(u - 1);
+#else
+  const uint64_t r0 = (z0 + (half - 1) + ((z0 >> sh) & 1)) & ~(u - 1);
+  const uint64_t r1 = (z1 + (half - 1) + ((z1 >> sh) & 1)) & ~(u - 1);
+#endif
+  return Pair64{r0, r1 - u};
+}
+
+// The plan as five edges.  With every sum below 2^55 a stretch's plan
+// follows from where its exact interval [P - M, P + E + M] lies against
+// 2^53, 2^54 and 2^55 (P the exact sum before it, E its exact sum, M a bound
+// on how far the CPU's rounded sum can stray from P).  Each edge is the
+// first item at which a non-decreasing quantity reaches a threshold:
+//   x0: P + E > 2^53        (end of the exact items)
+//   x1: P - M >= 2^53       (first item inside the binade of 2^53)
+//   x2: P + E + M >= 2^54   (first item that may leave it)
+//   x3: P - M >= 2^54       (first item inside the binade of 2^54)
+//   x4: P + E + M >= 2^55   (first item that may leave that one)
+// The segments, in order: exact [0, x0), across [x0, x1), 53 [x1, x2),
+// across [x2, x3), 54 [x3, x4), beyond [x4, n).
+constexpr int kEdges = 5;
+
+// Bit j: whether item k (exact prefix pk before it, pk1 after it) has met
+// the condition of edge j.
+BEF_HD unsigned edge_conds(uint64_t pk, uint64_t pk1, uint64_t M) {
+  constexpr uint64_t T53 = 1ull << 53, T54 = 1ull << 54, T55 = 1ull << 55;
+  const uint64_t lo = pk > M ? pk - M : 0;
+  return (unsigned)(pk1 > T53) | (unsigned)(lo >= T53) << 1 | (unsigned)(pk1 + M >= T54) << 2 |
+         (unsigned)(lo >= T54) << 3 | (unsigned)(pk1 + M >= T55) << 4;
+}
+
+// Segment g's plan (0 exact, 1 across, 2 the binade of 2^53, 3 across, 4
+// the binade of 2^54, 5 beyond).
+BEF_HD int fast_plan(int g) {
+  return g == 0 ? kPlanExact : g == 2 ? 53 : g == 4 ? 54 : (g == 5 ? -2 : kPlanCross);
+}
+
+// Applies segment g's exact, closed-form or beyond plan to s (Eg, Cg its
+// exact sum and odd count); false when it does not apply.
+BEF_HD bool fast_apply(uint64_t* s, int g, uint64_t Eg, uint64_t Cg) {
+  const int e = fast_plan(g);
+  if (e == kPlanExact) return try_exact(s, Eg);
+  if (e == 53 || e == 54) return try_apply(s, closed_pair(Eg, Cg, e), e);
+  return false;
+}
+
 // Pair of a run of terms t[0..n) inside binade e: the two trajectories of S
 // modulo 2^32 from an even and from an odd start.
 template <class Terms>

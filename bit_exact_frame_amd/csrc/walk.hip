@@ -274,28 +274,16 @@ __global__ void __launch_bounds__(256) k_pairs(Geometry g, RowArrays ra, unsigne
 // also records the exact prefix of the item sums and of the odd-square
 // counts at every segment start.  A segment planned exact adds its sum; a
 // segment planned in the binade of 2^53 or 2^54 adds its closed-form pair
-// (below), from the two prefix differences alone; other binades compose
+// from the two prefix differences alone; other binades compose
 // their items' pairs with an ordered tree.  A segment that does not fit goes
 // item by item: a row to its runs, a run to its terms.
 //
-// Closed form: every float square in units is 0 or 1 modulo 4 (an odd
-// square is 1 mod 8; an even one is a multiple of 4; squares past 2^24 are
-// rounded to multiples of 2 whose significand is even, or coarser).  In the
-// binade of 2^53 (last place 2) an even term is exact and leaves S/2's
-// parity alone, and an odd term is a tie: from S = 0 mod 4 it goes down by
-// 1, from S = 2 mod 4 up by 1, and leaves S = 0 mod 4.  So a stretch of
-// terms with exact sum E and c odd terms adds E - c from an even start and
-// E - c + 2 from an odd one (E from both when c = 0).  In the binade of 2^54
-// (last place 4) an odd term is 1 mod 4, below half a place: it goes down by
-// 1 whatever the parity, so both starts add E - c.
+// Closed form (closed_pair in the step header): every float square in units
+// is 0 or 1 modulo 4, so in the binades of 2^53 and 2^54 a stretch's pair
+// follows from its exact sum and its count of odd squares.
 
 constexpr int kStage = 4096;  // samples of one row staged in LDS by a fallback
 constexpr int kMaxSeg = 64;   // segments a walk handles as segments
-
-__device__ __forceinline__ Pair64 closed_pair(uint64_t E, uint64_t c, int e) {
-  const uint64_t a0 = E - c;
-  return Pair64{a0, (e == 53 && c > 0) ? a0 + 2 : a0};
-}
 
 struct Seg {
   uint64_t P;   // exact sum of the items before the segment
@@ -586,31 +574,12 @@ struct Walker {
 // The segments, in order, are exact [0, x0), across [x0, x1), 53 [x1, x2),
 // across [x2, x3), 54 [x3, x4), beyond [x4, n); empty ones are skipped.
 
-constexpr int kEdges = 5;
 constexpr int kRowsPer = (kChunk + kT - 1) / kT;  // rows per thread when loading a plane's sums
 
 // ---------------------------------------------------------------------------
-// The fast path: one wave (64 lanes, no block barrier) per plane.
-//
-// With every sum below 2^55 a stretch's plan follows from where its exact
-// interval [P - M, P + E + M] lies against 2^53, 2^54 and 2^55 (P the exact
-// sum before it, E its exact sum, M a bound on how far the CPU's rounded
-// sum can stray from P).  Each edge of a plan is the first item at which a
-// non-decreasing quantity reaches a threshold:
-//   x0: P + E > 2^53        (end of the exact items)
-//   x1: P - M >= 2^53       (first item inside the binade of 2^53)
-//   x2: P + E + M >= 2^54   (first item that may leave it)
-//   x3: P - M >= 2^54       (first item inside the binade of 2^54)
-//   x4: P + E + M >= 2^55   (first item that may leave that one)
-// The segments, in order: exact [0, x0), across [x0, x1), 53 [x1, x2),
-// across [x2, x3), 54 [x3, x4), beyond [x4, n).
-
-__device__ __forceinline__ unsigned edge_conds(uint64_t pk, uint64_t pk1, uint64_t M) {
-  constexpr uint64_t T53 = 1ull << 53, T54 = 1ull << 54, T55 = 1ull << 55;
-  const uint64_t lo = pk > M ? pk - M : 0;
-  return (unsigned)(pk1 > T53) | (unsigned)(lo >= T53) << 1 | (unsigned)(pk1 + M >= T54) << 2 |
-         (unsigned)(lo >= T54) << 3 | (unsigned)(pk1 + M >= T55) << 4;
-}
+// The fast path: one wave (64 lanes, no block barrier) per plane, with the
+// plan as five threshold edges (edge_conds, fast_plan, fast_apply in the
+// step header).
 
 // Edges of n items (uniform over the wave): x[j], the exact prefix P[j]
 // (base included) and odd count PC[j] before each edge; entry kEdges is n
@@ -684,21 +653,6 @@ __device__ __forceinline__ WEdges wave_edges(int n, int c, uint64_t le, uint32_t
     pending &= ~owned;
   }
   return r;
-}
-
-// Segment g of the edges (0 exact, 1 across, 2 the binade of 2^53, 3 across,
-// 4 the binade of 2^54, 5 beyond): its plan.
-__device__ __forceinline__ int fast_plan(int g) {
-  return g == 0 ? kPlanExact : g == 2 ? 53 : g == 4 ? 54 : (g == 5 ? -2 : kPlanCross);
-}
-
-// Applies segment g's exact, closed-form or beyond plan to s (Eg, Cg its
-// exact sum and odd count); returns false when it does not apply.
-__device__ __forceinline__ bool fast_apply(uint64_t* s, int g, uint64_t Eg, uint64_t Cg) {
-  const int e = fast_plan(g);
-  if (e == kPlanExact) return try_exact(s, Eg);
-  if (e == 53 || e == 54) return try_apply(s, closed_pair(Eg, Cg, e), e);
-  return false;
 }
 
 // A crossing row staged in LDS by one wave: samples (zeros from w up to
@@ -885,18 +839,6 @@ __device__ bool wave_walk(uint64_t* out, uint64_t* exact, const uint64_t* lE, co
   }
   *out = s;
   return true;
-}
-
-// Pair of one noise row t inside binade e (sh = e - 52, u = 2^sh): the
-// double add moves S by t rounded to a multiple of u, ties to the even
-// multiple, which depends on S only through its parity p = (S / u) mod 2.
-// With v = p * u standing in for S: RNE_u(v + t) - v for p = 0 and 1.
-__device__ __forceinline__ Pair64 noise_row_pair(uint64_t t, int sh) {
-  const uint64_t u = 1ull << sh, half = u >> 1;
-  const uint64_t z0 = t, z1 = u + t;
-  const uint64_t r0 = (z0 + (half - 1) + ((z0 >> sh) & 1)) & ~(u - 1);
-  const uint64_t r1 = (z1 + (half - 1) + ((z1 >> sh) & 1)) & ~(u - 1);
-  return Pair64{r0, r1 - u};
 }
 
 // The fast PSNR noise by one wave: rows' exact sums in lR (LDS, h <=

@@ -158,6 +158,14 @@ void bef_release(void);
 /* out = {S1, S2_exact, S2_cpu} of one plane, in units. */
 int bef_host_plane_units(const void *plane, int w, int h, ptrdiff_t stride,
                          int bpc, unsigned dbg_flags, uint64_t out[3]);
+/* The fast path's decisions on one plane: out = {1 if the fast path
+ * applies (else 0, and the general walk takes the plane), S_cpu, S_exact}. */
+int bef_host_fast_units(const void *plane, int w, int h, ptrdiff_t stride,
+                        int bpc, uint64_t out[3]);
+/* The fast noise: out = {1 if it applies, bits of the noise double in
+ * units, exact sum}. */
+int bef_host_fast_noise(const void *ref, const void *dis, int w, int h,
+                        ptrdiff_t stride, int bpc, uint64_t out[3]);
 /* *bits = bit pattern of the noise double in units; *exact = exact sum. */
 int bef_host_noise_units(const void *ref, const void *dis, int w, int h,
                          ptrdiff_t stride, int bpc, uint64_t *bits,

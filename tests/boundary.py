@@ -71,6 +71,9 @@ def build(kind: str):
     ``b53``    exact sum 2^53
     ``b53p3``  exact sum 2^53 over the first h-3 rows, then each of the last
                three rows holds one sample of value 1 (a tie each)
+    ``odd53``  exact sum 2^53 - 2 over the first h-1 rows; the last row holds
+               2, 100 and fifty 1s: the sum enters the binade of 2^53 with S/2
+               odd and meets fifty ties there (a stretch from an odd start)
     ``b54p7``  exact sum 2^53, then only even samples (terms divisible by 4,
                so every add is exact in the binades of 2^53 and 2^54) up to
                exactly 2^54, then seven samples of value 1 at the end
@@ -86,6 +89,11 @@ def build(kind: str):
         _fill_to(flat[:body], 0, TWO53, 0, 65536, _rng(3), False)
         for r in (H - 3, H - 2, H - 1):
             plane[r, W // 2] = 1
+    elif kind == "odd53":
+        _fill_to(flat[:(H - 1) * W], 0, TWO53 - 2, 0, 65536, _rng(6), False)
+        plane[H - 1, 0] = 2       # 2^53 - 2 + 4 = 2^53 + 2: S / 2 odd
+        plane[H - 1, 1] = 100     # + 10000 exactly: still odd
+        plane[H - 1, 2:52] = 1    # fifty ties from an odd start
     elif kind == "b54p7":
         pos = _fill_to(flat[:body], 0, TWO53, 32768, 65536, _rng(4), False)
         _fill_to(flat[:body], pos, TWO53, 32768, 65536, _rng(5), True)
@@ -95,4 +103,4 @@ def build(kind: str):
     return plane
 
 
-KINDS = ("b53m1", "b53", "b53p3", "b54p7")
+KINDS = ("b53m1", "b53", "b53p3", "b54p7", "odd53")

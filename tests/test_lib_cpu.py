@@ -192,6 +192,54 @@ def test_host_emulation_terms_only(api):
         assert api.bef_host_plane_units(p, 16, dbg=4 | 2)[2] == oracle_units(name)[1], name
 
 
+@functools.lru_cache(maxsize=None)
+def letterbox_plane():
+    """Exact sum 2^53 + 5000 from bright samples, then rows of zeros."""
+    p = np.zeros((2160, 3840), np.uint16)
+    boundary._fill_to(p.reshape(-1), 0, (1 << 53) + 5000, 40000, 65536,
+                      np.random.Generator(np.random.PCG64(1653)), False)
+    return p
+
+
+def test_fast_emulation_matches_oracle(api):
+    """The fast path's decisions (threshold edges, closed forms, rows and
+    terms at an edge) give the oracle's sum on every plane below 2^55, and
+    hand the planes past 2^55 to the general walk."""
+    cases = list(planes()) + [("letterbox", letterbox_plane())]
+    for name, p in cases:
+        got = api.bef_host_fast_units(p, 16)
+        exact = int(checkers.terms_moment(p).sum(dtype=np.uint64))
+        assert got[2] == exact, name
+        if exact >= 1 << 55:
+            assert got[0] == 0, name
+            continue
+        if name == "letterbox":
+            acc = oracle.Oracle().moment_sums(p, np.zeros_like(p), 16)
+            want = int(math.ldexp(acc[2], 16))
+        else:
+            want = oracle_units(name)[1]
+        assert got[0] == 1 and got[1] == want, (name, got, want)
+
+
+@functools.lru_cache(maxsize=None)
+def noise_pairs():
+    """Frame pairs whose noise rounds: half-range (binade of 2^53) and a
+    high/low pair past 2^54."""
+    r5, d5 = synth.make_frames(5, frames=1)
+    rng = np.random.Generator(np.random.PCG64(5454))
+    hi = rng.integers(48000, 65536, size=(2160, 3840)).astype(np.uint16)
+    lo = rng.integers(0, 16000, size=(2160, 3840)).astype(np.uint16)
+    return [("c5", r5[0], d5[0]), ("past 2^54", hi, lo)]
+
+
+def test_fast_noise_emulation_matches_oracle(api, orc):
+    for name, r, d in noise_pairs():
+        got = api.bef_host_fast_noise(r, d, 16)
+        noise = orc.psnr_sum(r, d, 16)
+        assert got[0] == 1, name
+        assert np.array([got[1]], np.uint64).view(np.float64)[0] == math.ldexp(noise, 16), name
+
+
 def test_host_noise_matches_oracle(api, orc):
     for key in (4, 5):
         r, d = synth.make_frames(key, frames=1)
@@ -249,6 +297,8 @@ MUTANTS = {
     5: "the term-by-term fallback as exact adds",
     6: "no rounding at all",
     7: "a lane's run order reversed",
+    8: "the closed form's +2 from an odd start forgotten",
+    9: "a noise row's ties rounded to odd",
 }
 
 
@@ -273,4 +323,25 @@ def test_header_break_is_caught(tmp_path, mutant):
                 wrong.append((flags, name))
         if wrong:
             break
+    if not wrong:  # the fast path's decisions, then the fast noise
+        lib.bef_host_fast_units.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_ssize_t, ctypes.c_int,
+                                            ctypes.POINTER(ctypes.c_uint64)]
+        lib.bef_host_fast_noise.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                            ctypes.c_int, ctypes.c_ssize_t, ctypes.c_int,
+                                            ctypes.POINTER(ctypes.c_uint64)]
+        for name, p in planes():
+            h, w = p.shape
+            out = (ctypes.c_uint64 * 3)()
+            assert lib.bef_host_fast_units(p.ctypes.data, w, h, w, 16, out) == 0
+            if out[0] == 1 and out[1] != oracle_units(name)[1]:
+                wrong.append(("fast", name))
+        o = oracle.Oracle()
+        for name, r, d in noise_pairs():
+            h, w = r.shape
+            out = (ctypes.c_uint64 * 3)()
+            assert lib.bef_host_fast_noise(r.ctypes.data, d.ctypes.data, w, h, w, 16, out) == 0
+            v = np.array([out[1]], np.uint64).view(np.float64)[0]
+            if out[0] == 1 and v != math.ldexp(o.psnr_sum(r, d, 16), 16):
+                wrong.append(("fast noise", name))
     assert wrong, f"break '{MUTANTS[mutant]}' was not caught"
