@@ -180,6 +180,28 @@ def test_past_2_55_4096x2560(api, orc):
     check_batch(api, orc, ref, dis, 16, label="4096x2560 past 2^55")
 
 
+def test_past_2_53_2560x1440_16bit(api, orc):
+    """A 16-bit 2560x1440 frame past 2^53, the size on which the twins'
+    rounded-once result was measured off (ADR-1497, Context).  High content
+    fills the ref plane to about 2^53.2 units, and one sample in ten is a
+    small codeword whose odd square ties past 2^53 (squares of codewords of
+    2^15.5 and more are multiples of 2^7 and add exactly there); dark dis
+    content puts the noise past 2^53 as well; rows are padded to 2624 samples of
+    0xFFFF that must never be read."""
+    rng = np.random.Generator(np.random.PCG64(2560))
+    ref = np.full((2, 1440, 2624), 0xFFFF, dtype=np.uint16)
+    dis = np.full_like(ref, 0xFFFF)
+    body = rng.integers(46000, 65536, size=(2, 1440, 2560))
+    small = rng.random(size=body.shape) < 0.1  # odd squares: ties past 2^53
+    body[small] = rng.integers(0, 4096, size=int(small.sum()))
+    ref[:, :, :2560] = body
+    dis[:, :, :2560] = rng.integers(0, 8000, size=(2, 1440, 2560))
+    units = api.bef_frames_units(dev(ref), dev(dis), 16, w=2560)
+    assert (units[:, 2] > 1 << 53).all() and (units[:, 4] != units[:, 2]).any()
+    assert (units[:, 6] > 1 << 53).all()
+    check_batch(api, orc, ref, dis, 16, w=2560, label="2560x1440 16-bit past 2^53")
+
+
 def test_wide_rows_past_2_53(api, orc):
     """7680x1100 full-range noise crosses 2^53 in a row wider than the fast
     path stages (the general walk reads such rows from memory)."""
