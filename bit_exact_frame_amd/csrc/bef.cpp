@@ -268,6 +268,16 @@ int prepare(Call& c, const void* ref, const void* dis, int w, int h, ptrdiff_t s
   return 0;
 }
 
+// A caller's stream must belong to the planes' device (NULL: that device's
+// default stream).
+int check_stream(const Call& c, hipStream_t st) {
+  if (!st) return 0;
+  hipDevice_t sd = -1;
+  BEF_HIP(hipStreamGetDevice(st, &sd));
+  if (sd != c.dev) return fail(-EINVAL, "stream of device %d, planes on device %d", (int)sd, c.dev);
+  return 0;
+}
+
 int enqueue(const Call& c, hipStream_t st, double* d_results) {
   const unsigned dbg = g_dbg;
   BEF_HIP(timed(0, [&](hipEvent_t a, hipEvent_t b) { return launch_rows(c.g, c.ra, st, a, b); }));
@@ -292,7 +302,7 @@ int run_sync(const void* ref, const void* dis, int w, int h, ptrdiff_t stride, p
   int rc = prepare(c, ref, dis, w, h, stride, pitch, nframes, bpc);
   if (rc) return rc;
   hipStream_t st = (hipStream_t)stream;
-  if ((rc = enqueue(c, st, c.d_results))) return rc;
+  if ((rc = check_stream(c, st)) || (rc = enqueue(c, st, c.d_results))) return rc;
   double* hres = (double*)g_arena[c.dev].host;
   uint64_t* hun = (uint64_t*)((char*)hres + up256((size_t)nframes * 6 * 8));
   BEF_HIP(hipMemcpyAsync(hres, c.d_results, (size_t)nframes * 6 * 8, hipMemcpyDeviceToHost, st));
@@ -447,7 +457,7 @@ int bef_frames_async(const void* ref, const void* dis, int w, int h, ptrdiff_t s
   DevGuard dg;
   Call c;
   int rc = prepare(c, ref, dis, w, h, stride, frame_pitch, nframes, bpc);
-  if (rc) return rc;
+  if (rc || (rc = check_stream(c, (hipStream_t)stream))) return rc;
   return enqueue(c, (hipStream_t)stream, dev_results);
 }
 
@@ -462,6 +472,7 @@ int bef_read_ceiling(const void* ref, const void* dis, int w, int h, ptrdiff_t s
   if (rc) return rc;
   if (c.g.cb == 0) return fail(-EINVAL, "rows hold no whole 4-byte chunks at this alignment");
   const hipStream_t st = (hipStream_t)stream;
+  if ((rc = check_stream(c, st))) return rc;
   BEF_HIP(timed(4, [&](hipEvent_t a, hipEvent_t b) {
     return launch_read_ceiling(c.g, dev_out, st, a, b);
   }));
@@ -479,13 +490,13 @@ int bef_frames_host(const void* ref, const void* dis, int w, int h, ptrdiff_t st
 
 int moment_frame(const void* ref, const void* dis, int w, int h, ptrdiff_t stride, int bpc,
                  double out[4]) {
-  if (!out) return -EINVAL;
+  if (!out) return fail(-EINVAL, "NULL out");
   return bef_frames(ref, dis, w, h, stride, 0, 1, bpc, nullptr, out, nullptr);
 }
 
 int psnr_noise(const void* ref, const void* dis, int w, int h, ptrdiff_t stride, int bpc,
                double out[2]) {
-  if (!out) return -EINVAL;
+  if (!out) return fail(-EINVAL, "NULL out");
   return bef_frames(ref, dis, w, h, stride, 0, 1, bpc, nullptr, nullptr, out);
 }
 
@@ -516,7 +527,7 @@ int bef_timing_read(int kernel, double* ms, long* launches) {
 void bef_timing_reset(void) {
   std::lock_guard<std::mutex> lk(g_mu);
   ev_collect();
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < 5; ++k) {
     g_ms[k] = 0;
     g_n[k] = 0;
   }
@@ -537,7 +548,7 @@ void bef_release(void) {
   DevGuard dg;
   for (int d = 0; d < kMaxDev; ++d) {
     Arena& a = g_arena[d];
-    if (!a.base && !a.host) continue;
+    if (!a.base && !a.host && !a.pipe && !a.copy_st) continue;
     (void)hipSetDevice(d);
     if (a.base) (void)hipFree(a.base);
     if (a.host) (void)hipHostFree(a.host);

@@ -30,6 +30,7 @@
  *   stride     distance between row starts, in SAMPLES, >= w.  Samples
  *              between w and stride are never read.
  *   bpc        bits per sample, 8..16.
+ *   device     ref and dis must be on one device; the work runs there.
  *   return     0 on success; -EINVAL (-22) for invalid arguments; -ENOMEM
  *              (-12) when scratch memory cannot be allocated; -EIO (-5) for
  *              a HIP runtime error (text in bef_last_error()).  Outputs are
@@ -61,11 +62,12 @@ int moment_frame(const void *ref, const void *dis, int w, int h,
 int psnr_noise(const void *ref, const void *dis, int w, int h,
                ptrdiff_t stride, int bpc, double out[2]);
 
-/* Fused, batched: nframes frames, frame_pitch samples apart (>= h*stride
- * not required; frames may not overlap in a way that matters since they
- * are only read).  Each plane is read once for both reductions.
- * stream: a hipStream_t (NULL = the default stream).  The call enqueues
- * its kernels on that stream and waits once at the end for the results.
+/* Fused, batched: nframes frames, frame_pitch samples apart (frames are
+ * only read, so a pitch below h*stride, i.e. overlapping frames, is
+ * allowed).  Each plane is read once for both reductions.
+ * stream: a hipStream_t of the planes' device (NULL = that device's default
+ * stream; a stream of another device is -EINVAL).  The call enqueues its
+ * kernels on that stream and waits once at the end for the results.
  * moments (HOST, [nframes][4]) and psnr (HOST, [nframes][2]) may each be
  * NULL.  1 <= nframes <= 65535. */
 int bef_frames(const void *ref, const void *dis, int w, int h,

@@ -353,3 +353,48 @@ def test_bad_arguments(api):
     host = np.zeros((4, 4), np.uint16)
     assert lib.moment_frame(host.ctypes.data, host.ctypes.data, 4, 4, 4, 16, out) == -22
     assert api.last_error() != ""
+    assert lib.moment_frame(p, p, 4, 4, 4, 16, None) == -22
+    assert "NULL out" in api.last_error()
+    assert lib.psnr_noise(p, p, 4, 4, 4, 16, None) == -22
+    assert "NULL out" in api.last_error()
+
+
+def test_stream_of_the_planes_device(api, orc):
+    """A caller's stream on the planes' device is accepted, by the sync,
+    async and diagnostic entry points alike."""
+    import torch
+    ref, dis = synth.make_frames(2, frames=2)
+    r, d = dev(ref), dev(dis)
+    s = torch.cuda.Stream()
+    mom, ps = api.bef_frames(r, d, 10, w=synth.WORKLOADS[2].w, stream=s)
+    emom, eps = expect(orc, ref, dis, 10, synth.WORKLOADS[2].w)
+    assert (bits(mom) == bits(emom)).all() and (bits(ps) == bits(eps)).all()
+    out = torch.zeros((2, 6), dtype=torch.float64, device="cuda")
+    api.bef_frames_async(r, d, 10, out, w=synth.WORKLOADS[2].w, stream=s)
+    s.synchronize()
+    got = out.cpu().numpy()
+    assert (bits(got[:, :4]) == bits(emom)).all() and (bits(got[:, 4:]) == bits(eps)).all()
+
+
+def test_timing_counters(api):
+    """Per-kernel timing counts each timed launch once, and a reset clears
+    every counter, the read-ceiling one included."""
+    import torch
+    ref, dis = synth.make_frames(4, frames=2)
+    r, d = dev(ref), dev(dis)
+    cout = torch.zeros(2 * ref.shape[1], dtype=torch.int32, device="cuda")
+    api.bef_timing_enable(True)
+    try:
+        api.bef_timing_reset()
+        for _ in range(3):
+            api.bef_frames(r, d, 16)
+            api.bef_read_ceiling(r, d, cout)
+        torch.cuda.synchronize()
+        counts = {k: api.bef_timing_read(k) for k in ("rows", "walk", "ceiling")}
+        assert all(n == 3 and ms > 0 for ms, n in counts.values()), counts
+        api.bef_timing_reset()
+        assert all(api.bef_timing_read(k) == (0.0, 0) for k in api.KERNELS), \
+            {k: api.bef_timing_read(k) for k in api.KERNELS}
+    finally:
+        api.bef_timing_enable(False)
+        api.bef_timing_reset()
