@@ -79,7 +79,12 @@ int bef_frames(const void *ref, const void *dis, int w, int h,
  * noise, mse), caller-owned, written when the stream reaches that point.
  * The call returns after enqueueing; it does not synchronise.  Calls share
  * the library's per-device scratch: two calls whose GPU work overlaps (on
- * different streams) race; enqueue them on one stream. */
+ * different streams) race; enqueue them on one stream.
+ * Graph capture: once a call of the same or a larger shape has grown the
+ * scratch, the call enqueues kernel launches only (no allocation, memset
+ * or synchronisation), so it may be captured into a HIP graph; a replay
+ * reads whatever frames the captured buffers hold at that time.  A call
+ * that must grow the scratch allocates and fails under capture. */
 int bef_frames_async(const void *ref, const void *dis, int w, int h,
                      ptrdiff_t stride, ptrdiff_t frame_pitch, int nframes,
                      int bpc, void *stream, double *dev_results);

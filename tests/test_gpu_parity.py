@@ -269,6 +269,38 @@ def test_async_matches_sync(api, orc):
     assert (bits(got[:, :4]) == bits(mom)).all() and (bits(got[:, 4:]) == bits(ps)).all()
 
 
+def test_graph_capture_replays(api, orc):
+    """bef_frames_async only enqueues kernels once its scratch has grown (no
+    allocation, memset or sync), so a caller can capture it in a HIP graph.
+    Each replay reads whatever frames the buffers then hold: two frame sets
+    alternate, with eager copies and syncs between replays, and every replay
+    is checked against the oracle."""
+    import torch
+    r5, d5 = synth.make_frames(5, frames=2)
+    r4, d4 = synth.make_frames(4, frames=2)
+    want = {k: expect(orc, r, d, 16, None) for k, (r, d) in {5: (r5, d5), 4: (r4, d4)}.items()}
+    R, D = dev(r5), dev(d5)
+    out = torch.zeros((2, 6), dtype=torch.float64, device="cuda")
+    api.bef_frames_async(R, D, 16, out)  # grows the scratch outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        api.bef_frames_async(R, D, 16, out)
+    torch.cuda.synchronize()
+    for n, key in enumerate([4, 5, 4, 5, 5]):
+        r, d = (r4, d4) if key == 4 else (r5, d5)
+        R.copy_(torch.from_numpy(r))
+        D.copy_(torch.from_numpy(d))
+        out.fill_(-1.0)
+        torch.cuda.synchronize()
+        say(f"[gpu] graph replay {n} frames of workload {key}")
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        emom, eps = want[key]
+        assert (bits(got[:, :4]) == bits(emom)).all() and (bits(got[:, 4:]) == bits(eps)).all(), n
+
+
 def test_deterministic(api):
     ref, dis = synth.make_frames(4, frames=2)
     r, d = dev(ref), dev(dis)
