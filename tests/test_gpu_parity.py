@@ -132,6 +132,27 @@ def test_shapes(api, orc, w, h, stride, bpc, frames):
     check_batch(api, orc, ref, dis, bpc, w=w, label=f"shape {w}x{h}/{stride}")
 
 
+@pytest.mark.parametrize("bpc", [8, 16])
+def test_most_frames(api, orc, bpc):
+    """The largest batch, 65535 frames (tiny ones: 3x2, rows not aligned),
+    every frame against the oracle."""
+    ref, dis = synth.uniform_planes(65535 + bpc, 65535, 2, 3, 3, bpc)
+    check_batch(api, orc, ref, dis, bpc, w=3, label=f"65535 frames bpc {bpc}")
+
+
+def test_tallest_plane_past_2_53(api, orc):
+    """The tallest plane, h = 32768 (w = 128), with high content so that
+    the second-moment sums pass 2^53 late in the plane."""
+    rng = np.random.Generator(np.random.PCG64(32768))
+    ref = rng.integers(56000, 65536, size=(1, 32768, 128)).astype(np.uint16)
+    small = rng.random(size=ref.shape) < 0.05
+    ref[small] = rng.integers(0, 4096, size=int(small.sum())).astype(np.uint16)
+    dis = rng.integers(0, 65536, size=ref.shape).astype(np.uint16)
+    units = api.bef_frames_units(dev(ref), dev(dis), 16)
+    assert (units[:, 2] > 1 << 53).all() and (units[:, 4] != units[:, 2]).all()
+    check_batch(api, orc, ref, dis, 16, label="128x32768")
+
+
 def test_single_frame_entry_points(api, orc):
     wl = synth.WORKLOADS[3]
     ref, dis = synth.make_frames(3, frames=1)
