@@ -8,12 +8,14 @@ frames already resident in HBM.  Batches rotate through a ring of device
 copies larger than the 256 MB Infinity Cache, so every step reads its
 frames from HBM.  Prints ONE JSON line.
 
-value          frames per second over the timed steps (torch events on the
-               launch stream, bracketed by synchronisations)
+value          frames per second over the K timed steps that follow the W
+               warmup steps (torch events on the launch stream, bracketed by
+               synchronisations; no per-kernel events inside)
 roofline       the row-sum kernel (the dominant one): algorithmic bytes per
                launch (2 planes x w x h x 2 B x frames) over its average
-               duration, measured with HIP events the library records on the
-               launch stream; peak = MI355X HBM3E 8 TB/s
+               duration, measured over a second pass of K steps with HIP
+               events that each dispatch records on the launch stream;
+               peak = MI355X HBM3E 8 TB/s
 cpu_baseline   the CPU oracle (plain loops), timed on this host's cores, one
                frame per thread, on a bounded sample of the same frames
 """
@@ -102,7 +104,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", type=int, default=4)
     ap.add_argument("--ring", type=int, default=0, help="device copies of the batch (0 = auto)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
@@ -151,33 +153,38 @@ def main():
     api.bef_debug_set(0)
     mom, ps = api.bef_frames(refs[0], diss[0], wl.bpc, w=wl.w)
 
-    for k in range(args.warmup):
-        api.bef_frames_async(refs[k % ring], diss[k % ring], wl.bpc, out, w=wl.w, stream=stream)
+    def steps(n):
+        for k in range(n):
+            api.bef_frames_async(refs[k % ring], diss[k % ring], wl.bpc, out, w=wl.w,
+                                 stream=stream)
+
+    # The GPU's clocks take about 20 ms of sustained load to settle (the row
+    # kernel runs up to 25% slower before that); the default warmup covers
+    # about 27 ms of steps.
+    steps(args.warmup)
     torch.cuda.synchronize()
 
-    api.bef_timing_enable(True)
-    api.bef_timing_reset()
+    # value: K steps with no per-kernel events
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     ev0.record(stream)
-    for k in range(args.steps):
-        api.bef_frames_async(refs[k % ring], diss[k % ring], wl.bpc, out, w=wl.w, stream=stream)
+    steps(args.steps)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    clean_ms = ev0.elapsed_time(ev1)
+
+    # roofline: the same K steps again, each kernel timed by HIP events that
+    # its own dispatch records on the launch stream
+    api.bef_timing_enable(True)
+    api.bef_timing_reset()
+    ev0.record(stream)
+    steps(args.steps)
     ev1.record(stream)
     torch.cuda.synchronize()
     api.bef_timing_enable(False)
     total_ms = ev0.elapsed_time(ev1)
     rows_ms, rows_n = api.bef_timing_read("rows")
     walk_ms, walk_n = api.bef_timing_read("walk")
-
-    # the same steps untimed by the library (no per-kernel events)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for k in range(args.steps):
-        api.bef_frames_async(refs[k % ring], diss[k % ring], wl.bpc, out, w=wl.w, stream=stream)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    clean_ms = ev0.elapsed_time(ev1)
 
     # context, outside the timed steps: the row pass's access pattern read
     # with no arithmetic (the practical ceiling of its memory side)
