@@ -104,7 +104,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", type=int, default=4)
     ap.add_argument("--ring", type=int, default=0, help="device copies of the batch (0 = auto)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
@@ -158,9 +158,9 @@ def main():
             api.bef_frames_async(refs[k % ring], diss[k % ring], wl.bpc, out, w=wl.w,
                                  stream=stream)
 
-    # The GPU's clocks take about 20 ms of sustained load to settle (the row
-    # kernel runs up to 25% slower before that); the default warmup covers
-    # about 27 ms of steps.
+    # The GPU's clocks take about 20-25 ms of sustained load to settle (the
+    # row kernel runs up to 25% slower before that); the default warmup
+    # covers about 45 ms of steps.
     steps(args.warmup)
     torch.cuda.synchronize()
 
