@@ -13,6 +13,7 @@ import pytest
 
 import boundary
 import oracle
+import random_frames
 from bit_exact_frame_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -221,6 +222,14 @@ def test_past_2_53_2560x1440_16bit(api, orc):
     assert (units[:, 2] > 1 << 53).all() and (units[:, 4] != units[:, 2]).any()
     assert (units[:, 6] > 1 << 53).all()
     check_batch(api, orc, ref, dis, 16, w=2560, label="2560x1440 16-bit past 2^53")
+
+
+@pytest.mark.parametrize("k", range(random_frames.N_CASES))
+def test_random_crossings(api, orc, k):
+    """Seeded random planes whose sum crosses 2^53 or 2^54 at a random row
+    and column, with random width, padding, bit depth, tail and dis."""
+    ref, dis, w, bpc, label = random_frames.case(k)
+    check_batch(api, orc, ref[None], dis[None], bpc, w=w, label=label)
 
 
 def test_wide_rows_past_2_53(api, orc):

@@ -22,6 +22,7 @@ import pytest
 import boundary
 import checkers
 import oracle
+import random_frames
 from bit_exact_frame_amd import synth
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -219,6 +220,25 @@ def test_fast_emulation_matches_oracle(api):
         else:
             want = oracle_units(name)[1]
         assert got[0] == 1 and got[1] == want, (name, got, want)
+
+
+@pytest.mark.parametrize("k", range(random_frames.N_CASES))
+def test_emulation_random_crossings(api, orc, k):
+    """The general walk and the fast path's decisions, emulated on the host,
+    give the oracle's sums on seeded random planes that cross 2^53 or 2^54
+    at a random row and column; the fast noise too."""
+    ref, dis, w, bpc, label = random_frames.case(k)
+    acc = orc.moment_sums(ref, dis, bpc, w=w)
+    want = int(math.ldexp(acc[2], 2 * (bpc - 8)))
+    exact = int(checkers.terms_moment(ref[:, :w]).sum(dtype=np.uint64))
+    got = api.bef_host_plane_units(ref, bpc, w=w)
+    assert got[1] == exact and got[2] == want, (label, got, want)
+    fast = api.bef_host_fast_units(ref, bpc, w=w)
+    assert fast[0] == 1 and fast[1] == want and fast[2] == exact, (label, fast, want)
+    fn = api.bef_host_fast_noise(ref, dis, bpc, w=w)
+    noise = orc.psnr_sum(ref, dis, bpc, w=w)
+    assert fn[0] == 1, label
+    assert np.array([fn[1]], np.uint64).view(np.float64)[0] == math.ldexp(noise, 2 * (bpc - 8)), label
 
 
 @functools.lru_cache(maxsize=None)
