@@ -34,7 +34,7 @@ def case(k: int):
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([0xBEF, 4242, k])))
     w = int(rng.integers(512, 6001))
     stride = w + int(rng.choice([0, 0, 7, 8, 64]))
-    bpc = int(rng.choice([12, 14, 16]))
+    bpc = int(rng.integers(9, 17))
     edge = TWO54 if k % 4 == 3 else TWO53
     target = edge + int(rng.integers(-(1 << 31), 1 << 31))
     lo = int(rng.choice([30000, 45000]))
