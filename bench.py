@@ -95,9 +95,17 @@ def cpu_baseline(ref, dis, bpc, w, budget_s=20.0, max_threads=16):
     with cf.ThreadPoolExecutor(max_workers=threads) as ex:
         list(ex.map(work, idx))
     dt = time.perf_counter() - t0
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")),
+                         None)
+    except OSError:
+        pass
     return {"value": n / dt, "unit": "frames/s", "cores": threads, "kind": "oracle",
             "sample": f"{n} frames of the batch ({frames} distinct), one frame per thread, "
-                      f"{threads} threads, {dt:.1f} s wall; one frame alone took {one * 1e3:.1f} ms"}
+                      f"{threads} threads, {dt:.1f} s wall; one frame alone took {one * 1e3:.1f} ms",
+            "one_thread_value": round(1.0 / one, 2), "cpu_model": model}
 
 
 def main():
