@@ -372,7 +372,10 @@ int run_host(const void* ref, const void* dis, int w, int h, ptrdiff_t stride, p
   if (rc) return rc;
   BEF_HIP(hipSetDevice(dev));
   const size_t B = bpc == 8 ? 1 : 2;
-  const size_t fbytes = (size_t)h * (size_t)stride * B;  // one plane of one frame
+  const size_t fbytes = (size_t)h * (size_t)stride * B;  // one plane of one frame in a slot
+  // what a frame's samples span in the caller's memory: up to sample w - 1
+  // of row h - 1 (the padding after it is not read)
+  const size_t span = ((size_t)(h - 1) * (size_t)stride + (size_t)w) * B;
   const int K = (int)std::max<size_t>(1, std::min<size_t>((size_t)nframes, kPipeChunkBytes / fbytes));
   const size_t slot = up256((size_t)K * fbytes);
   if ((rc = pipe_setup(dev, slot, (size_t)nframes * 6 * 8))) return rc;
@@ -389,11 +392,12 @@ int run_host(const void* ref, const void* dis, int w, int h, ptrdiff_t stride, p
       const char* src = (const char*)(pl == 0 ? ref : dis) + (size_t)k0 * (size_t)pitch * B;
       char* dst = pl == 0 ? dref : ddis;
       if (contiguous) {
-        BEF_HIP(hipMemcpyAsync(dst, src, (size_t)kn * fbytes, hipMemcpyHostToDevice, a.copy_st));
+        BEF_HIP(hipMemcpyAsync(dst, src, (size_t)(kn - 1) * fbytes + span, hipMemcpyHostToDevice,
+                               a.copy_st));
       } else {
         for (int f = 0; f < kn; ++f)
           BEF_HIP(hipMemcpyAsync(dst + (size_t)f * fbytes, src + (size_t)f * (size_t)pitch * B,
-                                 fbytes, hipMemcpyHostToDevice, a.copy_st));
+                                 span, hipMemcpyHostToDevice, a.copy_st));
       }
     }
     BEF_HIP(hipEventRecord(a.copied[sl], a.copy_st));

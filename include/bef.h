@@ -96,8 +96,10 @@ int bef_frames_async(const void *ref, const void *dis, int w, int h,
  * the reductions of the previous chunk (on a library compute stream).
  * Pinned host memory (hipHostMalloc, torch pin_memory) lets the uploads run
  * at the link's rate; pageable memory is staged by the HIP runtime.  The
- * slots are kept until bef_release().  moments / psnr: HOST, as in
- * bef_frames (either may be NULL). */
+ * slots are kept until bef_release().  Each frame is read from its first
+ * sample up to sample w - 1 of row h - 1: the padding after the last row is
+ * neither read nor required.  moments / psnr: HOST, as in bef_frames
+ * (either may be NULL). */
 int bef_frames_host(const void *ref, const void *dis, int w, int h,
                     ptrdiff_t stride, ptrdiff_t frame_pitch, int nframes,
                     int bpc, int device, double *moments, double *psnr);
