@@ -167,10 +167,17 @@ def main():
                                  stream=stream)
 
     # The GPU's clocks take about 20-25 ms of sustained load to settle (the
-    # row kernel runs up to 25% slower before that); the default warmup
-    # covers about 45 ms of steps.
+    # row kernel runs up to 25% slower before that).  After the W warmup
+    # steps, untimed steps continue until the warmup has lasted 50 ms (the
+    # default W alone covers about 45 ms); their count is reported.
+    t_warm = time.perf_counter()
     steps(args.warmup)
     torch.cuda.synchronize()
+    settle_steps = 0
+    while time.perf_counter() - t_warm < 0.05:
+        steps(20)
+        torch.cuda.synchronize()
+        settle_steps += 20
 
     # value: K steps with no per-kernel events
     ev0 = torch.cuda.Event(enable_timing=True)
@@ -253,7 +260,8 @@ def main():
                    "read_ceiling_GBps": None if ceiling is None else round(ceiling, 1),
                    "host_pipeline_fps_pcie_inclusive": None if host_fps is None else round(host_fps, 1),
                    "rows_over_read_ceiling": None if ceiling is None else round(achieved / ceiling, 4),
-                   "timed_with_events_ms_per_step": round(total_ms / args.steps, 5)},
+                   "timed_with_events_ms_per_step": round(total_ms / args.steps, 5),
+                   "settle_steps_after_warmup": settle_steps},
         "roofline": {"bound": "hbm", "kernel": "k_rows16", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
