@@ -182,11 +182,14 @@ hipError_t timed(int kernel, F launch) {
   return e;
 }
 
-// Load shape of the 16-bit row kernel: bytes per load (16, 8 or 4, as the
-// row starts allow) and load slots per lane per group (15, 8, 5 or 4).  A
-// wave spreads a row's whole chunks over its 64 lanes in groups of 64 * ng;
-// the shape that leaves the fewest idle bytes in the last group wins, then
-// the one with wider loads, then the larger group (more loads in flight).
+// Load shape of the 16-bit row kernel: bytes per load and load slots per
+// lane per group.  Measured at rows of 1920, 2560 and 3840 samples, 8-byte
+// loads beat 16- and 4-byte ones at every width, so the width is 8 bytes
+// whenever the plane starts, the row pitch and the frame pitch allow it,
+// else 4.  A wave spreads a row's whole chunks over its 64 lanes in groups
+// of 64 * ng: the group size that leaves the fewest idle slots in the
+// last group wins (an idle slot still costs its arithmetic, on zeros), then
+// the larger group (more loads in flight, fewer rounds).
 void load_shape(const void* ref, const void* dis, int w, ptrdiff_t stride, ptrdiff_t pitch,
                 int nframes, int* cb_out, int* ng_out) {
   uint64_t al = 16;
@@ -197,20 +200,20 @@ void load_shape(const void* ref, const void* dis, int w, ptrdiff_t stride, ptrdi
   limit((uintptr_t)dis);
   limit((uint64_t)stride * 2);
   if (nframes > 1) limit((uint64_t)pitch * 2);
-  int best_cb = 0, best_ng = 1;
-  uint64_t best_idle = ~0ull;
-  for (int cb = 16; cb >= 4; cb >>= 1) {
-    if ((uint64_t)cb > al) continue;
+  int cb = 0;
+  for (int c : {8, 4})
+    if (!cb && (uint64_t)c <= al && (uint64_t)w * 2 / c > 0) cb = c;
+  int best_ng = 1;
+  if (cb) {
     const uint64_t nc = (uint64_t)w * 2 / cb;
-    if (nc == 0) continue;
     const uint64_t nper = (nc + 63) / 64;
+    uint64_t best_idle = ~0ull;
     for (int ng : {15, 8, 5, 4}) {
-      if (ng == 15 && cb == 16) continue;  // (60 registers of loads: too many)
-      const uint64_t idle = (((nper + ng - 1) / ng) * ng * 64 - nc) * cb;
-      if (idle < best_idle) best_cb = cb, best_ng = ng, best_idle = idle;
+      const uint64_t idle = ((nper + ng - 1) / ng) * ng * 64 - nc;
+      if (idle < best_idle) best_ng = ng, best_idle = idle;
     }
   }
-  *cb_out = best_cb;
+  *cb_out = cb;
   *ng_out = best_ng;
 }
 

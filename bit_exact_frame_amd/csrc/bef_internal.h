@@ -19,8 +19,8 @@ struct Geometry {
   int nframes;
   int bpc;
   int vec;       // rows start on 16-byte boundaries (8-bit kernel)
-  int cb;        // 16-bit kernel: bytes per load (16, 8, 4; 0 = sample by sample)
-  int ng;        // 16-bit kernel: load slots per lane per group (4, 5, 8)
+  int cb;        // 16-bit kernel: bytes per load (8, 4; 0 = sample by sample)
+  int ng;        // 16-bit kernel: load slots per lane per group (4, 5, 8, 15)
   int need_odd;  // count odd squares per row (frames that can pass 2^53)
   int may_round; // some frame can pass 2^53 units (or forced)
 };

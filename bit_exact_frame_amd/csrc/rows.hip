@@ -1,7 +1,8 @@
 // rows.hip -- the streaming pass: per-row exact integer sums.
 //
 // k_rows16 / k_rows8: one wave per (row, frame).  The wave reads the row of
-// both planes once (16-byte nontemporal loads when rows are aligned), forms
+// both planes once (8-byte nontemporal loads when the rows allow them, else
+// 4-byte ones), forms
 // every term in registers and writes, per row: the sum of codewords of each
 // plane, the exact sum of float squares of each plane (units of 1/s^2), the
 // exact noise sum (float squares of ref - dis) and the number of odd float
@@ -80,14 +81,9 @@ __device__ __forceinline__ void take_sample16(uint32_t a, uint32_t b, Acc16& q) 
   }
 }
 
-// Loads of CB bytes (16, 8 or 4): 16 dwords per plane per lane per group.
+// Loads of CB bytes (8 or 4), NG of them per plane per lane per group.
 template <int CB>
 struct Chunk;
-template <>
-struct Chunk<16> {
-  typedef v4u T;
-  static __device__ __forceinline__ uint32_t dw(const T& v, int k) { return v[k]; }
-};
 template <>
 struct Chunk<8> {
   typedef uint32_t T __attribute__((ext_vector_type(2)));
@@ -103,9 +99,8 @@ template <bool ODD, int CB, int NG>
 __device__ __forceinline__ void rows16_body(const Geometry& g, const RowArrays& ra, int i, int f,
                                             int lane);
 
-// CB bytes per load (16, 8, 4; 0 = sample by sample, for rows not aligned
-// to 4 bytes), NG load slots per lane per group (4, 5, 8; 15 for 8- and
-// 4-byte loads).
+// CB bytes per load (8 or 4; 0 = sample by sample, for rows not aligned to
+// 4 bytes), NG load slots per lane per group (4, 5, 8 or 15).
 template <bool ODD, int CB, int NG>
 __global__ void __launch_bounds__(256) k_rows16(Geometry g, RowArrays ra) {
   const int lane = threadIdx.x & 63;
@@ -288,9 +283,6 @@ hipError_t launch_rows(const Geometry& g, const RowArrays& ra, hipStream_t st, h
     hipExtLaunchKernelGGL((k_rows16<false, CB, NG>), grid16, dim3(256), 0, st, ev0, ev1,      \
                           0, g, ra)
     switch (g.cb * 16 + g.ng) {
-      case 16 * 16 + 4: BEF_ROWS16(16, 4); break;
-      case 16 * 16 + 5: BEF_ROWS16(16, 5); break;
-      case 16 * 16 + 8: BEF_ROWS16(16, 8); break;
       case 8 * 16 + 4: BEF_ROWS16(8, 4); break;
       case 8 * 16 + 5: BEF_ROWS16(8, 5); break;
       case 8 * 16 + 8: BEF_ROWS16(8, 8); break;
@@ -312,9 +304,6 @@ hipError_t launch_read_ceiling(const Geometry& g, uint32_t* out, hipStream_t st,
 #define BEF_CEIL(CB, NG)                                                                       \
   hipExtLaunchKernelGGL((k_read_ceiling<CB, NG>), grid, dim3(256), 0, st, ev0, ev1, 0, g, out)
   switch (g.cb * 16 + g.ng) {
-    case 16 * 16 + 4: BEF_CEIL(16, 4); break;
-    case 16 * 16 + 5: BEF_CEIL(16, 5); break;
-    case 16 * 16 + 8: BEF_CEIL(16, 8); break;
     case 8 * 16 + 4: BEF_CEIL(8, 4); break;
     case 8 * 16 + 5: BEF_CEIL(8, 5); break;
     case 8 * 16 + 8: BEF_CEIL(8, 8); break;

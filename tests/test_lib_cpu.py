@@ -272,16 +272,16 @@ def test_host_noise_matches_oracle(api, orc):
 # ------------------------------------------------------ row kernel shape --
 
 # (bytes per load, slots per group) the row kernel's launcher instantiates
-LAUNCHED = {(16, 4), (16, 5), (16, 8), (8, 4), (8, 5), (8, 8), (8, 15), (4, 4), (4, 5),
-            (4, 8), (4, 15), (0, 1)}
+LAUNCHED = {(8, 4), (8, 5), (8, 8), (8, 15), (4, 4), (4, 5), (4, 8), (4, 15), (0, 1)}
 
 
 def test_load_shape_choice(api):
-    """For many widths and alignments the host picks a load width that the
-    rows allow, a shape the launcher has a kernel for, and no more idle lane
-    slots than any allowed shape would leave."""
+    """For many widths and alignments the host picks 8-byte loads whenever
+    the rows allow them (else 4-byte ones), a shape the launcher has a kernel
+    for, the fewest idle lane slots for that width, and on a tie the larger
+    group."""
     rng = np.random.Generator(np.random.PCG64(44))
-    widths = [1, 3, 4, 7, 8, 64, 100, 176, 511, 512, 520, 1000, 1280, 1920, 2560, 3840,
+    widths = [1, 2, 3, 4, 7, 8, 64, 100, 176, 511, 512, 520, 1000, 1280, 1920, 2560, 3840,
               4096, 4100, 7680, 32768] + [int(x) for x in rng.integers(1, 32769, size=60)]
     for w in widths:
         for base_align in (2, 4, 8, 16, 256):
@@ -294,15 +294,15 @@ def test_load_shape_choice(api):
                 for v in (ref, ref + 0x4000000, stride * 2, stride * 18):
                     while align > 1 and v % align:
                         align //= 2
+                want_cb = next((c for c in (8, 4) if c <= align and w * 2 // c > 0), 0)
+                assert cb == want_cb, (w, align, cb, want_cb)
                 if cb:
-                    assert cb <= align and cb in (4, 8, 16), (w, cb, align)
                     nc = w * 2 // cb
                     nper = -(-nc // 64)
-                    idle = (-(-nper // ng) * ng * 64 - nc) * cb
-                    best = min(((-(-(-(-(w * 2 // c) // 64)) // g) * g * 64 - w * 2 // c) * c)
-                               for c in (16, 8, 4) if c <= align and w * 2 // c > 0
-                               for g in (15, 8, 5, 4) if not (g == 15 and c == 16))
-                    assert idle == best, (w, align, cb, ng, idle, best)
+                    idles = {g: -(-nper // g) * g * 64 - nc for g in (15, 8, 5, 4)}
+                    best = min(idles.values())
+                    assert idles[ng] == best and ng == max(g for g in idles if idles[g] == best), \
+                        (w, align, cb, ng, idles)
                 else:
                     assert align < 4 or w * 2 < 4, (w, align)
 
