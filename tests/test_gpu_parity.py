@@ -154,6 +154,22 @@ def test_tallest_plane_past_2_53(api, orc):
     check_batch(api, orc, ref, dis, 16, label="128x32768")
 
 
+CONSTANTS = [(0, 0), (65535, 0), (0, 65535), (65535, 65535), (1, 0), (4095, 4094)]
+
+
+def test_constant_frames(api, orc):
+    """Degenerate 16-bit 3840x2160 frames of one value per plane: zeros,
+    the top codeword (every term 0xFFFE0000; the sum crosses 2^53 and 2^54
+    with no rounding, since every term is a multiple of 2^17), ones, and
+    the largest odd exact square against its neighbour."""
+    ref = np.stack([np.full((2160, 3840), r, np.uint16) for r, _ in CONSTANTS])
+    dis = np.stack([np.full((2160, 3840), d, np.uint16) for _, d in CONSTANTS])
+    check_batch(api, orc, ref, dis, 16, label="constant frames")
+    u = api.bef_frames_units(dev(ref), dev(dis), 16)
+    assert int(u[1, 2]) == 3840 * 2160 * 0xFFFE0000 == int(u[1, 4])
+    assert int(u[0, 2]) == 0 and int(u[0, 7]) == 0
+
+
 def test_single_frame_entry_points(api, orc):
     wl = synth.WORKLOADS[3]
     ref, dis = synth.make_frames(3, frames=1)
