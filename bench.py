@@ -200,6 +200,12 @@ def main():
     total_ms = ev0.elapsed_time(ev1)
     rows_ms, rows_n = api.bef_timing_read("rows")
     walk_ms, walk_n = api.bef_timing_read("walk")
+    # the plan and pair kernels run only where a plane can pass 2^55
+    extra_us = {}
+    for name in ("plan", "pairs"):
+        ms, n = api.bef_timing_read(name)
+        if n:
+            extra_us[f"{name}_avg_us"] = round(1e3 * ms / n, 2)
 
     # context, outside the timed steps: the row pass's access pattern read
     # with no arithmetic (the practical ceiling of its memory side)
@@ -257,6 +263,7 @@ def main():
                    "whole_path_frac": round(batch_bytes * args.steps / (clean_ms / 1e3) / 1e9
                                             / PEAK_HBM_GBS, 4),
                    "walk_avg_us": round(1e3 * walk_ms / max(walk_n, 1), 2),
+                   **extra_us,
                    "read_ceiling_GBps": None if ceiling is None else round(ceiling, 1),
                    "host_pipeline_fps_pcie_inclusive": None if host_fps is None else round(host_fps, 1),
                    "rows_over_read_ceiling": None if ceiling is None else round(achieved / ceiling, 4),

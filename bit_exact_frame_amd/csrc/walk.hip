@@ -228,15 +228,40 @@ __global__ void __launch_bounds__(kT) k_plan(Geometry g, RowArrays ra, unsigned 
 }
 
 // ---------------------------------------------------------------------------
-// k_pairs: the pair of a row under its planned binade, from 64 lane runs of
-// ceil(w/64) consecutive terms joined by an ordered shuffle-down tree.
+// k_pairs: the pair of a row under its planned binade.  One wave per row:
+// the row is staged in LDS a segment at a time with coalesced loads, each
+// lane forms the pair of its run of consecutive terms from LDS, an ordered
+// shuffle-down tree joins the 64 runs, and the segments' pairs are joined
+// in row order.
 
 __device__ __forceinline__ bool needs_pair(int e, unsigned dbg) {
   return e >= 55 || (e >= 53 && (dbg & BEF_DBG_NO_CLOSED_FORM));
 }
 
+constexpr int kPairSeg = 4096;  // samples of a row staged per wave at a time
+
+// Samples [s0, s0 + n) of a row into buf (n <= kPairSeg) by one wave: every
+// load is issued before the first store.
+template <typename T>
+__device__ __forceinline__ void wave_stage_segment(uint16_t* buf, const T* row, int s0, int n) {
+  const int lane = threadIdx.x & 63;
+  constexpr int U = kPairSeg / 64;
+  uint32_t v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int j = u * 64 + lane;
+    v[u] = j < n ? (uint32_t)row[s0 + j] : 0u;
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int j = u * 64 + lane;
+    if (j < n) buf[j] = (uint16_t)v[u];
+  }
+}
+
 template <typename T>
 __global__ void __launch_bounds__(256) k_pairs(Geometry g, RowArrays ra, unsigned dbg) {
+  __shared__ uint16_t seg[4][kPairSeg];
   const int lane = threadIdx.x & 63;
   const long task = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
   const long per = 2L * g.nframes;
@@ -246,20 +271,29 @@ __global__ void __launch_bounds__(256) k_pairs(Geometry g, RowArrays ra, unsigne
   const int pl = rem / g.nframes, f = rem % g.nframes;
   const long k = (long)(pl * g.nframes + f) * g.h + i;
   const int e = ra.plan[k];
-  if (!needs_pair(e, dbg)) return;
+  if (!needs_pair(e, dbg)) return;  // the whole wave: one task per wave
   const int sh = e - 52;
   const T* row = (const T*)(pl == 0 ? g.ref : g.dis) + (long)f * g.pitch + (long)i * g.stride;
-  const int L = (g.w + 63) >> 6;
-  const int j0 = min(lane * L, g.w), j1 = min(j0 + L, g.w);
-  Pair32 p = run_pair([&](int j) { return fsq_units(row[j0 + j]); }, j1 - j0, sh);
-  for (int off = 1; off < 64; off <<= 1) {
-    Pair32 o;
-    o.a0 = __shfl_down(p.a0, off);
-    o.a1 = __shfl_down(p.a1, off);
-    if ((lane & (2 * off - 1)) == 0) p = then32(p, o, sh);
+  uint16_t* buf = seg[threadIdx.x >> 6];
+  Pair32 acc = {0u, 0u};  // the identity
+  for (int s0 = 0; s0 < g.w; s0 += kPairSeg) {
+    const int n = min(kPairSeg, g.w - s0);
+    wave_stage_segment(buf, row, s0, n);
+    wave_lds_sync();
+    const int L = (n + 63) >> 6;
+    const int j0 = min(lane * L, n), j1 = min(j0 + L, n);
+    Pair32 p = run_pair([&](int j) { return fsq_units(buf[j0 + j]); }, j1 - j0, sh);
+    for (int off = 1; off < 64; off <<= 1) {
+      Pair32 o;
+      o.a0 = __shfl_down(p.a0, off);
+      o.a1 = __shfl_down(p.a1, off);
+      if ((lane & (2 * off - 1)) == 0) p = then32(p, o, sh);
+    }
+    acc = then32(acc, p, sh);  // meaningful in lane 0
+    wave_lds_sync();  // the next segment reuses buf
   }
   if (lane == 0) {
-    const Pair64 q = widen_pair(p, ra.r2[k]);
+    const Pair64 q = widen_pair(acc, ra.r2[k]);
     ra.pairs[2 * k] = q.a0;
     ra.pairs[2 * k + 1] = q.a1;
   }

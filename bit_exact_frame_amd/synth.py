@@ -1,4 +1,4 @@
-"""Seeded synthetic luma planes for the five frame workloads.
+"""Seeded synthetic luma planes for the frame workloads.
 
 This module only draws samples.  It holds none of the reductions'
 arithmetic (no squares, no sums), so the CPU oracle and the HIP path can
@@ -55,6 +55,15 @@ WORKLOADS = {
                 "ref, dis i.i.d. uniform [0,65535]"),
     5: Workload(5, "16bit_3840x2160_halfrange", 16, 3840, 2160, 3840, 8,
                 "ref U[32768,65535], dis U[0,32767]"),
+    # larger frames and real-content statistics (measured like the five above)
+    6: Workload(6, "16bit_7680x4320_fullrange", 16, 7680, 4320, 7680, 4,
+                "ref, dis i.i.d. uniform [0,65535] (sums pass 2^55)"),
+    7: Workload(7, "16bit_4096x2560_high_small20", 16, 4096, 2560, 4096, 4,
+                "ref U[40000,65535] with one sample in five replaced by U[0,8191]; "
+                "dis U[0,65535] (sums pass 2^55, with ties there)"),
+    8: Workload(8, "16bit_3840x2160_widened_dither", 16, 3840, 2160, 3840, 16,
+                "smooth 8-bit content widened to 16 bits with a seeded low byte "
+                "(widened_frames, mode dither)"),
 }
 
 
@@ -82,6 +91,14 @@ def _draw(wl: Workload, rng: np.random.Generator):
     elif wl.key == 5:
         ref = rng.integers(32768, 65536, size=(h, w))
         dis = rng.integers(0, 32768, size=(h, w))
+    elif wl.key == 6:
+        ref = rng.integers(0, 65536, size=(h, w))
+        dis = rng.integers(0, 65536, size=(h, w))
+    elif wl.key == 7:
+        ref = rng.integers(40000, 65536, size=(h, w))
+        small = rng.random(size=(h, w)) < 0.2
+        ref[small] = rng.integers(0, 8192, size=int(small.sum()))
+        dis = rng.integers(0, 65536, size=(h, w))
     else:
         raise KeyError(wl.key)
     return ref, dis
@@ -92,6 +109,8 @@ def make_frames(key: int, frames: int | None = None, first: int = 0):
     container dtype, frames ``first .. first+F-1``."""
     wl = WORKLOADS[key]
     n = wl.frames if frames is None else int(frames)
+    if key == 8:
+        return widened_frames("dither", n)
     pad = np.iinfo(wl.dtype).max
     ref = np.full((n, wl.h, wl.stride), pad, dtype=wl.dtype)
     dis = np.full((n, wl.h, wl.stride), pad, dtype=wl.dtype)
