@@ -187,27 +187,52 @@ __device__ PlanInfo plan_plane(const uint64_t* R, int8_t* plan, int w, int h, un
     else __syncthreads();
     for (int i = a; i < b; ++i) loc += cl->R[i];
   } else {
+    // the thread's own rows, eight loads in flight at a time
     uint64_t s1l = 0;
-    if (r1)
-      for (int i = threadIdx.x; i < h; i += kT) s1l += r1[i];
+    for (int i0 = a; i0 < b; i0 += 8) {
+      uint64_t rv[8];
+      uint32_t sv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u;
+        rv[u] = i < b ? R[i] : 0;
+        sv[u] = (r1 && i < b) ? r1[i] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        loc += rv[u];
+        s1l += sv[u];
+      }
+    }
     if (s1) *s1 = block_sum_u64(s1l, sm);
-    for (int i = a; i < b; ++i) loc += R[i];
   }
   uint64_t E;
   uint64_t p = block_excl_scan_u64(loc, &E, sm);
   const uint64_t M = E > kTwo53 ? ((uint64_t)w * (uint64_t)h) << (binade(E) - 53) : 0;
   int first = h;
   uint64_t pfirst = 0;
-  for (int i = a; i < b; ++i) {
-    const uint64_t r = keep ? cl->R[i] : R[i];
-    const int e = debug_plan(plan_of(p, r, M), i, dbg);
-    if (keep) cl->plan[i] = (int8_t)e;
-    else plan[i] = (int8_t)e;
-    if (e != kPlanExact && first == h) {
-      first = i;
-      pfirst = p;
+  for (int i0 = a; i0 < b; i0 += 8) {
+    uint64_t rv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u;
+      rv[u] = i < b ? (keep ? cl->R[i] : R[i]) : 0;
     }
-    p += r;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u;
+      if (i < b) {
+        const uint64_t r = rv[u];
+        const int e = debug_plan(plan_of(p, r, M), i, dbg);
+        if (keep) cl->plan[i] = (int8_t)e;
+        else plan[i] = (int8_t)e;
+        if (e != kPlanExact && first == h) {
+          first = i;
+          pfirst = p;
+        }
+        p += r;
+      }
+    }
   }
   const int i0 = block_min_int(first, sm);
   __syncthreads();
@@ -316,7 +341,8 @@ __global__ void __launch_bounds__(256) k_pairs(Geometry g, RowArrays ra, unsigne
 // is 0 or 1 modulo 4, so in the binades of 2^53 and 2^54 a stretch's pair
 // follows from its exact sum and its count of odd squares.
 
-constexpr int kStage = 4096;  // samples of one row staged in LDS by a fallback
+constexpr int kStage = 4096;  // samples of one row staged in LDS by the fast walk
+constexpr int kRowMax = 32768;  // samples of one row staged in LDS by the general walk (max w)
 constexpr int kMaxSeg = 64;   // segments a walk handles as segments
 
 struct Seg {
@@ -428,10 +454,8 @@ struct Walker {
   __device__ uint32_t sample(long k) const {
     return bpc8 ? ((const uint8_t*)plane)[k] : ((const uint16_t*)plane)[k];
   }
-  __device__ uint32_t term(int i, int j) const {
-    if (w <= kStage) return fsq_units(rowbuf[j]);
-    return fsq_units(sample((long)i * stride + j));
-  }
+  // Term j of row i, which fallback_row has staged in rowbuf.
+  __device__ uint32_t term(int, int j) const { return fsq_units(rowbuf[j]); }
   __device__ uint64_t terms(uint64_t s, int i, int j0, int j1) const {
     for (int j = j0; j < j1; ++j) s = rne53_add(s, term(i, j));
     return s;
@@ -453,10 +477,42 @@ struct Walker {
   // with its pairs under the binade S is in and the next one, planned from
   // their own exact prefix; a run that fits neither is added term by term.
   __device__ uint64_t fallback_row(uint64_t s, int i) const {
-    if (w <= kStage && *staged != i) {
+    if (*staged != i) {
+      // the row into LDS (w <= kRowMax), coalesced, each round's loads all
+      // issued before the first store
       __syncthreads();
       const long base = (long)i * stride;
-      for (int j = threadIdx.x; j < w; j += kT) rowbuf[j] = (uint16_t)sample(base + j);
+      const uint16_t* row16 = (const uint16_t*)plane + base;
+      if (!bpc8 && (w & 7) == 0 && ((uintptr_t)row16 & 15) == 0) {
+        // 16-byte loads: 8 samples each, at most 8 per thread (w <= 32768)
+        const int nv = w >> 3;
+        v4u v[kRowMax / 8 / kT];
+#pragma unroll
+        for (int u = 0; u < kRowMax / 8 / kT; ++u) {
+          const int c = u * kT + (int)threadIdx.x;
+          v[u] = c < nv ? ((const v4u*)row16)[c] : (v4u){0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < kRowMax / 8 / kT; ++u) {
+          const int c = u * kT + (int)threadIdx.x;
+          if (c < nv) ((v4u*)rowbuf)[c] = v[u];
+        }
+      } else {
+      constexpr int U = 16;
+      for (int j0 = 0; j0 < w; j0 += U * kT) {
+        uint32_t v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int j = j0 + u * kT + (int)threadIdx.x;
+          v[u] = j < w ? sample(base + j) : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int j = j0 + u * kT + (int)threadIdx.x;
+          if (j < w) rowbuf[j] = (uint16_t)v[u];
+        }
+      }
+      }
       if (threadIdx.x == 0) *staged = i;
       __syncthreads();
     }
@@ -875,34 +931,39 @@ __device__ bool wave_walk(uint64_t* out, uint64_t* exact, const uint64_t* lE, co
   return true;
 }
 
-// The fast PSNR noise by one wave: rows' exact sums in lR (LDS, h <=
-// kChunk) and per block thread t the sum of rows [t*cs, t*cs + cs) in pe
-// (lane l takes the rows of threads [8l, 8l + 8)), the same edges as the moment walk with margin 2 per row (each
-// add past 2^53 rounds by at most u/2 <= 2 units below 2^55), exact rows
-// added as integers, rows across an edge added with the double add, and
-// each stretch of rows inside one binade applied as one pair composed in
-// row order (the stretch spread evenly over the lanes, then an ordered
-// tree).  Returns false when it does not apply.
-__device__ bool wave_noise(double* out, uint64_t* exact, const uint64_t* lR, const uint64_t* pe,
-                           int cs, int h) {
+// The fast PSNR noise by one wave, over one chunk of n rows: their exact
+// sums in lR (LDS, n <= kChunk) and per block thread t the sum of chunk rows
+// [t*cs, t*cs + cs) in pe (lane l takes the rows of threads [8l, 8l + 8)).
+// *sp is the CPU's running sum in units before the chunk (an integer its
+// double holds) and P0 the exact sum of the rows before it; M bounds how far
+// the CPU's sum strays from the exact prefix over the whole plane (2 per
+// row: each add past 2^53 rounds by at most u/2 <= 2 units below 2^55).
+// The same edges as the moment walk: exact rows added as integers, rows
+// across an edge added with the double add, and each stretch of rows inside
+// one binade applied as one pair composed in row order (the stretch spread
+// evenly over the lanes, then an ordered tree).  On success *sp is the
+// running sum after the chunk; *exact is the exact sum after it either
+// way.  False when it does not apply.
+__device__ bool wave_noise(uint64_t* sp, uint64_t* exact, const uint64_t* lR, const uint64_t* pe,
+                           int cs, int n, uint64_t P0, uint64_t M) {
   const int lane = threadIdx.x & 63;
   constexpr int PER = kT / 64;
   const int c = PER * cs;
-  const int a = min(lane * c, h), cl = min(c, h - a);
+  const int a = min(lane * c, n), cl = min(c, n - a);
   uint64_t le = 0;
 #pragma unroll
   for (int q = 0; q < PER; ++q) le += pe[lane * PER + q];
   const uint64_t elast = cl > 0 ? lR[a + cl - 1] : 0;
-  const WEdges ed = wave_edges(h, c, le, 0u, elast, 0, 2ull * (uint64_t)h,
+  const WEdges ed = wave_edges(n, c, le, 0u, elast, P0, M,
                                [&](int k, uint64_t* e, uint32_t* cc) {
                                  *e = lR[k];
                                  *cc = 0;
                                });
   *exact = ed.P[kEdges];
   if (!ed.ok || ed.P[kEdges] >= (1ull << 55)) return false;
-  uint64_t s = 0;
+  uint64_t s = *sp;
   int ia = 0;
-  uint64_t Pa = 0;
+  uint64_t Pa = P0;
 #pragma unroll
   for (int g = 0; g <= kEdges; ++g) {
     const int b = ed.x[g];
@@ -917,8 +978,8 @@ __device__ bool wave_noise(double* out, uint64_t* exact, const uint64_t* lR, con
         s = (uint64_t)d;
       } else if (ep == 53 || ep == 54) {
         const int sh = ep - 52;
-        const int cs = (b - ia + 63) >> 6;
-        const int r0 = min(ia + lane * cs, b), r1 = min(r0 + cs, b);
+        const int rs = (b - ia + 63) >> 6;
+        const int r0 = min(ia + lane * rs, b), r1 = min(r0 + rs, b);
         Pair64 acc = pair64_id();
         for (int i = r0; i < r1; ++i) acc = then64(acc, noise_row_pair(lR[i], sh), sh);
         if (!try_apply(&s, wave_then(acc, sh), ep)) return false;
@@ -929,7 +990,7 @@ __device__ bool wave_noise(double* out, uint64_t* exact, const uint64_t* lR, con
     ia = b;
     Pa = ed.P[g];
   }
-  *out = (double)s;  // an integer the CPU's double holds: exact
+  *sp = s;
   return true;
 }
 
@@ -1015,6 +1076,7 @@ __global__ void __launch_bounds__(kT) k_walk(Geometry g, RowArrays ra, double* r
   __shared__ __attribute__((aligned(16))) RowStage stage[2];
   __shared__ uint64_t pe[kT], pz[kT];
   __shared__ uint32_t pc[kT];
+  __shared__ __attribute__((aligned(16))) uint16_t wide_row[kRowMax];  // a row the general walk leaves its plan in
   __shared__ int staged, fast_ok;
   __shared__ uint64_t res[3];
   const int f = blockIdx.x / 3, job = blockIdx.x % 3;
@@ -1027,26 +1089,38 @@ __global__ void __launch_bounds__(kT) k_walk(Geometry g, RowArrays ra, double* r
     double d = 0.0;
     const uint64_t* RN = ra.rn + (long)f * g.h;
     bool fast = false;
-    if (try_fast) {
-      const int cs = (g.h + kT - 1) / kT, i0 = (int)threadIdx.x * cs;
-      uint64_t v[kRowsPer];
+    if (dbg == 0 && g.may_round) {
+      // kChunk rows at a time: loaded into LDS by every thread, walked by
+      // wave 0 from the running sum while the other waves wait at the barrier
+      uint64_t srun = 0, P = 0;  // the CPU's running sum, the exact one
+      bool ok = true;
+      for (int base = 0; base < g.h && ok; base += kChunk) {
+        const int nr = min(kChunk, g.h - base);
+        const int cs = (nr + kT - 1) / kT, i0 = (int)threadIdx.x * cs;
+        uint64_t v[kRowsPer];
 #pragma unroll
-      for (int q = 0; q < kRowsPer; ++q)  // every load issued before the first use
-        v[q] = q < cs && i0 + q < g.h ? RN[i0 + q] : 0;
-      uint64_t e = 0;
+        for (int q = 0; q < kRowsPer; ++q)  // every load issued before the first use
+          v[q] = q < cs && i0 + q < nr ? RN[base + i0 + q] : 0;
+        uint64_t e = 0;
 #pragma unroll
-      for (int q = 0; q < kRowsPer; ++q) {
-        if (q < cs && i0 + q < g.h) rows.R[i0 + q] = v[q];
-        e += v[q];
+        for (int q = 0; q < kRowsPer; ++q) {
+          if (q < cs && i0 + q < nr) rows.R[i0 + q] = v[q];
+          e += v[q];
+        }
+        pe[threadIdx.x] = e;
+        __syncthreads();
+        if (wave == 0) {
+          const bool okc = wave_noise(&srun, &P, rows.R, pe, cs, nr, P, 2ull * (uint64_t)g.h);
+          if (threadIdx.x == 0) fast_ok = okc;
+        }
+        __syncthreads();  // after it, rows.R and pe are free for the next chunk
+        ok = fast_ok != 0;
       }
-      pe[threadIdx.x] = e;
-      __syncthreads();
-      if (wave == 0) {
-        const bool ok = wave_noise(&d, &ex, rows.R, pe, cs, g.h);
-        if (threadIdx.x == 0) fast_ok = ok;
+      if (ok) {
+        d = (double)srun;  // an integer the CPU's double holds: exact
+        ex = P;
+        fast = true;
       }
-      __syncthreads();
-      fast = fast_ok != 0;
     }
     if (!fast) d = noise_chain(RN, g.h, sm, rows.R, &ex);
     if (threadIdx.x == 0) {
@@ -1115,7 +1189,7 @@ __global__ void __launch_bounds__(kT) k_walk(Geometry g, RowArrays ra, double* r
     if (!fast) {
       general_walk(plane, g.stride, g.w, g.h, g.bpc == 8, ra.r2 + off, ra.codd + off,
                    ra.r1 + off, ra.plan + off, ra.pairs + 2 * off, dbg, sm, rows, runs, rseg,
-                   useg, stage[0].x, &staged, res);
+                   useg, wide_row, &staged, res);
       S = res[0];
       E = res[1];
       s1 = res[2];
