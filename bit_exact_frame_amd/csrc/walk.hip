@@ -270,6 +270,24 @@ constexpr int kPairSeg = 4096;  // samples of a row staged per wave at a time
 template <typename T>
 __device__ __forceinline__ void wave_stage_segment(uint16_t* buf, const T* row, int s0, int n) {
   const int lane = threadIdx.x & 63;
+  if (sizeof(T) == 2 && ((uintptr_t)(row + s0) & 15) == 0) {
+    // 16-byte loads of whole 8-sample chunks, then the tail sample by sample
+    const int nv = n >> 3;
+    constexpr int UV = kPairSeg / 8 / 64;
+    v4u v[UV];
+#pragma unroll
+    for (int u = 0; u < UV; ++u) {
+      const int c = u * 64 + lane;
+      v[u] = c < nv ? ((const v4u*)(row + s0))[c] : (v4u){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < UV; ++u) {
+      const int c = u * 64 + lane;
+      if (c < nv) ((v4u*)buf)[c] = v[u];
+    }
+    for (int j = nv * 8 + lane; j < n; j += 64) buf[j] = (uint16_t)row[s0 + j];
+    return;
+  }
   constexpr int U = kPairSeg / 64;
   uint32_t v[U];
 #pragma unroll
@@ -286,7 +304,7 @@ __device__ __forceinline__ void wave_stage_segment(uint16_t* buf, const T* row, 
 
 template <typename T>
 __global__ void __launch_bounds__(256) k_pairs(Geometry g, RowArrays ra, unsigned dbg) {
-  __shared__ uint16_t seg[4][kPairSeg];
+  __shared__ __attribute__((aligned(16))) uint16_t seg[4][kPairSeg];
   const int lane = threadIdx.x & 63;
   const long task = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
   const long per = 2L * g.nframes;
