@@ -1046,9 +1046,28 @@ __device__ double noise_chain(const uint64_t* RN, int h, BlockScratch& sm, uint6
   for (int base = i0; base < h; base += kChunk) {
     const int n = min(kChunk, h - base);
     __syncthreads();
-    for (int k = threadIdx.x; k < n; k += kT) stage[k] = RN[base + k];
+    uint64_t v[kRowsPer];
+#pragma unroll
+    for (int q = 0; q < kRowsPer; ++q) {  // every load issued before the first store
+      const int k = q * kT + (int)threadIdx.x;
+      v[q] = k < n ? RN[base + k] : 0;
+    }
+#pragma unroll
+    for (int q = 0; q < kRowsPer; ++q) {
+      const int k = q * kT + (int)threadIdx.x;
+      if (k < n) stage[k] = v[q];
+    }
     __syncthreads();
-    for (int k = 0; k < n; ++k) d = d + (double)stage[k];
+    // the adds stay in row order; eight rows are read ahead of them
+    int k = 0;
+    for (; k + 8 <= n; k += 8) {
+      double r[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) r[q] = (double)stage[k + q];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) d = d + r[q];
+    }
+    for (; k < n; ++k) d = d + (double)stage[k];
   }
   return d;
 }
