@@ -474,9 +474,21 @@ struct Walker {
   }
   // Term j of row i, which fallback_row has staged in rowbuf.
   __device__ uint32_t term(int, int j) const { return fsq_units(rowbuf[j]); }
+  // Terms [j0, j1) of row i added to s one at a time with the double add,
+  // the CPU's own step (s is a value its double holds); terms are read
+  // eight ahead of the ordered adds.
   __device__ uint64_t terms(uint64_t s, int i, int j0, int j1) const {
-    for (int j = j0; j < j1; ++j) s = rne53_add(s, term(i, j));
-    return s;
+    double d = (double)s;
+    int j = j0;
+    for (; j + 8 <= j1; j += 8) {
+      double t[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) t[q] = (double)term(i, j + q);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) d = d + t[q];
+    }
+    for (; j < j1; ++j) d = d + (double)term(i, j);
+    return (uint64_t)d;
   }
 
   // Pair of row k of the chunk starting at row c0, under its plan e.
