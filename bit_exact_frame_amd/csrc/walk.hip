@@ -659,10 +659,25 @@ struct Walker {
     for (int a = 0; a < h; a += kChunk) {
       const int n = min(kChunk, h - a);
       __syncthreads();
-      for (int k = threadIdx.x; k < n; k += kT) {
-        rows.R[k] = R[a + k];
-        rows.C[k] = (uint16_t)C[a + k];
-        rows.plan[k] = plan[a + k];
+      constexpr int U = (kChunk + kT - 1) / kT;
+      uint64_t rv[U];
+      uint32_t cv[U];
+      int8_t pv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {  // every load issued before the first store
+        const int k = u * kT + (int)threadIdx.x;
+        rv[u] = k < n ? R[a + k] : 0;
+        cv[u] = k < n ? C[a + k] : 0;
+        pv[u] = k < n ? plan[a + k] : (int8_t)0;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int k = u * kT + (int)threadIdx.x;
+        if (k < n) {
+          rows.R[k] = rv[u];
+          rows.C[k] = (uint16_t)cv[u];
+          rows.plan[k] = pv[u];
+        }
       }
       __syncthreads();
       s = walk_chunk(a, n, s);
