@@ -288,17 +288,19 @@ __device__ __forceinline__ void wave_stage_segment(uint16_t* buf, const T* row, 
     for (int j = nv * 8 + lane; j < n; j += 64) buf[j] = (uint16_t)row[s0 + j];
     return;
   }
-  constexpr int U = kPairSeg / 64;
-  uint32_t v[U];
+  constexpr int U = 16;  // loads in flight per lane per round
+  for (int j0 = 0; j0 < n; j0 += U * 64) {
+    uint32_t v[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int j = u * 64 + lane;
-    v[u] = j < n ? (uint32_t)row[s0 + j] : 0u;
-  }
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + u * 64 + lane;
+      v[u] = j < n ? (uint32_t)row[s0 + j] : 0u;
+    }
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int j = u * 64 + lane;
-    if (j < n) buf[j] = (uint16_t)v[u];
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + u * 64 + lane;
+      if (j < n) buf[j] = (uint16_t)v[u];
+    }
   }
 }
 
