@@ -689,20 +689,22 @@ struct Walker {
 };
 
 // ---------------------------------------------------------------------------
-// Fast walk: the common case, with a short sequential path.  Rows held in
-// LDS; one pass gives every row's exact prefix and odd-square prefix and the
-// segment table; segments planned exact or in the binades of 2^53 and 2^54
-// are added from prefix differences (closed form); a row planned across a
-// binade edge is split into kT runs the same way, and only its crossing
-// run(s) go term by term.  Anything else (planes taller than one chunk,
-// rows wider than kStage, binades from 2^55, many segments, a stretch that
-// is refused, test modes) returns false and the general walk runs instead.
+// Fast walk: the common case, with a short sequential path run by one wave.
+// The plane's row sums sit in LDS; the plan is five threshold edges (below),
+// found by two wave scans; stretches planned exact or in the binades of
+// 2^53 and 2^54 are added from prefix differences (closed form); a row
+// across an edge is split into 64 lane runs the same way, and only the
+// terms at an edge go one at a time, with the double add.  Anything else
+// (planes taller than one chunk, rows wider than kStage, sums from 2^55, a
+// stretch that is refused, test modes) returns false and the general walk
+// runs instead.
 
 // With every sum below 2^55 an item's plan follows from where its exact
 // interval [P - M, P + E + M] lies against 2^53, 2^54 and 2^55.  Each edge
 // of a plan is the first item at which a non-decreasing quantity (P + E, or
-// P - M, or P + E + M) reaches a threshold, so one block minimum over the
-// items finds all of them:
+// P - M, or P + E + M) reaches a threshold, so one scan over the lanes'
+// chunks and one over the items of the chunk that holds the edge find each
+// of them:
 //   x0: P + E > 2^53        (end of the exact items)
 //   x1: P - M >= 2^53       (first item inside the binade of 2^53)
 //   x2: P + E + M >= 2^54   (first item that may leave it)
