@@ -2,16 +2,19 @@
 //
 //   k_plan     (only for frames that can pass 2^55 units, or under a test
 //              flag) exact row prefix and per-row binade plan, for k_pairs.
-//   k_pairs    (same condition) the row's pair under its planned binade:
-//              64 lane runs joined by an ordered tree (ADR-1497 Decision).
+//   k_pairs    (same condition) the row's pair under its planned binade,
+//              one wave per row staged in LDS: 64 lane runs joined by an
+//              ordered tree, segments of 4096 samples joined in row order
+//              (ADR-1497 Decision).
 //   k_walk     one 512-thread block per (frame, plane) takes the rows in
 //              order: exact adds up to 2^53, stretches of rows inside one
 //              binade applied as one pair (closed form in the binades of
 //              2^53 and 2^54), rows that cross a binade edge split into runs,
 //              runs that cross added term by term with the double add
-//              (ADR-1497 Decision); one block per frame adds the noise rows
-//              into a double in row order (ADR-1499 Decision); then the
-//              divisions.
+//              (ADR-1497 Decision); one block per frame takes the noise rows
+//              in order the same way, a chunk of rows at a time, each row
+//              a double add as on the CPU or inside a stretch's composed
+//              pair (ADR-1499 Decision); then the divisions.
 //
 // Units: 1/s^2 for squares, 1/s for first moments (s = 2^(bpc-8)).  No
 // atomics anywhere: every sum has one owner and a fixed order.
@@ -348,7 +351,9 @@ __global__ void __launch_bounds__(256) k_pairs(Geometry g, RowArrays ra, unsigne
 // k_walk.
 //
 // The walk is latency-bound: one block per (frame, plane) and a short
-// sequential path.  Items (the rows of a plane, or the runs of a row that
+// sequential path.  The general walk (any geometry, any sum, every test
+// mode; the fast path below covers the common case with one wave): items
+// (the rows of a plane, or the runs of a row that
 // leaves its plan) are grouped into segments of equal plan by one pass that
 // also records the exact prefix of the item sums and of the odd-square
 // counts at every segment start.  A segment planned exact adds its sum; a
