@@ -330,7 +330,25 @@ __global__ void __launch_bounds__(256) k_pairs(Geometry g, RowArrays ra, unsigne
     wave_lds_sync();
     const int L = (n + 63) >> 6;
     const int j0 = min(lane * L, n), j1 = min(j0 + L, n);
-    Pair32 p = run_pair([&](int j) { return fsq_units(buf[j0 + j]); }, j1 - j0, sh);
+    Pair32 p;
+    if ((L & 7) == 0 && (j1 - j0) == L) {
+      // a whole run of 8-sample chunks: one 16-byte LDS read per 8 terms,
+      // the two trajectories stepped term by term in order
+      const uint32_t u = 1u << sh;
+      uint32_t v0 = 0u, v1 = u;
+      for (int c = j0 >> 3; c < (j0 + L) >> 3; ++c) {
+        const v4u x = ((const v4u*)buf)[c];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const uint32_t t = fsq_units((x[q >> 1] >> (16 * (q & 1))) & 0xFFFFu);
+          v0 = traj_step(v0, t, sh);
+          v1 = traj_step(v1, t, sh);
+        }
+      }
+      p = Pair32{v0, v1 - u};
+    } else {
+      p = run_pair([&](int j) { return fsq_units(buf[j0 + j]); }, j1 - j0, sh);
+    }
     for (int off = 1; off < 64; off <<= 1) {
       Pair32 o;
       o.a0 = __shfl_down(p.a0, off);
