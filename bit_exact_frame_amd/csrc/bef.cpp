@@ -82,7 +82,7 @@ int validate(const void* ref, const void* dis, int w, int h, ptrdiff_t stride,
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t r1, r2, rn, codd, plan, pairs, results, units, total;
+  size_t r1, r2, rn, codd, plan, pairs, psum, results, units, total;
 };
 
 Layout layout(int F, int h) {
@@ -95,6 +95,7 @@ Layout layout(int F, int h) {
   L.codd = o; o = up256(o + 2 * rows * 4);
   L.plan = o; o = up256(o + 2 * rows);
   L.pairs = o; o = up256(o + 4 * rows * 8);
+  L.psum = o; o = up256(o + (size_t)F * 4 * 8);
   L.results = o; o = up256(o + (size_t)F * 6 * 8);
   L.units = o; o = up256(o + (size_t)F * 8 * 8);
   L.total = o;
@@ -257,6 +258,7 @@ int prepare(Call& c, const void* ref, const void* dis, int w, int h, ptrdiff_t s
   g.may_round = (maxsum > kTwo53) || force;
   g.need_odd = g.may_round && bpc != 8;
   c.need_pairs = g.may_round && (maxsum >= (1ull << 55) || g_dbg != 0);
+  g.planned = c.need_pairs;
   c.L = layout(nframes, h);
   if ((rc = ensure(c.dev, c.L.total, (size_t)nframes * 8 * 8 + (size_t)nframes * 6 * 8 + 256))) return rc;
   char* base = (char*)g_arena[c.dev].base;
@@ -266,6 +268,7 @@ int prepare(Call& c, const void* ref, const void* dis, int w, int h, ptrdiff_t s
   c.ra.codd = (uint32_t*)(base + c.L.codd);
   c.ra.plan = (int8_t*)(base + c.L.plan);
   c.ra.pairs = (uint64_t*)(base + c.L.pairs);
+  c.ra.psum = (uint64_t*)(base + c.L.psum);
   c.d_results = (double*)(base + c.L.results);
   c.d_units = (uint64_t*)(base + c.L.units);
   return 0;

@@ -23,6 +23,7 @@ struct Geometry {
   int ng;        // 16-bit kernel: load slots per lane per group (4, 5, 8, 15)
   int need_odd;  // count odd squares per row (frames that can pass 2^53)
   int may_round; // some frame can pass 2^53 units (or forced)
+  int planned;   // k_plan runs before the walk (plan and psum filled)
 };
 
 // Device scratch, [plane][frame][row] (plane 0 = ref, 1 = dis) unless noted.
@@ -33,6 +34,7 @@ struct RowArrays {
   uint32_t* codd;   // number of odd float squares
   int8_t* plan;     // kPlanExact, kPlanCross or a binade
   uint64_t* pairs;  // [plane][frame][row][2] row pair (binades >= 55)
+  uint64_t* psum;   // [plane][frame][2] exact plane sums of r2 and r1 (by k_plan)
 };
 
 // Each launch goes out with hipExtLaunchKernel; ev0 / ev1 (or null) are

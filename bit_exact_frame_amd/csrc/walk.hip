@@ -86,6 +86,34 @@ __device__ __forceinline__ uint64_t block_excl_scan_u64(uint64_t v, uint64_t* to
   return before + inc - v;
 }
 
+// Two-value exclusive block scan (one set of barriers).
+__device__ __forceinline__ void block_excl_scan2(uint64_t v, uint64_t u, uint64_t* ev,
+                                                 uint64_t* eu, uint64_t* tv, uint64_t* tu,
+                                                 BlockScratch& sm) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const uint64_t iv = wave_incl_scan_u64(v), iu = wave_incl_scan_u64(u);
+  __syncthreads();
+  if (lane == 63) {
+    sm.w64[2 * wv] = iv;
+    sm.w64[2 * wv + 1] = iu;
+  }
+  __syncthreads();
+  uint64_t bv = 0, bu = 0, av = 0, au = 0;
+  for (int k = 0; k < kWaves; ++k) {
+    const uint64_t x = sm.w64[2 * k], y = sm.w64[2 * k + 1];
+    if (k < wv) {
+      bv += x;
+      bu += y;
+    }
+    av += x;
+    au += y;
+  }
+  *ev = bv + iv - v;
+  *eu = bu + iu - u;
+  *tv = av;
+  *tu = au;
+}
+
 // Ordered composition of one pair per lane (lane 0 first) inside a wave:
 // lane l takes lane l+1 (quad_perm xor 1), l+2 (quad_perm xor 2), l+4
 // (row_shl:4), l+8 (row_shl:8); the four 16-lane row composites are read
@@ -129,9 +157,7 @@ __device__ __forceinline__ Pair64 block_then(Pair64 p, int sh, BlockScratch& sm)
 // ---------------------------------------------------------------------------
 // Plan (shared by k_plan and k_walk), one pass: thread t owns a contiguous
 // chunk of rows; one block scan of the chunk totals gives every row's exact
-// prefix, hence its plan.  Also returns the first row that is not planned
-// exact and the exact sum before it (every add before it stays at or below
-// 2^53, so that sum is the CPU's running sum there).
+// prefix, hence its plan.
 
 __device__ int debug_plan(int e, int i, unsigned dbg) {
   if (e >= 53 && (dbg & BEF_DBG_PLAN_NONE)) return kPlanCross;
@@ -147,23 +173,23 @@ struct RowLds {
   int8_t plan[kChunk];
 };
 
-struct PlanInfo {
-  uint64_t E;   // exact plane sum
-  int i0;       // first row not planned exact (h if none)
-  uint64_t P0;  // exact sum of rows [0, i0)
-};
-
-// When cl is given and h <= kChunk, the rows' sums, odd counts and plans
-// are left in LDS, indexed by row, and the global plan array is not
-// written; *s1 (if given) receives the plane's first-moment sum from r1.
-__device__ PlanInfo plan_plane(const uint64_t* R, int8_t* plan, int w, int h, unsigned dbg,
+// Returns the exact plane sum.  When cl is given and h <= kChunk, the rows'
+// sums, odd counts and plans are left in LDS, indexed by row, and the global
+// plan array is not written; *s1 (if given) receives the plane's
+// first-moment sum from r1.  kHoldRows lets a thread with at most 16 rows
+// keep them in registers between the two passes.
+template <bool kHoldRows = false>
+__device__ uint64_t plan_plane(const uint64_t* R, int8_t* plan, int w, int h, unsigned dbg,
                                BlockScratch& sm, RowLds* cl = nullptr,
                                const uint32_t* C = nullptr, const uint32_t* r1 = nullptr,
                                uint64_t* s1 = nullptr) {
   const int c = (h + kT - 1) / kT;
   const int a = min((int)threadIdx.x * c, h), b = min(a + c, h);
   const bool keep = cl != nullptr && h <= kChunk;
-  uint64_t loc = 0;
+  constexpr int kHold = 16;  // rows per thread held in registers between the passes
+  const bool hold = kHoldRows && !keep && c <= kHold;
+  uint64_t hv[kHold];
+  uint64_t loc = 0, s1l = 0;
   if (keep) {
     // every load issued before the first is used: one memory round trip
     constexpr int U = (kChunk + kT - 1) / kT;
@@ -176,7 +202,6 @@ __device__ PlanInfo plan_plane(const uint64_t* R, int8_t* plan, int w, int h, un
       cv[u] = i < h ? C[i] : 0;
       sv[u] = (i < h && r1) ? r1[i] : 0;
     }
-    uint64_t s1l = 0;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i = threadIdx.x + u * kT;
@@ -189,9 +214,22 @@ __device__ PlanInfo plan_plane(const uint64_t* R, int8_t* plan, int w, int h, un
     if (s1) *s1 = block_sum_u64(s1l, sm);  // also the barrier before reading cl
     else __syncthreads();
     for (int i = a; i < b; ++i) loc += cl->R[i];
+  } else if (hold) {
+    // the thread's rows in one round trip, kept for the second pass
+    uint32_t sv[kHold];
+#pragma unroll
+    for (int u = 0; u < kHold; ++u) {
+      const int i = a + u;
+      hv[u] = i < b ? R[i] : 0;
+      sv[u] = (r1 && i < b) ? r1[i] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kHold; ++u) {
+      loc += hv[u];
+      s1l += sv[u];
+    }
   } else {
     // the thread's own rows, eight loads in flight at a time
-    uint64_t s1l = 0;
     for (int i0 = a; i0 < b; i0 += 8) {
       uint64_t rv[8];
       uint32_t sv[8];
@@ -207,52 +245,59 @@ __device__ PlanInfo plan_plane(const uint64_t* R, int8_t* plan, int w, int h, un
         s1l += sv[u];
       }
     }
-    if (s1) *s1 = block_sum_u64(s1l, sm);
   }
-  uint64_t E;
-  uint64_t p = block_excl_scan_u64(loc, &E, sm);
+  uint64_t E, p;
+  if (s1 && !keep) {  // the first-moment sum rides on the scan's barriers
+    uint64_t ps1;
+    block_excl_scan2(loc, s1l, &p, &ps1, &E, s1, sm);
+  } else {
+    p = block_excl_scan_u64(loc, &E, sm);
+  }
   const uint64_t M = E > kTwo53 ? ((uint64_t)w * (uint64_t)h) << (binade(E) - 53) : 0;
-  int first = h;
-  uint64_t pfirst = 0;
-  for (int i0 = a; i0 < b; i0 += 8) {
-    uint64_t rv[8];
+  auto emit = [&](int i, uint64_t r) {  // row i's plan from its exact prefix p
+    const int e = debug_plan(plan_of(p, r, M), i, dbg);
+    if (keep) cl->plan[i] = (int8_t)e;
+    else plan[i] = (int8_t)e;
+    p += r;
+  };
+  if (hold) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = i0 + u;
-      rv[u] = i < b ? (keep ? cl->R[i] : R[i]) : 0;
-    }
+    for (int u = 0; u < kHold; ++u)
+      if (a + u < b) emit(a + u, hv[u]);
+  } else {
+    for (int i0 = a; i0 < b; i0 += 8) {
+      uint64_t rv[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = i0 + u;
-      if (i < b) {
-        const uint64_t r = rv[u];
-        const int e = debug_plan(plan_of(p, r, M), i, dbg);
-        if (keep) cl->plan[i] = (int8_t)e;
-        else plan[i] = (int8_t)e;
-        if (e != kPlanExact && first == h) {
-          first = i;
-          pfirst = p;
-        }
-        p += r;
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u;
+        rv[u] = i < b ? (keep ? cl->R[i] : R[i]) : 0;
       }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (i0 + u < b) emit(i0 + u, rv[u]);
     }
   }
-  const int i0 = block_min_int(first, sm);
-  __syncthreads();
-  if (i0 < h && first == i0) sm.v[0] = pfirst;
-  __syncthreads();
-  return PlanInfo{E, i0, i0 < h ? sm.v[0] : E};
+  if (keep) __syncthreads();  // the plans in LDS visible to the whole block
+  return E;
 }
 
 __device__ __forceinline__ bool may_round(uint64_t E, unsigned dbg) {
   return E > kTwo53 || (dbg & BEF_DBG_FORCE_ROUND);
 }
 
+// Also leaves the plane's exact sums of r2 and r1 in psum, so that the
+// general walk need not plan the plane again.
 __global__ void __launch_bounds__(kT) k_plan(Geometry g, RowArrays ra, unsigned dbg) {
   __shared__ BlockScratch sm;
   const int f = blockIdx.x >> 1, pl = blockIdx.x & 1;
   const long off = (long)(pl * g.nframes + f) * g.h;
-  plan_plane(ra.r2 + off, ra.plan + off, g.w, g.h, dbg, sm);
+  uint64_t s1 = 0;
+  const uint64_t E =
+      plan_plane<true>(ra.r2 + off, ra.plan + off, g.w, g.h, dbg, sm, nullptr, nullptr, ra.r1 + off, &s1);
+  if (threadIdx.x == 0) {
+    ra.psum[2 * (pl * g.nframes + f)] = E;
+    ra.psum[2 * (pl * g.nframes + f) + 1] = s1;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -405,34 +450,6 @@ struct RunLds {
   int8_t plan[kT];
 };
 
-// Two-value exclusive block scan (one set of barriers).
-__device__ __forceinline__ void block_excl_scan2(uint64_t v, uint64_t u, uint64_t* ev,
-                                                 uint64_t* eu, uint64_t* tv, uint64_t* tu,
-                                                 BlockScratch& sm) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const uint64_t iv = wave_incl_scan_u64(v), iu = wave_incl_scan_u64(u);
-  __syncthreads();
-  if (lane == 63) {
-    sm.w64[2 * wv] = iv;
-    sm.w64[2 * wv + 1] = iu;
-  }
-  __syncthreads();
-  uint64_t bv = 0, bu = 0, av = 0, au = 0;
-  for (int k = 0; k < kWaves; ++k) {
-    const uint64_t x = sm.w64[2 * k], y = sm.w64[2 * k + 1];
-    if (k < wv) {
-      bv += x;
-      bu += y;
-    }
-    av += x;
-    au += y;
-  }
-  *ev = bv + iv - v;
-  *eu = bu + iu - u;
-  *tv = av;
-  *tu = au;
-}
-
 // Segment table of items [0, n) whose sums E, odd counts C and plans are in
 // LDS (plan already final and visible).  Thread t owns items
 // [t*c, t*c + c).  Returns the number of segments; the table holds
@@ -481,7 +498,7 @@ struct Walker {
   const void* plane;  // this frame's plane
   long stride;
   int w, h, bpc8;
-  const uint64_t* R;  // global, for planes taller than one chunk
+  const uint64_t* R;  // global row sums, loaded a chunk at a time unless held in LDS
   const uint32_t* C;
   const int8_t* plan;
   const uint64_t* pairs;
@@ -676,10 +693,10 @@ struct Walker {
     return s;
   }
 
-  // The plane from S = 0, a chunk of rows at a time (plan_plane has left the
-  // rows in LDS when the plane fits one chunk).
-  __device__ uint64_t walk_rows() const {
-    if (h <= kChunk) return walk_chunk(0, h, 0);
+  // The plane from S = 0, a chunk of rows at a time (when `held`, plan_plane
+  // has left the rows of a plane that fits one chunk in LDS).
+  __device__ uint64_t walk_rows(bool held) const {
+    if (held) return walk_chunk(0, h, 0);
     uint64_t s = 0;
     for (int a = 0; a < h; a += kChunk) {
       const int n = min(kChunk, h - a);
@@ -1131,23 +1148,29 @@ __device__ double noise_chain(const uint64_t* RN, int h, BlockScratch& sm, uint6
 __device__ __noinline__ void general_walk(const char* plane, long stride, int w, int h, int bpc8,
                                           const uint64_t* r2, const uint32_t* codd,
                                           const uint32_t* r1, int8_t* plan, uint64_t* pairs,
-                                          unsigned dbg, BlockScratch& sm, RowLds& rows,
-                                          RunLds& runs, Seg* rseg, Seg* useg,
-                                          uint16_t* rowbuf, int* staged, uint64_t* res) {
+                                          const uint64_t* psum, unsigned dbg,
+                                          BlockScratch& sm, RowLds& rows, RunLds& runs,
+                                          Seg* rseg, Seg* useg, uint16_t* rowbuf, int* staged,
+                                          uint64_t* res) {
   __syncthreads();
-  uint64_t s1 = 0;
-  const PlanInfo pi = plan_plane(r2, plan, w, h, dbg, sm, &rows, codd, r1, &s1);
-  uint64_t S = pi.E;
-  if (may_round(pi.E, dbg)) {
+  uint64_t E, s1 = 0;
+  if (psum) {  // planned by k_plan
+    E = psum[0];
+    s1 = psum[1];
+  } else {
+    E = plan_plane(r2, plan, w, h, dbg, sm, &rows, codd, r1, &s1);
+  }
+  uint64_t S = E;
+  if (may_round(E, dbg)) {
     if (threadIdx.x == 0) *staged = -1;
     __syncthreads();
     const Walker wk{plane, stride, w,   h,     bpc8, r2,   codd,  plan,   pairs,
                     dbg,   sm,     rows, runs, rseg, useg, rowbuf, staged};
-    S = wk.walk_rows();
+    S = wk.walk_rows(!psum && h <= kChunk);
   }
   if (threadIdx.x == 0) {
     res[0] = S;
-    res[1] = pi.E;
+    res[1] = E;
     res[2] = s1;
   }
   __syncthreads();
@@ -1279,8 +1302,9 @@ __global__ void __launch_bounds__(kT) k_walk(Geometry g, RowArrays ra, double* r
     }
     if (!fast) {
       general_walk(plane, g.stride, g.w, g.h, g.bpc == 8, ra.r2 + off, ra.codd + off,
-                   ra.r1 + off, ra.plan + off, ra.pairs + 2 * off, dbg, sm, rows, runs, rseg,
-                   useg, wide_row, &staged, res);
+                   ra.r1 + off, ra.plan + off, ra.pairs + 2 * off,
+                   g.planned ? ra.psum + 2 * (pl * g.nframes + f) : nullptr, dbg, sm, rows, runs,
+                   rseg, useg, wide_row, &staged, res);
       S = res[0];
       E = res[1];
       s1 = res[2];
