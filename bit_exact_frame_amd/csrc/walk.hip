@@ -545,6 +545,125 @@ struct Walker {
     return Pair64{E + (uint64_t)(int64_t)runs.B0[k], E + (uint64_t)(int64_t)runs.B1[k]};
   }
 
+  // A row the plan does not fit, by groups of runs: kT runs of ceil(w/kT)
+  // terms, each planned from its exact prefix with the row's margin.  A
+  // row meets at most one edge, so its runs fall in at most three groups
+  // in row order: with S below 2^53 exact, across, binade eA; else binade
+  // eA, across, binade eB.  A group inside a binade adds its closed-form
+  // pair (binades of 2^53 and 2^54) or its runs' pairs joined in order; the
+  // group across the edge goes term by term.  Returns false (S untouched)
+  // when the runs do not form such groups or a group's step does not apply.
+  __device__ bool row_groups(uint64_t* sp, int i) const {
+    const uint64_t s0 = *sp;
+    const bool low = s0 < kTwo53;
+    const int eA = low ? 53 : binade(s0), eB = eA + 1;
+    const int e2 = low ? eA : eB;  // binade of group 2 (group 0: exact or eA)
+    const int L = (w + kT - 1) / kT, nr = (w + L - 1) / L;
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const int j0 = min(t * L, w), j1 = min(j0 + L, w);
+    uint64_t E = 0;
+    uint32_t c = 0;
+    for (int j = j0; j < j1; j += 8) {  // eight LDS reads in flight at a time
+      uint32_t x[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) x[q] = j + q < j1 ? term(i, j + q) : 0u;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        E += x[q];
+        c += x[q] & 1u;
+      }
+    }
+    uint64_t Q, QC, tot, totc;
+    block_excl_scan2(E, c, &Q, &QC, &tot, &totc, sm);
+    int g = 3;  // the run's group; 3: none of the three
+    if (t < nr) {
+      const int p = plan_of(s0 + Q, E, (uint64_t)w << (eB - 53));
+      g = p == kPlanCross ? 1 : (p == (low ? kPlanExact : eA)) ? 0 : p == e2 ? 2 : 3;
+    }
+    // pairs of the runs of groups in binades from 2^55 up, joined in order
+    const bool tree0 = !low && eA >= 55, tree2 = e2 >= 55;
+    Pair64 c0 = pair64_id(), c2 = pair64_id();
+    if (tree0 || tree2) {
+      const int e = g == 0 ? eA : e2;
+      if ((g == 0 && tree0) || (g == 2 && tree2)) {
+        // the run's two trajectories (run_pair's steps), terms read eight at a time
+        const int sh = e - 52;
+        const uint32_t u = 1u << sh;
+        uint32_t v0 = 0u, v1 = u;
+        for (int j = j0; j < j1; j += 8) {
+          uint32_t x[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) x[q] = j + q < j1 ? term(i, j + q) : 0u;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            if (j + q < j1) {
+              v0 = traj_step(v0, x[q], sh);
+              v1 = traj_step(v1, x[q], sh);
+            }
+          }
+        }
+        const Pair64 pr = widen_pair(Pair32{v0, v1 - u}, E);
+        if (g == 0) c0 = pr;
+        else c2 = pr;
+      }
+      if (tree0) c0 = wave_then(c0, eA - 52);
+      if (tree2) c2 = wave_then(c2, e2 - 52);
+      if (lane == 0) {
+        runs.E[4 * wv] = c0.a0;
+        runs.E[4 * wv + 1] = c0.a1;
+        runs.E[4 * wv + 2] = c2.a0;
+        runs.E[4 * wv + 3] = c2.a1;
+      }
+    }
+    runs.plan[t] = (int8_t)g;
+    if (t == 0) {
+      sm.iv[0] = 0;  // set when the groups are not in order
+      for (int k = 0; k < 3; ++k) useg[k].start = -1;
+    }
+    __syncthreads();
+    if (t < nr) {
+      const int gp = t > 0 ? runs.plan[t - 1] : -1;
+      if (g == 3 || gp > g) sm.iv[0] = 1;
+      if (gp != g && g < 3) useg[g] = Seg{Q, QC, t, g};
+    }
+    if (tree0 || tree2) {  // the waves' composites joined in order
+      c0 = Pair64{runs.E[0], runs.E[1]};
+      c2 = Pair64{runs.E[2], runs.E[3]};
+      for (int k = 1; k < kWaves; ++k) {
+        c0 = then64(c0, Pair64{runs.E[4 * k], runs.E[4 * k + 1]}, eA - 52);
+        c2 = then64(c2, Pair64{runs.E[4 * k + 2], runs.E[4 * k + 3]}, e2 - 52);
+      }
+    }
+    __syncthreads();
+    if (sm.iv[0]) return false;
+    Seg G[4];  // the three groups' starts (start -1: empty), then the end
+#pragma unroll
+    for (int k = 0; k < 3; ++k) G[k] = useg[k];
+    G[3] = Seg{tot, totc, nr, 3};
+    uint64_t s = s0;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const Seg A = G[k];
+      if (A.start < 0) continue;
+      const Seg B = G[k + 1].start >= 0 ? G[k + 1] : (k == 0 && G[2].start >= 0) ? G[2] : G[3];
+      const uint64_t P1 = B.P, PC1 = B.PC;
+      const int b = B.start;
+      if (k == 1) {
+        s = terms(s, i, A.start * L, min(b * L, w));
+        continue;
+      }
+      if (k == 0 && low) {
+        if (!try_exact(&s, P1 - A.P)) return false;
+        continue;
+      }
+      const int e = k == 0 ? eA : e2;
+      const Pair64 pr = e <= 54 ? closed_pair(P1 - A.P, PC1 - A.PC, e) : (k == 0 ? c0 : c2);
+      if (!try_apply(&s, pr, e)) return false;
+    }
+    *sp = s;
+    return true;
+  }
+
   // A row the plan does not fit, from S: kT runs of ceil(w/kT) terms, each
   // with its pairs under the binade S is in and the next one, planned from
   // their own exact prefix; a run that fits neither is added term by term.
@@ -589,6 +708,11 @@ struct Walker {
       __syncthreads();
     }
     if (dbg & BEF_DBG_TERMS_ONLY) return terms(s, i, 0, w);
+    if (!(dbg & (BEF_DBG_PLAN_WRONG | BEF_DBG_PLAN_NONE | BEF_DBG_NO_STRETCH |
+                 BEF_DBG_NO_CLOSED_FORM))) {
+      uint64_t s2 = s;
+      if (row_groups(&s2, i)) return s2;  // else the segment walk over the runs below
+    }
     const int eA = s < kTwo53 ? 53 : binade(s);
     const int eB = eA + 1;
     const int L = (w + kT - 1) / kT;
