@@ -708,8 +708,8 @@ struct Walker {
       __syncthreads();
     }
     if (dbg & BEF_DBG_TERMS_ONLY) return terms(s, i, 0, w);
-    if (!(dbg & (BEF_DBG_PLAN_WRONG | BEF_DBG_PLAN_NONE | BEF_DBG_NO_STRETCH |
-                 BEF_DBG_NO_CLOSED_FORM))) {
+    // (the test modes without stretches or closed forms keep to the segment walk)
+    if (!(dbg & (BEF_DBG_NO_STRETCH | BEF_DBG_NO_CLOSED_FORM))) {
       uint64_t s2 = s;
       if (row_groups(&s2, i)) return s2;  // else the segment walk over the runs below
     }
