@@ -353,10 +353,11 @@ __device__ __forceinline__ void wave_stage_segment(uint16_t* buf, const T* row, 
 }
 
 template <typename T>
-__global__ void __launch_bounds__(256) k_pairs(Geometry g, RowArrays ra, unsigned dbg) {
+__global__ void __launch_bounds__(256) k_pairs(Geometry g, RowArrays ra, unsigned dbg,
+                                                long task0) {
   __shared__ __attribute__((aligned(16))) uint16_t seg[4][kPairSeg];
   const int lane = threadIdx.x & 63;
-  const long task = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const long task = task0 + (long)blockIdx.x * 4 + (threadIdx.x >> 6);
   const long per = 2L * g.nframes;
   if (task >= per * g.h) return;
   const int i = g.h - 1 - (int)(task / per);  // last rows first
@@ -1458,10 +1459,22 @@ hipError_t launch_plan(const Geometry& g, const RowArrays& ra, unsigned dbg, hip
 hipError_t launch_pairs(const Geometry& g, const RowArrays& ra, unsigned dbg, hipStream_t st,
                         hipEvent_t ev0, hipEvent_t ev1) {
   const long tasks = 2L * g.nframes * g.h;
-  const unsigned blocks = (unsigned)((tasks + 3) / 4);
-  if (g.bpc == 8) hipExtLaunchKernelGGL(k_pairs<uint8_t>, dim3(blocks), dim3(256), 0, st, ev0, ev1, 0, g, ra, dbg);
-  else hipExtLaunchKernelGGL(k_pairs<uint16_t>, dim3(blocks), dim3(256), 0, st, ev0, ev1, 0, g, ra, dbg);
-  return hipGetLastError();
+  const int rpb = 4;  // rows per block, one wave each
+  const long blocks = (tasks + rpb - 1) / rpb;
+  // a dispatch's grid, in work-items, must stay below 2^32
+  const long kMaxBlocks = (dbg & BEF_DBG_SPLIT_LAUNCH) ? 64 : 1L << 23;
+  for (long b0 = 0; b0 < blocks; b0 += kMaxBlocks) {
+    const unsigned nb = (unsigned)(blocks - b0 < kMaxBlocks ? blocks - b0 : kMaxBlocks);
+    hipEvent_t e0 = b0 == 0 ? ev0 : nullptr, e1 = b0 + nb >= blocks ? ev1 : nullptr;
+    const long t0 = b0 * rpb;
+    if (g.bpc == 8)
+      hipExtLaunchKernelGGL(k_pairs<uint8_t>, dim3(nb), dim3(256), 0, st, e0, e1, 0, g, ra, dbg, t0);
+    else
+      hipExtLaunchKernelGGL(k_pairs<uint16_t>, dim3(nb), dim3(256), 0, st, e0, e1, 0, g, ra, dbg, t0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_walk(const Geometry& g, const RowArrays& ra, double* results, uint64_t* units,

@@ -124,6 +124,8 @@ const char *bef_last_error(void);
  *   BEF_DBG_NO_STRETCH  apply planned rows one by one, not as stretches
  *   BEF_DBG_NO_CLOSED_FORM  form every planned row's pair from lane runs,
  *                       also in the binades of 2^53 and 2^54
+ *   BEF_DBG_SPLIT_LAUNCH  split the row-pair pass into dispatches of 64
+ *                       blocks (the split that very large batches take)
  * Returns the previous flags. */
 #define BEF_DBG_PLAN_WRONG 1u
 #define BEF_DBG_PLAN_NONE 2u
@@ -131,6 +133,7 @@ const char *bef_last_error(void);
 #define BEF_DBG_FORCE_ROUND 8u
 #define BEF_DBG_NO_STRETCH 16u
 #define BEF_DBG_NO_CLOSED_FORM 32u
+#define BEF_DBG_SPLIT_LAUNCH 64u
 unsigned bef_debug_set(unsigned flags);
 
 /* Diagnostic, not part of the reductions: the memory side of the 16-bit

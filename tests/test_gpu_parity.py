@@ -180,14 +180,15 @@ def test_single_frame_entry_points(api, orc):
     assert bits(p).tolist() == bits(orc.psnr_noise(ref[0], dis[0], 12, w=wl.w)).tolist()
 
 
-DEBUG = [1, 2, 4, 8, 16, 32, 1 | 16, 2 | 32, 8 | 32]
+DEBUG = [1, 2, 4, 8, 16, 32, 1 | 16, 2 | 32, 8 | 32, 32 | 64]
 
 
 @pytest.mark.parametrize("flags", DEBUG)
 def test_debug_paths_same_bits(api, orc, flags):
     """Wrong plans, no plans, terms only, forced rounding, no stretches, no
-    closed form: every path must give the CPU's bits (ADR-1497, Decision:
-    any plan, even a wrong one, only changes which increments are used)."""
+    closed form, row pairs in many small dispatches: every path must give
+    the CPU's bits (ADR-1497, Decision: any plan, even a wrong one, only
+    changes which increments are used)."""
     r4, d4 = synth.make_frames(4, frames=2)
     r5, d5 = synth.make_frames(5, frames=1)
     b = boundary.build("b53p3")
