@@ -1,7 +1,8 @@
 // walk.hip -- the ordered part: plan, pairs and the walk of each plane.
 //
 //   k_plan     (only for frames that can pass 2^55 units, or under a test
-//              flag) exact row prefix and per-row binade plan, for k_pairs.
+//              flag) exact row prefix and per-row binade plan, for k_pairs
+//              and the walk, and each plane's exact sums, for the walk.
 //   k_pairs    (same condition) the row's pair under its planned binade,
 //              one wave per row staged in LDS: 64 lane runs joined by an
 //              ordered tree, segments of 4096 samples joined in row order
@@ -9,9 +10,11 @@
 //   k_walk     one 512-thread block per (frame, plane) takes the rows in
 //              order: exact adds up to 2^53, stretches of rows inside one
 //              binade applied as one pair (closed form in the binades of
-//              2^53 and 2^54), rows that cross a binade edge split into runs,
-//              runs that cross added term by term with the double add
-//              (ADR-1497 Decision); one block per frame takes the noise rows
+//              2^53 and 2^54), rows that cross a binade edge split into runs
+//              taken as at most three groups (inside a binade or exact,
+//              across the edge, inside the next binade), runs that cross
+//              added term by term with the double add (ADR-1497
+//              Decision); one block per frame takes the noise rows
 //              in order the same way, a chunk of rows at a time, each row
 //              a double add as on the CPU or inside a stretch's composed
 //              pair (ADR-1499 Decision); then the divisions.
