@@ -168,7 +168,7 @@ __device__ int debug_plan(int e, int i, unsigned dbg) {
   return e;
 }
 
-constexpr int kChunk = 2176;  // rows held in LDS by the walk
+constexpr int kChunk = 4352;  // rows held in LDS by the walk
 
 struct RowLds {
   uint64_t R[kChunk];
@@ -1325,7 +1325,11 @@ __global__ void __launch_bounds__(kT) k_walk(Geometry g, RowArrays ra, double* r
   const int k = g.bpc - 8;
   const double n = (double)g.w * (double)g.h;
   const int wave = threadIdx.x >> 6;
-  const bool try_fast = dbg == 0 && g.may_round && g.h <= kChunk && g.w <= kStage;
+  // the fast path stops below 2^55: a plane k_plan has summed past it goes
+  // straight to the general walk
+  const bool try_fast = dbg == 0 && g.may_round && g.h <= kChunk && g.w <= kStage &&
+                        !(g.planned && job < 2 &&
+                          ra.psum[2 * (job * g.nframes + f)] >= (1ull << 55));
   if (job == 2) {
     uint64_t ex = 0;
     double d = 0.0;

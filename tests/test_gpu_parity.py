@@ -209,15 +209,15 @@ def test_past_2_55_8k_noise(api, orc):
 
 
 def test_noise_past_2_55_tall(api, orc):
-    """A 7680x4320 frame of high ref against low dis: the noise passes 2^55
-    on a plane taller than one chunk of rows, so the noise takes the row
-    chain (every add a double add past 2^53), and both moments pass 2^55."""
+    """A 7680x4608 frame of high ref against low dis: the noise passes 2^55
+    on a plane taller than one chunk of rows (4352 rows), so the noise runs
+    chunk by chunk past 2^53, and both moments pass 2^55."""
     rng = np.random.Generator(np.random.PCG64(7655))
-    ref = rng.integers(48000, 65536, size=(1, 4320, 7680)).astype(np.uint16)
-    dis = rng.integers(0, 16000, size=(1, 4320, 7680)).astype(np.uint16)
+    ref = rng.integers(48000, 65536, size=(1, 4608, 7680)).astype(np.uint16)
+    dis = rng.integers(0, 16000, size=(1, 4608, 7680)).astype(np.uint16)
     u = api.bef_frames_units(dev(ref), dev(dis), 16)
     assert int(u[0, 6]) > 1 << 55
-    check_batch(api, orc, ref, dis, 16, label="7680x4320 noise past 2^55")
+    check_batch(api, orc, ref, dis, 16, label="7680x4608 noise past 2^55")
 
 
 def test_past_2_55_4096x2560(api, orc):
