@@ -25,10 +25,11 @@ from checkers import t_table
 
 TWO53 = 1 << 53
 TWO54 = 1 << 54
-N_CASES = 16
+N_CASES = 16      # through the host emulation (CPU) and on the GPU
+N_GPU_CASES = 64  # on the GPU only (cases 16 and up are GPU-only)
 
 
-@functools.lru_cache(maxsize=None)
+@functools.lru_cache(maxsize=4)  # a few cases, not all of them, held at once
 def case(k: int):
     """(ref[h, stride], dis[h, stride], w, bpc, label) of case k."""
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([0xBEF, 4242, k])))

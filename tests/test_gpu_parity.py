@@ -255,7 +255,7 @@ def test_past_2_53_2560x1440_16bit(api, orc):
     check_batch(api, orc, ref, dis, 16, w=2560, label="2560x1440 16-bit past 2^53")
 
 
-@pytest.mark.parametrize("k", range(random_frames.N_CASES))
+@pytest.mark.parametrize("k", range(random_frames.N_GPU_CASES))
 def test_random_crossings(api, orc, k):
     """Seeded random planes whose sum crosses 2^53 or 2^54 at a random row
     and column, with random width, padding, bit depth, tail and dis."""
