@@ -272,6 +272,17 @@ def test_wide_rows_past_2_53(api, orc):
     check_batch(api, orc, ref, dis, 16, label="7680x1100")
 
 
+@pytest.mark.parametrize("h", [4352, 4353])
+def test_one_chunk_of_rows_past_2_53(api, orc, h):
+    """2048-wide full-range noise past 2^53 (below 2^55) in a plane of
+    exactly as many rows as the walk holds in LDS (4352: the fast path with
+    its most rows per thread) and in one row more (the general walk)."""
+    ref, dis = synth.uniform_planes(h, 1, h, 2048, 2048, 16)
+    units = api.bef_frames_units(dev(ref), dev(dis), 16)
+    assert (units[:, 2] > 1 << 53).all() and (units[:, 2] < 1 << 55).all()
+    check_batch(api, orc, ref, dis, 16, label=f"2048x{h}")
+
+
 def test_tall_plane_past_2_53(api, orc):
     """1024x8192 full-range noise: more rows than the walk holds in LDS."""
     ref, dis = synth.uniform_planes(8193, 1, 8192, 1024, 1024, 16)
