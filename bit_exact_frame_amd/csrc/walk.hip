@@ -498,6 +498,32 @@ __device__ __forceinline__ Pair64 compose_items(int a, int b, int sh, PairAt pai
   return block_then(acc, sh, sm);
 }
 
+// Rows [a, a + n) of a plane's row sums, odd counts and plans into LDS, every
+// load issued before the first store (no barrier).
+__device__ __forceinline__ void load_rows(RowLds& rows, const uint64_t* R, const uint32_t* C,
+                                          const int8_t* plan, int a, int n) {
+  constexpr int U = (kChunk + kT - 1) / kT;
+  uint64_t rv[U];
+  uint32_t cv[U];
+  int8_t pv[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int k = u * kT + (int)threadIdx.x;
+    rv[u] = k < n ? R[a + k] : 0;
+    cv[u] = k < n ? C[a + k] : 0;
+    pv[u] = k < n ? plan[a + k] : (int8_t)0;
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int k = u * kT + (int)threadIdx.x;
+    if (k < n) {
+      rows.R[k] = rv[u];
+      rows.C[k] = (uint16_t)cv[u];
+      rows.plan[k] = pv[u];
+    }
+  }
+}
+
 struct Walker {
   const void* plane;  // this frame's plane
   long stride;
@@ -823,33 +849,17 @@ struct Walker {
 
   // The plane from S = 0, a chunk of rows at a time (when `held`, plan_plane
   // has left the rows of a plane that fits one chunk in LDS).
-  __device__ uint64_t walk_rows(bool held) const {
+  // (first_loaded: the caller has put the first chunk in LDS already)
+  __device__ uint64_t walk_rows(bool held, bool first_loaded) const {
     if (held) return walk_chunk(0, h, 0);
     uint64_t s = 0;
     for (int a = 0; a < h; a += kChunk) {
       const int n = min(kChunk, h - a);
-      __syncthreads();
-      constexpr int U = (kChunk + kT - 1) / kT;
-      uint64_t rv[U];
-      uint32_t cv[U];
-      int8_t pv[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {  // every load issued before the first store
-        const int k = u * kT + (int)threadIdx.x;
-        rv[u] = k < n ? R[a + k] : 0;
-        cv[u] = k < n ? C[a + k] : 0;
-        pv[u] = k < n ? plan[a + k] : (int8_t)0;
+      if (a > 0 || !first_loaded) {
+        __syncthreads();
+        load_rows(rows, R, C, plan, a, n);
+        __syncthreads();
       }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int k = u * kT + (int)threadIdx.x;
-        if (k < n) {
-          rows.R[k] = rv[u];
-          rows.C[k] = (uint16_t)cv[u];
-          rows.plan[k] = pv[u];
-        }
-      }
-      __syncthreads();
       s = walk_chunk(a, n, s);
     }
     return s;
@@ -1282,9 +1292,10 @@ __device__ __noinline__ void general_walk(const char* plane, long stride, int w,
                                           uint64_t* res) {
   __syncthreads();
   uint64_t E, s1 = 0;
-  if (psum) {  // planned by k_plan
+  if (psum) {  // planned by k_plan; the first chunk's rows come with the sums
     E = psum[0];
     s1 = psum[1];
+    load_rows(rows, r2, codd, plan, 0, min(kChunk, h));
   } else {
     E = plan_plane(r2, plan, w, h, dbg, sm, &rows, codd, r1, &s1);
   }
@@ -1294,7 +1305,7 @@ __device__ __noinline__ void general_walk(const char* plane, long stride, int w,
     __syncthreads();
     const Walker wk{plane, stride, w,   h,     bpc8, r2,   codd,  plan,   pairs,
                     dbg,   sm,     rows, runs, rseg, useg, rowbuf, staged};
-    S = wk.walk_rows(!psum && h <= kChunk);
+    S = wk.walk_rows(!psum && h <= kChunk, psum != nullptr);
   }
   if (threadIdx.x == 0) {
     res[0] = S;
