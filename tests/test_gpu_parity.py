@@ -381,11 +381,13 @@ def test_deterministic(api):
     assert (a == b).all()
 
 
-@pytest.mark.parametrize("key,pinned", [(5, False), (5, True), (3, True)])
+@pytest.mark.parametrize("key,pinned", [(5, False), (5, True), (3, True), (7, True)])
 def test_host_pipeline_matches_device(api, orc, key, pinned):
     """Frames from host memory, streamed through the two device slots (the
-    12-bit workload takes four chunks, so both slots are reloaded), give the
-    same bits as the device entry point and the oracle."""
+    12-bit workload takes four chunks, so both slots are reloaded; the
+    4096x2560 near-maximum frames pass 2^55, so each chunk plans and forms
+    row pairs), give the same bits as the device entry point and the
+    oracle."""
     import torch
     wl = synth.WORKLOADS[key]
     ref, dis = synth.make_frames(key)
