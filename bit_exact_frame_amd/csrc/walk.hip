@@ -414,6 +414,125 @@ __global__ void __launch_bounds__(256) k_pairs(Geometry g, RowArrays ra, unsigne
   }
 }
 
+
+// The pair pass for 16-bit planes whose rows start on 16-byte boundaries and
+// hold whole 8-sample chunks: each wave takes kPipeRows consecutive tasks
+// and runs their segments as one stream, the next segment's 16-byte loads
+// in flight (in registers) while the current one is summed from LDS.  The
+// arithmetic is k_pairs': the same runs, trees and joins, in the same order.
+// One row per wave: with more, too few waves have work (a wave's tasks are
+// one row of the same planes, which need pairs together or not at all).
+constexpr int kPipeRows = 1;
+
+__device__ __forceinline__ const uint16_t* pair_row(const Geometry& g, long task, long* k) {
+  const long per = 2L * g.nframes;
+  const int i = g.h - 1 - (int)(task / per);  // last rows first
+  const int rem = (int)(task % per);
+  const int pl = rem / g.nframes, f = rem % g.nframes;
+  *k = (long)(pl * g.nframes + f) * g.h + i;
+  return (const uint16_t*)(pl == 0 ? g.ref : g.dis) + (long)f * g.pitch + (long)i * g.stride;
+}
+
+__global__ void __launch_bounds__(256) k_pairs_pipe(Geometry g, RowArrays ra, unsigned dbg,
+                                                     long task0) {
+  __shared__ __attribute__((aligned(16))) uint16_t seg[4][kPairSeg];
+  const int lane = threadIdx.x & 63;
+  const long ntask = 2L * g.nframes * g.h;
+  const long t0 = task0 + ((long)blockIdx.x * 4 + (threadIdx.x >> 6)) * kPipeRows;
+  uint16_t* buf = seg[threadIdx.x >> 6];
+  // the wave's rows that need a pair (bit r: task t0 + r)
+  unsigned need = 0;
+#pragma unroll
+  for (int r = 0; r < kPipeRows; ++r) {
+    if (t0 + r < ntask) {
+      long k;
+      pair_row(g, t0 + r, &k);
+      if (needs_pair(ra.plan[k], dbg)) need |= 1u << r;
+    }
+  }
+  if (need == 0) return;  // wave-uniform
+  const int nseg = (g.w + kPairSeg - 1) / kPairSeg;
+  constexpr int UV = kPairSeg / 8 / 64;
+  int r = __builtin_ctz(need), sg = 0;
+  long k;
+  const uint16_t* row = pair_row(g, t0 + r, &k);
+  v4u v[UV];
+  auto issue = [&](const uint16_t* rw, int s0) {  // the segment's loads, not waited for
+    const int nv = min(kPairSeg, g.w - s0) >> 3;
+#pragma unroll
+    for (int u = 0; u < UV; ++u) {
+      const int c = u * 64 + lane;
+      v[u] = c < nv ? __builtin_nontemporal_load((const v4u*)(rw + s0) + c) : (v4u){0u, 0u, 0u, 0u};
+    }
+  };
+  issue(row, 0);
+  Pair32 acc = {0u, 0u};
+  int sh = ra.plan[k] - 52;
+  while (true) {
+    const int s0 = sg * kPairSeg, n = min(kPairSeg, g.w - s0), nv = n >> 3;
+#pragma unroll
+    for (int u = 0; u < UV; ++u) {
+      const int c = u * 64 + lane;
+      if (c < nv) ((v4u*)buf)[c] = v[u];
+    }
+    wave_lds_sync();
+    // the next segment: this row's next one, else the first of the next row with a pair
+    int rn = r, sn = sg + 1;
+    if (sn == nseg) {
+      const unsigned rest = need & ~((2u << r) - 1u);
+      rn = rest ? __builtin_ctz(rest) : kPipeRows;
+      sn = 0;
+    }
+    long kn = k;
+    const uint16_t* rown = row;
+    if (rn < kPipeRows) {
+      if (rn != r) rown = pair_row(g, t0 + rn, &kn);
+      issue(rown, sn * kPairSeg);
+    }
+    const int L = (n + 63) >> 6;
+    const int j0 = min(lane * L, n), j1 = min(j0 + L, n);
+    Pair32 p;
+    if ((L & 7) == 0 && (j1 - j0) == L) {
+      const uint32_t u = 1u << sh;
+      uint32_t v0 = 0u, v1 = u;
+      for (int c = j0 >> 3; c < (j0 + L) >> 3; ++c) {
+        const v4u x = ((const v4u*)buf)[c];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const uint32_t t = fsq_units((x[q >> 1] >> (16 * (q & 1))) & 0xFFFFu);
+          v0 = traj_step(v0, t, sh);
+          v1 = traj_step(v1, t, sh);
+        }
+      }
+      p = Pair32{v0, v1 - u};
+    } else {
+      p = run_pair([&](int j) { return fsq_units(buf[j0 + j]); }, j1 - j0, sh);
+    }
+    for (int off = 1; off < 64; off <<= 1) {
+      Pair32 o;
+      o.a0 = __shfl_down(p.a0, off);
+      o.a1 = __shfl_down(p.a1, off);
+      if ((lane & (2 * off - 1)) == 0) p = then32(p, o, sh);
+    }
+    acc = then32(acc, p, sh);  // meaningful in lane 0
+    if (sg == nseg - 1) {
+      if (lane == 0) {
+        const Pair64 q = widen_pair(acc, ra.r2[k]);
+        ra.pairs[2 * k] = q.a0;
+        ra.pairs[2 * k + 1] = q.a1;
+      }
+      acc = Pair32{0u, 0u};
+    }
+    wave_lds_sync();  // the next segment reuses buf
+    if (rn == kPipeRows) break;
+    if (rn != r) sh = ra.plan[kn] - 52;
+    r = rn;
+    sg = sn;
+    k = kn;
+    row = rown;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // k_walk.
 //
@@ -1477,7 +1596,9 @@ hipError_t launch_plan(const Geometry& g, const RowArrays& ra, unsigned dbg, hip
 hipError_t launch_pairs(const Geometry& g, const RowArrays& ra, unsigned dbg, hipStream_t st,
                         hipEvent_t ev0, hipEvent_t ev1) {
   const long tasks = 2L * g.nframes * g.h;
-  const int rpb = 4;  // rows per block, one wave each
+  // 16-bit rows on 16-byte boundaries, whole 8-sample chunks: the pipelined pass
+  const bool pipe = g.bpc != 8 && g.vec && (g.w & 7) == 0;
+  const int rpb = pipe ? 4 * kPipeRows : 4;  // rows per block
   const long blocks = (tasks + rpb - 1) / rpb;
   // a dispatch's grid, in work-items, must stay below 2^32
   const long kMaxBlocks = (dbg & BEF_DBG_SPLIT_LAUNCH) ? 64 : 1L << 23;
@@ -1485,7 +1606,9 @@ hipError_t launch_pairs(const Geometry& g, const RowArrays& ra, unsigned dbg, hi
     const unsigned nb = (unsigned)(blocks - b0 < kMaxBlocks ? blocks - b0 : kMaxBlocks);
     hipEvent_t e0 = b0 == 0 ? ev0 : nullptr, e1 = b0 + nb >= blocks ? ev1 : nullptr;
     const long t0 = b0 * rpb;
-    if (g.bpc == 8)
+    if (pipe)
+      hipExtLaunchKernelGGL(k_pairs_pipe, dim3(nb), dim3(256), 0, st, e0, e1, 0, g, ra, dbg, t0);
+    else if (g.bpc == 8)
       hipExtLaunchKernelGGL(k_pairs<uint8_t>, dim3(nb), dim3(256), 0, st, e0, e1, 0, g, ra, dbg, t0);
     else
       hipExtLaunchKernelGGL(k_pairs<uint16_t>, dim3(nb), dim3(256), 0, st, e0, e1, 0, g, ra, dbg, t0);
