@@ -208,6 +208,19 @@ def test_past_2_55_8k_noise(api, orc):
     check_batch(api, orc, ref, dis, 16, label="8k noise")
 
 
+@pytest.mark.parametrize("flags", [1, 2, 1 | 16, 2 | 32, 32 | 64])
+def test_8k_noise_debug_paths(api, orc, flags):
+    """8K noise (past 2^55, rows wider than the fast path stages) under
+    wrong plans, no plans, no stretches, no closed forms and split pair
+    dispatches: the general walk's every path gives the CPU's bits."""
+    ref, dis = synth.uniform_planes(8000, 1, 4320, 7680, 7680, 16)
+    old = api.bef_debug_set(flags)
+    try:
+        check_batch(api, orc, ref, dis, 16, label=f"8k noise, debug {flags}")
+    finally:
+        api.bef_debug_set(old)
+
+
 def test_noise_past_2_55_tall(api, orc):
     """A 7680x4608 frame of high ref against low dis: the noise passes 2^55
     on a plane taller than one chunk of rows (4352 rows), so the noise runs
