@@ -131,11 +131,20 @@ class Oracle:
         """ref/dis: (F, h, stride) arrays.  Returns (moments[F,4], psnr[F,2])."""
         assert ref.shape == dis.shape and ref.ndim == 3
         f, h, stride = ref.shape
-        w = stride if w is None else w
-        mom = np.zeros((f, 4), np.float64)
-        ps = np.zeros((f, 2), np.float64)
+        return self.frames_flat(ref, dis, bpc, w=stride if w is None else w, h=h,
+                                stride=stride, pitch=h * stride, nframes=f)
+
+    def frames_flat(self, ref, dis, bpc, *, w, h, stride, pitch, nframes):
+        """Frames laid out in one buffer each (any shape, C-contiguous):
+        frame f starts ``f * pitch`` samples in, rows ``stride`` samples
+        apart.  Returns (moments[F,4], psnr[F,2])."""
+        assert ref.dtype == dis.dtype and ref.size == dis.size
+        need = (nframes - 1) * pitch + (h - 1) * stride + w
+        assert nframes >= 1 and ref.size >= need, (ref.size, need)
+        mom = np.zeros((nframes, 4), np.float64)
+        ps = np.zeros((nframes, 2), np.float64)
         dp = ctypes.POINTER(ctypes.c_double)
         self._check(self.lib.oracle_frames(
-            self._ptr(ref), self._ptr(dis), w, h, stride, h * stride, f, bpc,
+            self._ptr(ref), self._ptr(dis), w, h, stride, pitch, nframes, bpc,
             mom.ctypes.data_as(dp), ps.ctypes.data_as(dp)), "oracle_frames")
         return mom, ps

@@ -257,6 +257,10 @@ int oracle_psnr_noise(const void *ref, const void *dis, int w, int h,
     return 0;
 }
 
+/* Batch helper: the extractors run once per frame (ADR-1497, Context;
+ * ADR-1499, Context), so a batch is the frames one after another, frame f
+ * starting f * frame_pitch samples after the first, each through the
+ * single-frame functions above. */
 int oracle_frames(const void *ref, const void *dis, int w, int h,
                   ptrdiff_t stride, ptrdiff_t frame_pitch, int nframes,
                   int bpc, double *moments, double *psnr)
@@ -264,8 +268,17 @@ int oracle_frames(const void *ref, const void *dis, int w, int h,
     if (nframes <= 0 || frame_pitch < 0) return -EINVAL_;
     const size_t bytes = bpc == 8 ? 1 : 2;
     for (int f = 0; f < nframes; f++) {
-        const char *r = (const char *)ref + (size_t)f * frame_pitch * bytes;
-        const char *d = (const char *)dis + (size_t)f * frame_pitch * bytes;
+#if ORACLE_MUTANT == 13
+        /* mutant: the pitch taken as bytes (not scaled by the sample size) */
+        const size_t off = (size_t)f * frame_pitch + 0 * bytes;
+#elif ORACLE_MUTANT == 14
+        /* mutant: frames assumed packed, h * stride samples apart */
+        const size_t off = (size_t)f * (size_t)h * (size_t)stride * bytes;
+#else
+        const size_t off = (size_t)f * frame_pitch * bytes;
+#endif
+        const char *r = (const char *)ref + off;
+        const char *d = (const char *)dis + off;
         int rc = 0;
         if (moments) rc = oracle_moment_frame(r, d, w, h, stride, bpc,
                                               moments + 4 * (size_t)f);

@@ -259,6 +259,79 @@ def check_boundary_frames(orc):
         assert to_units(n2, 16, 2) == g["psnr"], (kind, n2)
 
 
+def _expected_frame(ref, dis, bpc):
+    """The four moments and [noise, mse] of one (h, w) frame from the
+    integer checkers: each output is the CPU's accumulator in units (exact
+    below 2^53, the rounded fold past it) divided once by N * s^k."""
+    s = 1 << (bpc - 8)
+    n = ref.shape[0] * ref.shape[1]
+    r1, r2, _ = checkers.moment_units(ref)
+    d1, d2, _ = checkers.moment_units(dis)
+    dc, _ = checkers.psnr_units(ref, dis)
+    return ([float(Fraction(r1, n * s)), float(Fraction(d1, n * s)),
+             float(Fraction(r2, n * s * s)), float(Fraction(d2, n * s * s))],
+            [float(Fraction(dc, s * s)), float(Fraction(dc, s * s * n))])
+
+
+def _batch_layout(frames, stride, gap, top):
+    """Frames (F, h, w) into one flat buffer: rows ``stride`` samples apart,
+    frames ``h * stride + gap`` apart; padding and gaps hold ``top``."""
+    f, h, w = frames.shape
+    pitch = h * stride + gap
+    buf = np.full((f - 1) * pitch + h * stride, top, dtype=frames.dtype)
+    for k in range(f):
+        v = buf[k * pitch:k * pitch + h * stride].reshape(h, stride)
+        v[:, :w] = frames[k]
+    return buf, pitch
+
+
+def check_frames_batch(orc):
+    """The batch helper: frame f of a batch starts f * frame_pitch samples
+    after the first (the extractors run once per frame: ADR-1497, Context;
+    ADR-1499, Context).  Batches of 8-, 12- and 16-bit frames with padded
+    rows and a gap between frames (both holding the container's top value)
+    give, frame by frame, the values of the integer checkers and of the
+    single-frame calls; so do three 16-bit 3840x2160 frames past 2^53."""
+    rng = np.random.Generator(np.random.PCG64(2024))
+    for bpc, (w, h, pad, gap, nf) in ((8, (45, 7, 3, 29, 4)),
+                                      (12, (64, 9, 8, 77, 3)),
+                                      (16, (33, 5, 5, 123, 5))):
+        dt = np.uint8 if bpc == 8 else np.uint16
+        top = np.iinfo(dt).max
+        rf = rng.integers(0, 1 << bpc, size=(nf, h, w)).astype(dt)
+        df = rng.integers(0, 1 << bpc, size=(nf, h, w)).astype(dt)
+        rb, pitch = _batch_layout(rf, w + pad, gap, top)
+        db, _ = _batch_layout(df, w + pad, gap, top)
+        mom, ps = orc.frames_flat(rb, db, bpc, w=w, h=h, stride=w + pad, pitch=pitch,
+                                  nframes=nf)
+        for k in range(nf):
+            em, ep = _expected_frame(rf[k], df[k], bpc)
+            assert mom[k].tolist() == em, (bpc, k, mom[k], em)
+            assert ps[k].tolist() == ep, (bpc, k, ps[k], ep)
+            assert mom[k].tolist() == orc.moment_frame(rf[k], df[k], bpc)
+            assert ps[k].tolist() == orc.psnr_noise(rf[k], df[k], bpc)
+    # past 2^53: full range, half range, and the full-range frame swapped
+    r4, d4 = big_frame(4)
+    r5, d5 = big_frame(5)
+    rf = np.stack([r4, r5, d4])
+    df = np.stack([d4, d5, r4])
+    rb, pitch = _batch_layout(rf, 3840 + 16, 1000, 0xFFFF)
+    db, _ = _batch_layout(df, 3840 + 16, 1000, 0xFFFF)
+    mom, ps = orc.frames_flat(rb, db, 16, w=3840, h=2160, stride=3840 + 16, pitch=pitch,
+                              nframes=3)
+    (r41, r42, _), (d41, d42, _), (dc4, _) = big_frame_expect(4)
+    (r51, r52, _), (d51, d52, _), (dc5, _) = big_frame_expect(5)
+    n = 3840 * 2160
+    want = [([r41, d41, r42, d42], dc4), ([r51, d51, r52, d52], dc5),
+            ([d41, r41, d42, r42], dc4)]
+    for k, (u, dc) in enumerate(want):
+        em = [float(Fraction(u[0], n * 256)), float(Fraction(u[1], n * 256)),
+              float(Fraction(u[2], n * 65536)), float(Fraction(u[3], n * 65536))]
+        assert mom[k].tolist() == em, (k, mom[k], em)
+        assert ps[k].tolist() == [float(Fraction(dc, 65536)),
+                                  float(Fraction(dc, 65536 * n))], (k, ps[k])
+
+
 def check_bad_args(orc):
     """Invalid geometry or bit depth is rejected, not computed."""
     import ctypes
@@ -286,5 +359,6 @@ ALL_CHECKS = [
     check_swap_symmetry,
     check_past_2_53,
     check_boundary_frames,
+    check_frames_batch,
     check_bad_args,
 ]

@@ -5,7 +5,8 @@ ORACLE_MUTANT=k; the real oracle is never modified.  The list (see the
 mutant switches in oracle.c): square in double, float accumulator, last
 column dropped, stride ignored, ref/dis swapped, PSNR rows reversed, PSNR
 terms added straight into the frame sum, first moment halved, noise square
-in double, MSE divided by the width, scaler off by one bit.
+in double, MSE divided by the width, scaler off by one bit, a batch's
+frame pitch taken as bytes, a batch's frames assumed packed.
 """
 import os
 
@@ -14,7 +15,7 @@ import pytest
 import oracle
 import oracle_checks
 
-MUTANTS = [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 12]
+MUTANTS = [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 12, 13, 14]
 
 
 @pytest.mark.parametrize("mutant", MUTANTS)
