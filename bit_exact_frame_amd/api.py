@@ -104,6 +104,21 @@ def _geom(t, bpc, w):
     return f, h, stride, (stride if w is None else int(w))
 
 
+def _pair(ref, dis, bpc, w):
+    """Geometry of a (ref, dis) pair of device planes: both must pass the
+    same checks and have the same shape on the same device (the library
+    reads dis with ref's geometry)."""
+    geom = _geom(ref, bpc, w)
+    _geom(dis, bpc, w)
+    if tuple(dis.shape) != tuple(ref.shape):
+        raise BefError(f"ref and dis shapes differ: {tuple(ref.shape)} and {tuple(dis.shape)}")
+    if dis.device != ref.device:
+        raise BefError(f"ref on {ref.device}, dis on {dis.device}")
+    if not 1 <= geom[3] <= geom[2]:
+        raise BefError(f"w={geom[3]} outside 1..{geom[2]} (the planes' last dimension)")
+    return geom
+
+
 def _stream_ptr(stream):
     if stream is None:
         import torch
@@ -115,7 +130,7 @@ def _stream_ptr(stream):
 
 def moment_frame(ref, dis, bpc: int, w: int | None = None):
     """Four moments of one frame: [ref_1st, dis_1st, ref_2nd, dis_2nd]."""
-    _, h, stride, w = _geom(ref, bpc, w)
+    _, h, stride, w = _pair(ref, dis, bpc, w)
     out = (ctypes.c_double * 4)()
     _check(_lib.moment_frame(ref.data_ptr(), dis.data_ptr(), w, h, stride, bpc, out),
            "moment_frame")
@@ -124,7 +139,7 @@ def moment_frame(ref, dis, bpc: int, w: int | None = None):
 
 def psnr_noise(ref, dis, bpc: int, w: int | None = None):
     """[noise, mse] of one frame."""
-    _, h, stride, w = _geom(ref, bpc, w)
+    _, h, stride, w = _pair(ref, dis, bpc, w)
     out = (ctypes.c_double * 2)()
     _check(_lib.psnr_noise(ref.data_ptr(), dis.data_ptr(), w, h, stride, bpc, out),
            "psnr_noise")
@@ -133,7 +148,7 @@ def psnr_noise(ref, dis, bpc: int, w: int | None = None):
 
 def bef_frames(ref, dis, bpc: int, w: int | None = None, stream=None):
     """Batch: returns (moments float64[F,4], psnr float64[F,2])."""
-    f, h, stride, w = _geom(ref, bpc, w)
+    f, h, stride, w = _pair(ref, dis, bpc, w)
     mom = np.zeros((f, 4), np.float64)
     ps = np.zeros((f, 2), np.float64)
     _check(_lib.bef_frames(ref.data_ptr(), dis.data_ptr(), w, h, stride, h * stride, f,
@@ -178,7 +193,7 @@ def bef_frames_host(ref, dis, bpc: int, w: int | None = None, device: int = 0):
 def bef_frames_async(ref, dis, bpc: int, out, w: int | None = None, stream=None):
     """Batch into the float64 device tensor ``out`` [F,6]; no sync."""
     import torch
-    f, h, stride, w = _geom(ref, bpc, w)
+    f, h, stride, w = _pair(ref, dis, bpc, w)
     if out.dtype != torch.float64 or not out.is_cuda or out.numel() < 6 * f:
         raise BefError("out must be a float64 device tensor of at least 6*F")
     _check(_lib.bef_frames_async(ref.data_ptr(), dis.data_ptr(), w, h, stride, h * stride,
@@ -188,7 +203,7 @@ def bef_frames_async(ref, dis, bpc: int, out, w: int | None = None, stream=None)
 
 def bef_frames_units(ref, dis, bpc: int, w: int | None = None, stream=None):
     """Batch diagnostics: uint64[F,8] integer sums in units."""
-    f, h, stride, w = _geom(ref, bpc, w)
+    f, h, stride, w = _pair(ref, dis, bpc, w)
     units = np.zeros((f, 8), np.uint64)
     _check(_lib.bef_frames_units(ref.data_ptr(), dis.data_ptr(), w, h, stride, h * stride,
                                  f, bpc, _stream_ptr(stream), units.ctypes.data_as(_u64p)),
@@ -200,7 +215,7 @@ def bef_read_ceiling(ref, dis, out, w: int | None = None, stream=None):
     """Diagnostic read-only pass over 16-bit planes (the row pass's memory
     side); ``out`` is a uint32 device tensor of at least F*h words."""
     import torch
-    f, h, stride, w = _geom(ref, 16, w)
+    f, h, stride, w = _pair(ref, dis, 16, w)
     if out.dtype != torch.int32 and out.dtype != torch.uint32:
         raise BefError("out must be a 32-bit integer device tensor")
     if not out.is_cuda or out.numel() < f * h:
