@@ -39,10 +39,11 @@ _lib.moment_frame.argtypes = [_vp, _vp, _i, _i, _pd, _i, _dp]
 _lib.psnr_noise.argtypes = [_vp, _vp, _i, _i, _pd, _i, _dp]
 _lib.bef_frames.argtypes = [_vp, _vp, _i, _i, _pd, _pd, _i, _i, _vp, _dp, _dp]
 _lib.bef_frames_async.argtypes = [_vp, _vp, _i, _i, _pd, _pd, _i, _i, _vp, _vp]
+_lib.bef_frames_noalloc.argtypes = [_vp, _vp, _i, _i, _pd, _pd, _i, _i, _vp, _vp]
 _lib.bef_frames_units.argtypes = [_vp, _vp, _i, _i, _pd, _pd, _i, _i, _vp, _u64p]
 _lib.bef_read_ceiling.argtypes = [_vp, _vp, _i, _i, _pd, _pd, _i, _vp, _vp]
 _lib.bef_frames_host.argtypes = [_vp, _vp, _i, _i, _pd, _pd, _i, _i, _i, _dp, _dp]
-for _n in ("moment_frame", "psnr_noise", "bef_frames", "bef_frames_async",
+for _n in ("moment_frame", "psnr_noise", "bef_frames", "bef_frames_async", "bef_frames_noalloc",
            "bef_frames_units", "bef_read_ceiling", "bef_frames_host"):
     getattr(_lib, _n).restype = _i
 _lib.bef_last_error.restype = ctypes.c_char_p
@@ -199,6 +200,18 @@ def bef_frames_async(ref, dis, bpc: int, out, w: int | None = None, stream=None)
     _check(_lib.bef_frames_async(ref.data_ptr(), dis.data_ptr(), w, h, stride, h * stride,
                                  f, bpc, _stream_ptr(stream), ctypes.c_void_p(out.data_ptr())),
            "bef_frames_async")
+
+
+def bef_frames_noalloc(ref, dis, bpc: int, out, w: int | None = None, stream=None):
+    """As bef_frames_async, with the library's static scratch: the call
+    allocates nothing.  ``out``: float64 device tensor [F,6]."""
+    import torch
+    f, h, stride, w = _pair(ref, dis, bpc, w)
+    if out.dtype != torch.float64 or not out.is_cuda or out.numel() < 6 * f:
+        raise BefError("out must be a float64 device tensor of at least 6*F")
+    _check(_lib.bef_frames_noalloc(ref.data_ptr(), dis.data_ptr(), w, h, stride, h * stride,
+                                   f, bpc, _stream_ptr(stream), ctypes.c_void_p(out.data_ptr())),
+           "bef_frames_noalloc")
 
 
 def bef_frames_units(ref, dis, bpc: int, w: int | None = None, stream=None):

@@ -11,7 +11,6 @@
 
 #include <algorithm>
 #include <mutex>
-#include <string>
 #include <vector>
 
 #include "bef_internal.h"
@@ -19,10 +18,19 @@
 
 using namespace bef;
 
+// Scratch of bef_frames_noalloc: a device array of fixed size in the
+// library's code object, one copy per GPU, held until the process ends.
+// Host code never uses the name itself (on the host it is only a stand-in
+// symbol): each device's address comes from hipGetSymbolAddress, taken
+// once per device with that device current, and goes to the kernels as an
+// argument, as the arena's base does.
+static constexpr size_t kStaticScratchBytes = 16ull << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
 namespace {
 
 std::mutex g_mu;
-thread_local std::string g_err;
+thread_local char g_err[512];
 unsigned g_dbg = 0;
 
 constexpr int kMaxDev = 64;
@@ -39,6 +47,9 @@ struct Arena {
 };
 Arena g_arena[kMaxDev];
 
+// Per-device address of the static scratch (below), taken once per device.
+void* g_static_ptr[kMaxDev] = {};
+
 // Kernel timing (events recorded on the launch stream).
 struct EvPair {
   int kernel;
@@ -51,14 +62,14 @@ double g_ms[5] = {0, 0, 0, 0, 0};
 long g_n[5] = {0, 0, 0, 0, 0};
 
 int fail(int rc, const char* fmt, ...) {
-  char buf[512];
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(buf, sizeof buf, fmt, ap);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
   va_end(ap);
-  g_err = buf;
   return rc;
 }
+
+void clear_err() { g_err[0] = 0; }
 
 #define BEF_HIP(call)                                                              \
   do {                                                                             \
@@ -228,8 +239,9 @@ struct Call {
   bool need_pairs;
 };
 
-int prepare(Call& c, const void* ref, const void* dis, int w, int h, ptrdiff_t stride,
-            ptrdiff_t pitch, int nframes, int bpc) {
+// Arguments, device and geometry of a call; allocates nothing.
+int setup(Call& c, const void* ref, const void* dis, int w, int h, ptrdiff_t stride,
+          ptrdiff_t pitch, int nframes, int bpc) {
   int rc = validate(ref, dis, w, h, stride, pitch, nframes, bpc);
   if (rc) return rc;
   int dev2 = 0;
@@ -260,8 +272,13 @@ int prepare(Call& c, const void* ref, const void* dis, int w, int h, ptrdiff_t s
   c.need_pairs = g.may_round && (maxsum >= (1ull << 55) || g_dbg != 0);
   g.planned = c.need_pairs;
   c.L = layout(nframes, h);
-  if ((rc = ensure(c.dev, c.L.total, (size_t)nframes * 8 * 8 + (size_t)nframes * 6 * 8 + 256))) return rc;
-  char* base = (char*)g_arena[c.dev].base;
+  return 0;
+}
+
+// The call's row arrays, units and results inside scratch memory at base
+// (c.L.total bytes, 256-byte aligned).  Every element a kernel reads is
+// written earlier in the same call, so the memory need not be cleared.
+void bind(Call& c, char* base) {
   c.ra.r1 = (uint32_t*)(base + c.L.r1);
   c.ra.r2 = (uint64_t*)(base + c.L.r2);
   c.ra.rn = (uint64_t*)(base + c.L.rn);
@@ -271,6 +288,16 @@ int prepare(Call& c, const void* ref, const void* dis, int w, int h, ptrdiff_t s
   c.ra.psum = (uint64_t*)(base + c.L.psum);
   c.d_results = (double*)(base + c.L.results);
   c.d_units = (uint64_t*)(base + c.L.units);
+}
+
+// setup, then the library's arena (grown on demand) as scratch.
+int prepare(Call& c, const void* ref, const void* dis, int w, int h, ptrdiff_t stride,
+            ptrdiff_t pitch, int nframes, int bpc) {
+  int rc = setup(c, ref, dis, w, h, stride, pitch, nframes, bpc);
+  if (rc) return rc;
+  if ((rc = ensure(c.dev, c.L.total, (size_t)nframes * 8 * 8 + (size_t)nframes * 6 * 8 + 256)))
+    return rc;
+  bind(c, (char*)g_arena[c.dev].base);
   return 0;
 }
 
@@ -284,8 +311,17 @@ int check_stream(const Call& c, hipStream_t st) {
   return 0;
 }
 
-int enqueue(const Call& c, hipStream_t st, double* d_results) {
+int enqueue(const Call& c, hipStream_t st, double* d_results, bool may_time = true) {
   const unsigned dbg = g_dbg;
+  if (!may_time) {  // no event is created or recorded
+    BEF_HIP(launch_rows(c.g, c.ra, st, nullptr, nullptr));
+    if (c.need_pairs) {
+      BEF_HIP(launch_plan(c.g, c.ra, dbg, st, nullptr, nullptr));
+      BEF_HIP(launch_pairs(c.g, c.ra, dbg, st, nullptr, nullptr));
+    }
+    BEF_HIP(launch_walk(c.g, c.ra, d_results, c.d_units, dbg, st, nullptr, nullptr));
+    return 0;
+  }
   BEF_HIP(timed(0, [&](hipEvent_t a, hipEvent_t b) { return launch_rows(c.g, c.ra, st, a, b); }));
   if (c.need_pairs) {
     BEF_HIP(timed(1, [&](hipEvent_t a, hipEvent_t b) {
@@ -442,7 +478,7 @@ int bef_frames(const void* ref, const void* dis, int w, int h, ptrdiff_t stride,
                ptrdiff_t frame_pitch, int nframes, int bpc, void* stream, double* moments,
                double* psnr) {
   std::lock_guard<std::mutex> lk(g_mu);
-  g_err.clear();
+  clear_err();
   DevGuard dg;
   return run_sync(ref, dis, w, h, stride, frame_pitch, nframes, bpc, stream, moments, psnr,
                   nullptr);
@@ -451,7 +487,7 @@ int bef_frames(const void* ref, const void* dis, int w, int h, ptrdiff_t stride,
 int bef_frames_units(const void* ref, const void* dis, int w, int h, ptrdiff_t stride,
                      ptrdiff_t frame_pitch, int nframes, int bpc, void* stream, uint64_t* units) {
   std::lock_guard<std::mutex> lk(g_mu);
-  g_err.clear();
+  clear_err();
   if (!units) return fail(-EINVAL, "NULL units");
   DevGuard dg;
   return run_sync(ref, dis, w, h, stride, frame_pitch, nframes, bpc, stream, nullptr, nullptr,
@@ -462,7 +498,7 @@ int bef_frames_async(const void* ref, const void* dis, int w, int h, ptrdiff_t s
                      ptrdiff_t frame_pitch, int nframes, int bpc, void* stream,
                      double* dev_results) {
   std::lock_guard<std::mutex> lk(g_mu);
-  g_err.clear();
+  clear_err();
   if (!dev_results) return fail(-EINVAL, "NULL dev_results");
   DevGuard dg;
   Call c;
@@ -471,10 +507,34 @@ int bef_frames_async(const void* ref, const void* dis, int w, int h, ptrdiff_t s
   return enqueue(c, (hipStream_t)stream, dev_results);
 }
 
+int bef_frames_noalloc(const void* ref, const void* dis, int w, int h, ptrdiff_t stride,
+                       ptrdiff_t frame_pitch, int nframes, int bpc, void* stream,
+                       double* dev_results) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  clear_err();
+  if (!dev_results) return fail(-EINVAL, "NULL dev_results");
+  DevGuard dg;
+  Call c;
+  int rc = setup(c, ref, dis, w, h, stride, frame_pitch, nframes, bpc);
+  if (rc || (rc = check_stream(c, (hipStream_t)stream))) return rc;
+  if (c.L.total > kStaticScratchBytes)
+    return fail(-EINVAL, "%d frames of %d rows need %zu bytes of scratch; the static scratch "
+                "holds %zu", nframes, h, c.L.total, kStaticScratchBytes);
+  void*& ptr = g_static_ptr[c.dev];
+  if (!ptr) {  // first call on this device (it is current: setup selected it)
+    void* p = nullptr;
+    BEF_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return fail(-EIO, "hipGetSymbolAddress gave no address for the static scratch");
+    ptr = p;
+  }
+  bind(c, (char*)ptr);
+  return enqueue(c, (hipStream_t)stream, dev_results, false);
+}
+
 int bef_read_ceiling(const void* ref, const void* dis, int w, int h, ptrdiff_t stride,
                      ptrdiff_t frame_pitch, int nframes, void* stream, uint32_t* dev_out) {
   std::lock_guard<std::mutex> lk(g_mu);
-  g_err.clear();
+  clear_err();
   if (!dev_out) return fail(-EINVAL, "NULL dev_out");
   DevGuard dg;
   Call c;
@@ -493,7 +553,7 @@ int bef_frames_host(const void* ref, const void* dis, int w, int h, ptrdiff_t st
                     ptrdiff_t frame_pitch, int nframes, int bpc, int device, double* moments,
                     double* psnr) {
   std::lock_guard<std::mutex> lk(g_mu);
-  g_err.clear();
+  clear_err();
   DevGuard dg;
   return run_host(ref, dis, w, h, stride, frame_pitch, nframes, bpc, device, moments, psnr);
 }
@@ -510,7 +570,7 @@ int psnr_noise(const void* ref, const void* dis, int w, int h, ptrdiff_t stride,
   return bef_frames(ref, dis, w, h, stride, 0, 1, bpc, nullptr, nullptr, out);
 }
 
-const char* bef_last_error(void) { return g_err.c_str(); }
+const char* bef_last_error(void) { return g_err; }
 
 unsigned bef_debug_set(unsigned flags) {
   std::lock_guard<std::mutex> lk(g_mu);

@@ -89,6 +89,23 @@ int bef_frames_async(const void *ref, const void *dis, int w, int h,
                      ptrdiff_t stride, ptrdiff_t frame_pitch, int nframes,
                      int bpc, void *stream, double *dev_results);
 
+/* For callers that cannot allocate (code under HIP graph capture, serving
+ * loops, harnesses that forbid hipMalloc): bef_frames_async with the
+ * library's static scratch instead of its arena.  Same arguments, limits,
+ * results (DEVICE dev_results, [nframes][6] doubles, caller-owned) and
+ * asynchrony.  The call allocates nothing (no hipMalloc, hipFree, pinned
+ * staging or timing events): its kernels use a fixed device array of
+ * 16 MiB per GPU, part of the library, held until the process ends.  A
+ * batch whose scratch would exceed it (about 74 bytes per row of each
+ * frame plus 144 bytes per frame: e.g. 100 frames of 2160 rows fit) is
+ * -EINVAL, with the sizes in bef_last_error().  Every call on a GPU shares
+ * that GPU's array: calls whose GPU work overlaps on one GPU (different
+ * streams) race; enqueue them on one stream.  The array keeps the last
+ * call's contents; no call depends on them. */
+int bef_frames_noalloc(const void *ref, const void *dis, int w, int h,
+                       ptrdiff_t stride, ptrdiff_t frame_pitch, int nframes,
+                       int bpc, void *stream, double *dev_results);
+
 /* As bef_frames, for frames in HOST memory (ref, dis: host pointers, same
  * layout and limits), on device `device`, synchronously.  The library
  * streams the frames through two device slots of up to 64 MiB per plane:
