@@ -11,13 +11,19 @@ frames from HBM.  Prints ONE JSON line.
 value          frames per second over the K timed steps that follow the W
                warmup steps (torch events on the launch stream, bracketed by
                synchronisations; no per-kernel events inside)
+config         the run's figures; for the 16-bit 3840x2160 full-range
+               workload (the default) also config.halfrange, the half-range
+               workload (8 frames a step) measured the same way in the same
+               run
 roofline       the row-sum kernel (the dominant one): algorithmic bytes per
                launch (2 planes x w x h x 2 B x frames) over its average
                duration, measured over a second pass of K steps with HIP
                events that each dispatch records on the launch stream;
                peak = MI355X HBM3E 8 TB/s
-cpu_baseline   the CPU oracle (plain loops), timed on this host's cores, one
-               frame per thread, on a bounded sample of the same frames
+cpu_baseline   the CPU oracle (plain loops) on host copies of the same frames:
+               one core (frames one after another, warm) and all of this
+               process's CPUs (one frame per thread), with nproc and the
+               CPU model
 """
 from __future__ import annotations
 
@@ -68,33 +74,9 @@ def recorded_traffic(workload_name):
     return int(rec["hbm_bytes_per_launch"])
 
 
-def cpu_baseline(ref, dis, bpc, w, budget_s=20.0, max_threads=16):
-    """Time the oracle over host copies of the batch, one frame per thread."""
-    import concurrent.futures as cf
-
-    import numpy as np
-
-    import oracle
-
-    orc = oracle.Oracle()
-    t0 = time.perf_counter()
-    orc.frames(ref[:1], dis[:1], bpc, w=w)
-    one = time.perf_counter() - t0
-    threads = max(1, min(max_threads, os.cpu_count() or 1))
-    frames = ref.shape[0]
-    # enough frames for about budget_s of CPU work in total, at least one
-    # pass over the batch
-    n = max(frames, int(math.ceil(budget_s / max(one, 1e-6))))
-    n = int(math.ceil(n / threads) * threads)
-    idx = [k % frames for k in range(n)]
-
-    def work(k):
-        return orc.frames(ref[k:k + 1], dis[k:k + 1], bpc, w=w)
-
-    t0 = time.perf_counter()
-    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
-        list(ex.map(work, idx))
-    dt = time.perf_counter() - t0
+def cpu_facts():
+    """Host CPU count (nproc), the CPUs this process may run on, and the
+    model string /proc/cpuinfo gives."""
     model = None
     try:
         with open("/proc/cpuinfo") as f:
@@ -102,10 +84,143 @@ def cpu_baseline(ref, dis, bpc, w, budget_s=20.0, max_threads=16):
                          None)
     except OSError:
         pass
-    return {"value": n / dt, "unit": "frames/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} frames of the batch ({frames} distinct), one frame per thread, "
-                      f"{threads} threads, {dt:.1f} s wall; one frame alone took {one * 1e3:.1f} ms",
-            "one_thread_value": round(1.0 / one, 2), "cpu_model": model}
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 1
+    return os.cpu_count() or 1, usable, model
+
+
+def cpu_baseline(ref, dis, bpc, w, bytes_per_frame, budget_s=20.0, one_core_frames=8):
+    """The oracle (plain loops) on host copies of the batch: (1) one core,
+    frames one after another, warm, over ``one_core_frames`` frames; (2) all
+    cores, one frame per thread (each frame's loop stays serial) with as many
+    threads as this process has CPUs, over about ``budget_s`` of CPU work."""
+    import concurrent.futures as cf
+
+    import oracle
+
+    orc = oracle.Oracle()
+    nproc, usable, model = cpu_facts()
+    frames = ref.shape[0]
+
+    def one(k):
+        k %= frames
+        return orc.frames(ref[k:k + 1], dis[k:k + 1], bpc, w=w)
+
+    one(0)  # warm: library loaded, pages touched
+    t0 = time.perf_counter()
+    for k in range(one_core_frames):
+        one(k)
+    t1 = time.perf_counter() - t0
+    per_frame = t1 / one_core_frames
+    threads = usable
+    n = max(frames, int(math.ceil(budget_s / max(per_frame, 1e-6))))
+    n = int(math.ceil(n / threads) * threads)
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(one, range(n)))
+    dt = time.perf_counter() - t0
+    fps_all = n / dt
+    fps_one = one_core_frames / t1
+    return {"value": round(fps_all, 2), "unit": "frames/s", "cores": threads, "kind": "oracle",
+            "sample": f"all cores: {n} frames of the batch ({frames} distinct), one frame per "
+                      f"thread, {threads} threads, {dt:.2f} s wall; one core: {one_core_frames} "
+                      f"frames one after another after a warm-up frame, {t1:.2f} s",
+            "GBps": round(fps_all * bytes_per_frame / 1e9, 3),
+            "one_core_value": round(fps_one, 2),
+            "one_core_GBps": round(fps_one * bytes_per_frame / 1e9, 3),
+            "one_core_ms_per_frame": round(1e3 * per_frame, 2),
+            "nproc": nproc, "usable_cpus": usable, "cpu_model": model}
+
+
+def measure(api, key, steps, warmup, ring=0, ceiling=True):
+    """Whole-path throughput of workload ``key``: batches rotate through a
+    ring of device copies of at least 1 GB, W warm-up steps (plus settle
+    steps until the warm-up has lasted 50 ms), K timed steps bracketed by
+    events on the launch stream, then K more steps with per-kernel events
+    for the kernels' averages.  Returns a dict of figures and the frames."""
+    import numpy as np
+    import torch
+
+    from bit_exact_frame_amd import synth
+
+    wl = synth.WORKLOADS[key]
+    ref_h, dis_h = synth.make_frames(key)
+    F = ref_h.shape[0]
+    batch_bytes = F * wl.bytes_per_frame
+    ring = ring or max(2, int(math.ceil(1e9 / batch_bytes)))
+    refs = [torch.from_numpy(ref_h).cuda() for _ in range(ring)]
+    diss = [torch.from_numpy(dis_h).cuda() for _ in range(ring)]
+    out = torch.empty((F, 6), dtype=torch.float64, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    # correctness of this very configuration, outside the timed region
+    api.bef_debug_set(0)
+    mom, ps = api.bef_frames(refs[0], diss[0], wl.bpc, w=wl.w)
+
+    def run(n):
+        for k in range(n):
+            api.bef_frames_async(refs[k % ring], diss[k % ring], wl.bpc, out, w=wl.w,
+                                 stream=stream)
+
+    # The GPU's clocks take about 20-25 ms of sustained load to settle (the
+    # row kernel runs up to 25% slower before that).
+    t_warm = time.perf_counter()
+    run(warmup)
+    torch.cuda.synchronize()
+    settle = 0
+    while time.perf_counter() - t_warm < 0.05:
+        run(20)
+        torch.cuda.synchronize()
+        settle += 20
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    run(steps)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    clean_ms = ev0.elapsed_time(ev1)
+    got = out.cpu().numpy()
+    assert (got[:, :4].view(np.uint64) == mom.view(np.uint64)).all()
+    assert (got[:, 4:].view(np.uint64) == ps.view(np.uint64)).all()
+
+    # the same K steps again, each kernel timed by HIP events that its own
+    # dispatch records on the launch stream
+    api.bef_timing_enable(True)
+    api.bef_timing_reset()
+    ev0.record(stream)
+    run(steps)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    api.bef_timing_enable(False)
+    total_ms = ev0.elapsed_time(ev1)
+    kern = {}
+    for name in ("rows", "plan", "pairs", "walk"):
+        ms, n = api.bef_timing_read(name)
+        if n:
+            kern[name] = 1e3 * ms / n  # microseconds per launch
+
+    ceil_gbps = None
+    if ceiling and wl.bpc != 8:
+        cout = torch.empty(F * wl.h, dtype=torch.int32, device="cuda")
+        for k in range(10):
+            api.bef_read_ceiling(refs[k % ring], diss[k % ring], cout, w=wl.w, stream=stream)
+        torch.cuda.synchronize()
+        api.bef_timing_enable(True)
+        api.bef_timing_reset()
+        for k in range(max(20, steps // 2)):
+            api.bef_read_ceiling(refs[k % ring], diss[k % ring], cout, w=wl.w, stream=stream)
+        torch.cuda.synchronize()
+        api.bef_timing_enable(False)
+        c_ms, c_n = api.bef_timing_read("ceiling")
+        ceil_gbps = batch_bytes / (c_ms / c_n / 1e3) / 1e9
+    del refs, diss
+    gbps = batch_bytes * steps / (clean_ms / 1e3) / 1e9
+    return {"wl": wl, "F": F, "ring": ring, "settle": settle, "clean_ms": clean_ms,
+            "total_ms": total_ms, "kern": kern, "ceiling": ceil_gbps, "batch_bytes": batch_bytes,
+            "fps": F * steps / (clean_ms / 1e3), "gbps": gbps, "ref_h": ref_h, "dis_h": dis_h}
 
 
 def main():
@@ -118,6 +233,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--no-host", action="store_true",
                     help="skip the host-memory pipeline figure (PCIe-inclusive context)")
+    ap.add_argument("--no-half", action="store_true",
+                    help="skip the 16-bit 3840x2160 half-range leg reported under config")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="only run device-to-device copies of MIB MiB (HBM counter "
                          "calibration) and exit")
@@ -140,89 +257,15 @@ def main():
               "communication, so one GPU's throughput is the figure.", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
-    from bit_exact_frame_amd import api, synth
+    from bit_exact_frame_amd import api
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
-    wl = synth.WORKLOADS[args.workload]
-    ref_h, dis_h = synth.make_frames(args.workload)
-    F = ref_h.shape[0]
-    batch_bytes = F * wl.bytes_per_frame
-    ring = args.ring or max(2, int(math.ceil(4 * 256e6 / batch_bytes)))
-    refs = [torch.from_numpy(ref_h).cuda() for _ in range(ring)]
-    diss = [torch.from_numpy(dis_h).cuda() for _ in range(ring)]
-    out = torch.empty((F, 6), dtype=torch.float64, device="cuda")
-    stream = torch.cuda.current_stream()
-
-    # correctness of this very configuration, outside the timed region
-    api.bef_debug_set(0)
-    mom, ps = api.bef_frames(refs[0], diss[0], wl.bpc, w=wl.w)
-
-    def steps(n):
-        for k in range(n):
-            api.bef_frames_async(refs[k % ring], diss[k % ring], wl.bpc, out, w=wl.w,
-                                 stream=stream)
-
-    # The GPU's clocks take about 20-25 ms of sustained load to settle (the
-    # row kernel runs up to 25% slower before that).  After the W warmup
-    # steps, untimed steps continue until the warmup has lasted 50 ms (the
-    # default W alone covers about 45 ms); their count is reported.
-    t_warm = time.perf_counter()
-    steps(args.warmup)
-    torch.cuda.synchronize()
-    settle_steps = 0
-    while time.perf_counter() - t_warm < 0.05:
-        steps(20)
-        torch.cuda.synchronize()
-        settle_steps += 20
-
-    # value: K steps with no per-kernel events
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    steps(args.steps)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    clean_ms = ev0.elapsed_time(ev1)
-
-    # roofline: the same K steps again, each kernel timed by HIP events that
-    # its own dispatch records on the launch stream
-    api.bef_timing_enable(True)
-    api.bef_timing_reset()
-    ev0.record(stream)
-    steps(args.steps)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    api.bef_timing_enable(False)
-    total_ms = ev0.elapsed_time(ev1)
-    rows_ms, rows_n = api.bef_timing_read("rows")
-    walk_ms, walk_n = api.bef_timing_read("walk")
-    # the plan and pair kernels run only where a plane can pass 2^55
-    extra_us = {}
-    for name in ("plan", "pairs"):
-        ms, n = api.bef_timing_read(name)
-        if n:
-            extra_us[f"{name}_avg_us"] = round(1e3 * ms / n, 2)
-
-    # context, outside the timed steps: the row pass's access pattern read
-    # with no arithmetic (the practical ceiling of its memory side)
-    ceiling = None
-    if wl.bpc != 8:
-        cout = torch.empty(F * wl.h, dtype=torch.int32, device="cuda")
-        for k in range(10):
-            api.bef_read_ceiling(refs[k % ring], diss[k % ring], cout, w=wl.w, stream=stream)
-        torch.cuda.synchronize()
-        api.bef_timing_enable(True)
-        api.bef_timing_reset()
-        for k in range(max(20, args.steps // 2)):
-            api.bef_read_ceiling(refs[k % ring], diss[k % ring], cout, w=wl.w, stream=stream)
-        torch.cuda.synchronize()
-        api.bef_timing_enable(False)
-        c_ms, c_n = api.bef_timing_read("ceiling")
-        ceiling = batch_bytes / (c_ms / c_n / 1e3) / 1e9
+    m = measure(api, args.workload, args.steps, args.warmup, ring=args.ring)
+    wl, F, batch_bytes = m["wl"], m["F"], m["batch_bytes"]
+    ref_h, dis_h = m["ref_h"], m["dis_h"]
 
     # context: the same frames from pinned host memory through the library's
     # two-slot upload pipeline (PCIe-inclusive rate; never the value)
@@ -236,48 +279,67 @@ def main():
         host_fps = 3 * F / (time.perf_counter() - t0)
         del rp, dp
 
-    ms_per_step = clean_ms / args.steps
-    fps = F * args.steps / (clean_ms / 1e3)
-    rows_avg_ms = rows_ms / max(rows_n, 1)
-    achieved = batch_bytes / (rows_avg_ms / 1e3) / 1e9
+    # the half-range 16-bit 3840x2160 workload (8 frames a step), measured
+    # the same way in the same run
+    half = None
+    if args.workload == 4 and not args.no_half:
+        h5 = measure(api, 5, args.steps, args.warmup)
+        r5 = h5["kern"].get("rows")
+        half = {"workload": h5["wl"].name, "frames_per_step": h5["F"],
+                "recipe": h5["wl"].recipe, "ring_copies": h5["ring"],
+                "fps": round(h5["fps"], 1),
+                "ms_per_step": round(h5["clean_ms"] / args.steps, 5),
+                "whole_path_GBps": round(h5["gbps"], 1),
+                "whole_path_frac": round(h5["gbps"] / PEAK_HBM_GBS, 4),
+                "rows_avg_us": None if r5 is None else round(r5, 2),
+                "rows_frac": None if r5 is None else
+                round(h5["batch_bytes"] / (r5 / 1e6) / 1e9 / PEAK_HBM_GBS, 4),
+                "walk_avg_us": round(h5["kern"].get("walk", 0.0), 2),
+                "read_ceiling_GBps": None if h5["ceiling"] is None else round(h5["ceiling"], 1),
+                "settle_steps_after_warmup": h5["settle"]}
 
-    got = out.cpu().numpy()
-    assert (got[:, :4].view(np.uint64) == mom.view(np.uint64)).all()
-
+    rows_us = m["kern"]["rows"]
+    achieved = batch_bytes / (rows_us / 1e6) / 1e9
+    ceiling = m["ceiling"]
+    config = {"workload": wl.name, "frames_per_step": F, "w": wl.w, "h": wl.h,
+              "bpc": wl.bpc, "recipe": wl.recipe, "ring_copies": m["ring"],
+              "whole_path_GBps": round(m["gbps"], 1),
+              "whole_path_frac": round(m["gbps"] / PEAK_HBM_GBS, 4),
+              "walk_avg_us": round(m["kern"].get("walk", 0.0), 2)}
+    for name in ("plan", "pairs"):  # only where a plane can pass 2^55
+        if name in m["kern"]:
+            config[f"{name}_avg_us"] = round(m["kern"][name], 2)
+    config.update({
+        "read_ceiling_GBps": None if ceiling is None else round(ceiling, 1),
+        "host_pipeline_fps_pcie_inclusive": None if host_fps is None else round(host_fps, 1),
+        "rows_over_read_ceiling": None if ceiling is None else round(achieved / ceiling, 4),
+        "timed_with_events_ms_per_step": round(m["total_ms"] / args.steps, 5),
+        "settle_steps_after_warmup": m["settle"]})
+    if half is not None:
+        config["halfrange"] = half
     rec = {
         "metric": "frames/sec and achieved HBM GB/s (% of peak), 16-bit 3840x2160, 1 MI355X",
-        "value": round(fps, 1),
+        "value": round(m["fps"], 1),
         "unit": "frames/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": round(m["clean_ms"] / args.steps, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "u16 in, u64/f64 sums",
         "data": "synthetic",
-        "config": {"workload": wl.name, "frames_per_step": F, "w": wl.w, "h": wl.h,
-                   "bpc": wl.bpc, "recipe": wl.recipe, "ring_copies": ring,
-                   "whole_path_GBps": round(batch_bytes * args.steps / (clean_ms / 1e3) / 1e9, 1),
-                   "whole_path_frac": round(batch_bytes * args.steps / (clean_ms / 1e3) / 1e9
-                                            / PEAK_HBM_GBS, 4),
-                   "walk_avg_us": round(1e3 * walk_ms / max(walk_n, 1), 2),
-                   **extra_us,
-                   "read_ceiling_GBps": None if ceiling is None else round(ceiling, 1),
-                   "host_pipeline_fps_pcie_inclusive": None if host_fps is None else round(host_fps, 1),
-                   "rows_over_read_ceiling": None if ceiling is None else round(achieved / ceiling, 4),
-                   "timed_with_events_ms_per_step": round(total_ms / args.steps, 5),
-                   "settle_steps_after_warmup": settle_steps},
+        "config": config,
         "roofline": {"bound": "hbm", "kernel": "k_rows16", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": recorded_traffic(wl.name),
                      "bytes_per_launch": batch_bytes,
-                     "avg_launch_us": round(rows_avg_ms * 1e3, 2)},
+                     "avg_launch_us": round(rows_us, 2)},
     }
     if not args.no_cpu:
-        rec["cpu_baseline"] = cpu_baseline(ref_h, dis_h, wl.bpc, wl.w)
+        rec["cpu_baseline"] = cpu_baseline(ref_h, dis_h, wl.bpc, wl.w, wl.bytes_per_frame)
     print(json.dumps(rec), flush=True)
 
 

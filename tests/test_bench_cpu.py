@@ -61,3 +61,19 @@ def test_workload_table():
     assert ref.shape == (wl.frames, wl.h, wl.stride) == dis.shape
     assert ref.dtype == dis.dtype == (np.uint8 if wl.bpc == 8 else np.uint16)
     assert int(ref[:, :, :wl.w].max()) < (1 << wl.bpc)
+
+
+def test_cpu_baseline_fields():
+    """The oracle leg reports a warm one-core rate over several frames, an
+    all-cores rate with one thread per usable CPU, nproc and the CPU model
+    (small frames and a short budget here)."""
+    wl = synth.WORKLOADS[1]
+    ref, dis = synth.make_frames(1)
+    rec = bench.cpu_baseline(ref, dis, wl.bpc, wl.w, wl.bytes_per_frame, budget_s=0.2,
+                             one_core_frames=8)
+    nproc, usable, _ = bench.cpu_facts()
+    assert rec["kind"] == "oracle" and rec["unit"] == "frames/s"
+    assert rec["cores"] == usable and rec["nproc"] == nproc == os.cpu_count()
+    assert rec["value"] > 0 and rec["one_core_value"] > 0
+    assert abs(rec["GBps"] - rec["value"] * wl.bytes_per_frame / 1e9) < 1e-3
+    assert "8 frames one after another" in rec["sample"]
