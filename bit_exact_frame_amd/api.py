@@ -47,6 +47,8 @@ for _n in ("moment_frame", "psnr_noise", "bef_frames", "bef_frames_async", "bef_
            "bef_frames_units", "bef_read_ceiling", "bef_frames_host"):
     getattr(_lib, _n).restype = _i
 _lib.bef_last_error.restype = ctypes.c_char_p
+_lib.bef_walk_paths.argtypes = [_vp, _i]
+_lib.bef_walk_paths.restype = _i
 _lib.bef_debug_set.argtypes = [_u]
 _lib.bef_debug_set.restype = _u
 _lib.bef_timing_enable.argtypes = [_i]
@@ -54,22 +56,13 @@ _lib.bef_timing_read.argtypes = [_i, _dp, ctypes.POINTER(ctypes.c_long)]
 _lib.bef_release.restype = None
 _lib.bef_timing_reset.restype = None
 
-# test hooks (host only)
-_lib.bef_host_plane_units.argtypes = [_vp, _i, _i, _pd, _i, _u, _u64p]
-_lib.bef_host_noise_units.argtypes = [_vp, _vp, _i, _i, _pd, _i, _u64p, _u64p]
-_lib.bef_host_rne53_add.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
-_lib.bef_host_rne53_add.restype = ctypes.c_uint64
-_lib.bef_host_run_pair.argtypes = [_vp, _i, _i, _u64p]
-_lib.bef_host_fast_units.argtypes = [_vp, _i, _i, _pd, _i, _u64p]
-_lib.bef_host_fast_noise.argtypes = [_vp, _vp, _i, _i, _pd, _i, _u64p]
-_lib.bef_host_load_shape.argtypes = [_vp, _vp, _i, _pd, _pd, _i, ctypes.POINTER(ctypes.c_int)]
-
 DBG_PLAN_WRONG = 1
 DBG_PLAN_NONE = 2
 DBG_TERMS_ONLY = 4
 DBG_FORCE_ROUND = 8
 DBG_NO_STRETCH = 16
 DBG_NO_CLOSED_FORM = 32
+DBG_SPLIT_LAUNCH = 64
 
 KERNELS = {"rows": 0, "plan": 1, "pairs": 2, "walk": 3, "ceiling": 4}
 
@@ -238,6 +231,20 @@ def bef_read_ceiling(ref, dis, out, w: int | None = None, stream=None):
            "bef_read_ceiling")
 
 
+PATHS = {0: "sums", 1: "fast", 2: "general", 3: "chain"}
+
+
+def bef_walk_paths():
+    """Walk path of each (frame, job) of the last synchronous batch, as a
+    uint8 array [F, 3] (jobs: ref moments, dis moments, noise; codes in
+    PATHS)."""
+    n = _lib.bef_walk_paths(None, 0)
+    out = np.zeros(n, np.uint8)
+    if n:
+        _lib.bef_walk_paths(ctypes.c_void_p(out.ctypes.data), n)
+    return out.reshape(-1, 3)
+
+
 def bef_debug_set(flags: int) -> int:
     return int(_lib.bef_debug_set(int(flags)))
 
@@ -260,66 +267,3 @@ def bef_timing_read(kernel: str):
 
 def bef_release():
     _lib.bef_release()
-
-
-# ---- host-only test hooks --------------------------------------------------
-
-def bef_host_plane_units(plane: np.ndarray, bpc: int, w: int | None = None, dbg: int = 0):
-    h, stride = plane.shape
-    w = stride if w is None else w
-    out = (ctypes.c_uint64 * 3)()
-    _check(_lib.bef_host_plane_units(plane.ctypes.data, w, h, stride, bpc, dbg, out),
-           "bef_host_plane_units")
-    return list(out)
-
-
-def bef_host_noise_units(ref: np.ndarray, dis: np.ndarray, bpc: int, w: int | None = None):
-    h, stride = ref.shape
-    w = stride if w is None else w
-    bits = ctypes.c_uint64()
-    ex = ctypes.c_uint64()
-    _check(_lib.bef_host_noise_units(ref.ctypes.data, dis.ctypes.data, w, h, stride, bpc,
-                                     ctypes.byref(bits), ctypes.byref(ex)),
-           "bef_host_noise_units")
-    return bits.value, ex.value
-
-
-def bef_host_fast_units(plane: np.ndarray, bpc: int, w: int | None = None):
-    """[handled, S_cpu, S_exact] of the fast path's decisions on one plane."""
-    h, stride = plane.shape
-    w = stride if w is None else w
-    out = (ctypes.c_uint64 * 3)()
-    _check(_lib.bef_host_fast_units(plane.ctypes.data, w, h, stride, bpc, out),
-           "bef_host_fast_units")
-    return list(out)
-
-
-def bef_host_fast_noise(ref: np.ndarray, dis: np.ndarray, bpc: int, w: int | None = None):
-    """[handled, bits of the noise double in units, exact] of the fast noise."""
-    h, stride = ref.shape
-    w = stride if w is None else w
-    out = (ctypes.c_uint64 * 3)()
-    _check(_lib.bef_host_fast_noise(ref.ctypes.data, dis.ctypes.data, w, h, stride, bpc, out),
-           "bef_host_fast_noise")
-    return list(out)
-
-
-def bef_host_rne53_add(s: int, t: int) -> int:
-    return int(_lib.bef_host_rne53_add(s, t))
-
-
-def bef_host_run_pair(terms: np.ndarray, e: int):
-    t = np.ascontiguousarray(terms, dtype=np.uint32)
-    out = (ctypes.c_uint64 * 2)()
-    _check(_lib.bef_host_run_pair(t.ctypes.data, t.size, e, out), "bef_host_run_pair")
-    return list(out)
-
-
-def bef_host_load_shape(ref_addr: int, dis_addr: int, w: int, stride: int, frame_pitch: int,
-                        nframes: int):
-    """(bytes per load, load slots per group) the row kernel uses for planes
-    at these addresses (alignment only; nothing is read)."""
-    out = (ctypes.c_int * 2)()
-    _check(_lib.bef_host_load_shape(ctypes.c_void_p(ref_addr), ctypes.c_void_p(dis_addr), w,
-                                    stride, frame_pitch, nframes, out), "bef_host_load_shape")
-    return out[0], out[1]

@@ -1,11 +1,13 @@
 """Build libbef.so (HIP, gfx950) in-tree with hipcc.
 
     python -m bit_exact_frame_amd.build          # libbef.so
-    build(mutant=k, host_only=True, out=...)     # host-only test variants
+    build_host_emu(out, mutant=k)                # the tests' emulation library
 
 The library holds the streaming row kernels (rows.hip), the ordered plan /
-pair / walk kernels (walk.hip), the host runtime behind the C ABI (bef.cpp)
-and the host emulation test entry points (host_emu.cpp).
+pair / walk kernels (walk.hip) and the host runtime behind the C ABI
+(bef.cpp).  The host emulation of the kernels' steps (host_emu.cpp, test
+entry points of host_emu.h) is a separate host-only library that only the
+tests build and load.
 Every HIP source is compiled for gfx950 with packed FP32 instructions
 disabled and no floating-point contraction.
 """
@@ -21,7 +23,7 @@ LIB = os.path.join(HERE, "libbef.so")
 ARCH = os.environ.get("BEF_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["rows.hip", "walk.hip", "bef.cpp", "host_emu.cpp"]
+SOURCES = ["rows.hip", "walk.hip", "bef.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-fno-fast-math",
           "-Wall", "-Wno-unused-function", f"-I{os.path.join(ROOT, 'include')}"]
@@ -46,9 +48,12 @@ def build_host_emu(out: str, mutant: int = 0) -> str:
     """Host-only build of the emulation entry points (g++, no HIP), with an
     optional planted break in the shared step header (tests only)."""
     cmd = ["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-ffp-contract=off",
-           f"-DBEF_MUTANT={int(mutant)}", os.path.join(CSRC, "host_emu.cpp"),
-           "-o", out]
-    subprocess.run(cmd, check=True, capture_output=True, text=True)
+           "-Wall", f"-DBEF_MUTANT={int(mutant)}", os.path.join(CSRC, "host_emu.cpp"),
+           "-o", out + ".tmp"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("g++ failed:\n" + " ".join(cmd) + "\n" + res.stderr)
+    os.replace(out + ".tmp", out)
     return out
 
 

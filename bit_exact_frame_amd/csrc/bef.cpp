@@ -14,6 +14,7 @@
 #include <vector>
 
 #include "bef_internal.h"
+#include "load_shape.h"
 #include "ordsum.h"
 
 using namespace bef;
@@ -46,6 +47,9 @@ struct Arena {
   hipEvent_t copied[2] = {nullptr, nullptr}, done[2] = {nullptr, nullptr};
 };
 Arena g_arena[kMaxDev];
+
+// Walk paths of the last synchronous batch (bef_walk_paths).
+std::vector<uint8_t> g_paths;
 
 // Per-device address of the static scratch (below), taken once per device.
 void* g_static_ptr[kMaxDev] = {};
@@ -93,7 +97,9 @@ int validate(const void* ref, const void* dis, int w, int h, ptrdiff_t stride,
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t r1, r2, rn, codd, plan, pairs, psum, results, units, total;
+  size_t r1, r2, rn, codd, plan, pairs, psum, results, units, paths, total;
+  // results, units and paths are copied back together: bytes from results
+  size_t readback() const { return total - results; }
 };
 
 Layout layout(int F, int h) {
@@ -109,6 +115,7 @@ Layout layout(int F, int h) {
   L.psum = o; o = up256(o + (size_t)F * 4 * 8);
   L.results = o; o = up256(o + (size_t)F * 6 * 8);
   L.units = o; o = up256(o + (size_t)F * 8 * 8);
+  L.paths = o; o = up256(o + (size_t)F * 3);
   L.total = o;
   return L;
 }
@@ -194,41 +201,6 @@ hipError_t timed(int kernel, F launch) {
   return e;
 }
 
-// Load shape of the 16-bit row kernel: bytes per load and load slots per
-// lane per group.  Measured at rows of 1920, 2560 and 3840 samples, 8-byte
-// loads beat 16- and 4-byte ones at every width, so the width is 8 bytes
-// whenever the plane starts, the row pitch and the frame pitch allow it,
-// else 4.  A wave spreads a row's whole chunks over its 64 lanes in groups
-// of 64 * ng: the group size that leaves the fewest idle slots in the
-// last group wins (an idle slot still costs its arithmetic, on zeros), then
-// the larger group (more loads in flight, fewer rounds).
-void load_shape(const void* ref, const void* dis, int w, ptrdiff_t stride, ptrdiff_t pitch,
-                int nframes, int* cb_out, int* ng_out) {
-  uint64_t al = 16;
-  auto limit = [&](uint64_t v) {
-    while (al > 1 && v % al) al >>= 1;
-  };
-  limit((uintptr_t)ref);
-  limit((uintptr_t)dis);
-  limit((uint64_t)stride * 2);
-  if (nframes > 1) limit((uint64_t)pitch * 2);
-  int cb = 0;
-  for (int c : {8, 4})
-    if (!cb && (uint64_t)c <= al && (uint64_t)w * 2 / c > 0) cb = c;
-  int best_ng = 1;
-  if (cb) {
-    const uint64_t nc = (uint64_t)w * 2 / cb;
-    const uint64_t nper = (nc + 63) / 64;
-    uint64_t best_idle = ~0ull;
-    for (int ng : {15, 8, 5, 4}) {
-      const uint64_t idle = ((nper + ng - 1) / ng) * ng * 64 - nc;
-      if (idle < best_idle) best_ng = ng, best_idle = idle;
-    }
-  }
-  *cb_out = cb;
-  *ng_out = best_ng;
-}
-
 struct Call {
   Geometry g;
   int dev;
@@ -288,6 +260,7 @@ void bind(Call& c, char* base) {
   c.ra.psum = (uint64_t*)(base + c.L.psum);
   c.d_results = (double*)(base + c.L.results);
   c.d_units = (uint64_t*)(base + c.L.units);
+  c.ra.paths = (uint8_t*)(base + c.L.paths);
 }
 
 // setup, then the library's arena (grown on demand) as scratch.
@@ -295,8 +268,7 @@ int prepare(Call& c, const void* ref, const void* dis, int w, int h, ptrdiff_t s
             ptrdiff_t pitch, int nframes, int bpc) {
   int rc = setup(c, ref, dis, w, h, stride, pitch, nframes, bpc);
   if (rc) return rc;
-  if ((rc = ensure(c.dev, c.L.total, (size_t)nframes * 8 * 8 + (size_t)nframes * 6 * 8 + 256)))
-    return rc;
+  if ((rc = ensure(c.dev, c.L.total, c.L.readback()))) return rc;
   bind(c, (char*)g_arena[c.dev].base);
   return 0;
 }
@@ -345,12 +317,15 @@ int run_sync(const void* ref, const void* dis, int w, int h, ptrdiff_t stride, p
   if (rc) return rc;
   hipStream_t st = (hipStream_t)stream;
   if ((rc = check_stream(c, st)) || (rc = enqueue(c, st, c.d_results))) return rc;
-  double* hres = (double*)g_arena[c.dev].host;
-  uint64_t* hun = (uint64_t*)((char*)hres + up256((size_t)nframes * 6 * 8));
-  BEF_HIP(hipMemcpyAsync(hres, c.d_results, (size_t)nframes * 6 * 8, hipMemcpyDeviceToHost, st));
-  BEF_HIP(hipMemcpyAsync(hun, c.d_units, (size_t)nframes * 8 * 8, hipMemcpyDeviceToHost, st));
+  // results, units and walk paths lie together in the scratch: one copy
+  char* hb = (char*)g_arena[c.dev].host;
+  const double* hres = (const double*)hb;
+  const uint64_t* hun = (const uint64_t*)(hb + (c.L.units - c.L.results));
+  const uint8_t* hpath = (const uint8_t*)(hb + (c.L.paths - c.L.results));
+  BEF_HIP(hipMemcpyAsync(hb, c.d_results, c.L.readback(), hipMemcpyDeviceToHost, st));
   BEF_HIP(hipStreamSynchronize(st));
   if (g_timing) ev_collect();
+  g_paths.assign(hpath, hpath + 3 * (size_t)nframes);
   for (int f = 0; f < nframes; ++f) {
     if (moments)
       for (int k = 0; k < 4; ++k) moments[4 * f + k] = hres[6 * f + k];
@@ -572,6 +547,14 @@ int psnr_noise(const void* ref, const void* dis, int w, int h, ptrdiff_t stride,
 
 const char* bef_last_error(void) { return g_err; }
 
+int bef_walk_paths(uint8_t* out, int n) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  const int count = (int)g_paths.size();
+  if (out)
+    for (int k = 0; k < n && k < count; ++k) out[k] = g_paths[k];
+  return count;
+}
+
 unsigned bef_debug_set(unsigned flags) {
   std::lock_guard<std::mutex> lk(g_mu);
   const unsigned old = g_dbg;
@@ -601,13 +584,6 @@ void bef_timing_reset(void) {
     g_ms[k] = 0;
     g_n[k] = 0;
   }
-}
-
-int bef_host_load_shape(const void* ref, const void* dis, int w, ptrdiff_t stride,
-                        ptrdiff_t frame_pitch, int nframes, int out[2]) {
-  if (!out || w <= 0 || nframes <= 0) return -EINVAL;
-  load_shape(ref, dis, w, stride, frame_pitch, nframes, &out[0], &out[1]);
-  return 0;
 }
 
 void bef_release(void) {

@@ -35,7 +35,14 @@ struct RowArrays {
   int8_t* plan;     // kPlanExact, kPlanCross or a binade
   uint64_t* pairs;  // [plane][frame][row][2] row pair (binades >= 55)
   uint64_t* psum;   // [plane][frame][2] exact plane sums of r2 and r1 (by k_plan)
+  uint8_t* paths;   // [frame][3] path each walk block took (kPath*), diagnostics
 };
+
+// Walk paths, per (frame, job), jobs ref moments, dis moments, noise.
+constexpr uint8_t kPathSums = 0;     // no sum can pass 2^53: exact sums only
+constexpr uint8_t kPathFast = 1;     // the one-wave fast path (moments or noise)
+constexpr uint8_t kPathGeneral = 2;  // the general walk (moments)
+constexpr uint8_t kPathChain = 3;    // the row-by-row double chain (noise)
 
 // Each launch goes out with hipExtLaunchKernel; ev0 / ev1 (or null) are
 // recorded by the dispatch itself at the kernel's start and end.

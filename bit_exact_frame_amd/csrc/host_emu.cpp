@@ -1,25 +1,35 @@
 // host_emu.cpp -- the device algorithm's steps run serially on the host.
 //
-// Test entry points only (bef_host_*): they take HOST planes and follow the
-// same decisions as the kernels, with the integer steps of ordsum.h.  The
-// fast path: the plan as five threshold edges, exact and closed-form
-// segments, rows and terms at an edge one by one, noise stretches as
-// composed row pairs.  The general walk: exact per-row sums, a per-row plan
-// from the exact prefix, row pairs from 64 lane runs joined by an ordered
-// tree, a walk over stretches of rows with the same plan, a fallback of
-// each unfit row to 256 runs (planned by their own exact prefix) and of
-// each unfit run to single terms -- with the integer steps of ordsum.h.
+// Test entry points only (host_emu.h), built into their own library
+// (libbef_emu.so, g++); libbef.so does not contain them.  They take HOST
+// planes and follow the kernels' decisions and decomposition with the
+// integer steps of ordsum.h and its shared shape constants:
+//  - the general walk: exact per-row sums, a per-row plan from the exact
+//    prefix (with the test flags' wrong or missing plans), row pairs from
+//    segments of kPairSeg samples, each kPairLanes lane runs joined by a
+//    balanced ordered tree, segments joined in row order; the plane walked
+//    kWalkChunk rows at a time as stretches of rows with one plan (up to
+//    kWalkMaxSeg stretches, else row by row), a stretch's pair a
+//    kWalkThreads-leaf composition; a row that leaves its plan taken as
+//    at most three groups of its kWalkThreads runs (apply_groups), else
+//    its runs one by one under the binade S is in and the next, else its
+//    terms with the one-term step;
+//  - the fast path: the plan as five threshold edges, exact and
+//    closed-form stretches, the rows and terms at an edge one by one, and
+//    noise stretches as composed row pairs.
 // The pages' own host test does the same with the twins' steps (ADR-1497,
-// Decision: the host test runs the kernels' steps against the CPU loop,
-// with real and with deliberately wrong plans).  Nothing on the product
-// path calls this file.
+// Decision: the kernels' steps run on the host against the CPU loop, with
+// real and with deliberately wrong plans).
 #include <errno.h>
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "../../include/bef.h"
+#include "host_emu.h"
+#include "load_shape.h"
 #include "ordsum.h"
 
 using namespace bef;
@@ -37,34 +47,34 @@ struct Plane {
   }
 };
 
-// Balanced ordered tree over leaves (the shape of a shuffle-down tree).
-Pair64 tree64(std::vector<Pair64> v, int sh) {
-  if (v.empty()) return pair64_id();
+// Balanced ordered tree over a power-of-two number of leaves: leaf l takes
+// leaf l + off for off = 1, 2, 4, ... (the shape of the kernels' shuffle
+// and DPP trees, and of a block's tree over its waves).
+template <class P, class Then>
+P tree(std::vector<P> v, P id, Then then) {
   size_t n = 1;
   while (n < v.size()) n <<= 1;
-  v.resize(n, pair64_id());
+  v.resize(n, id);
   for (size_t off = 1; off < n; off <<= 1)
-    for (size_t l = 0; l + off < n; l += 2 * off) v[l] = then64(v[l], v[l + off], sh);
+    for (size_t l = 0; l + off < n; l += 2 * off) v[l] = then(v[l], v[l + off]);
   return v[0];
 }
-Pair32 tree32(std::vector<Pair32> v, int sh) {
-  if (v.empty()) return pair32_id();
-  size_t n = 1;
-  while (n < v.size()) n <<= 1;
-  v.resize(n, pair32_id());
-  for (size_t off = 1; off < n; off <<= 1)
-    for (size_t l = 0; l + off < n; l += 2 * off) v[l] = then32(v[l], v[l + off], sh);
-  return v[0];
+Pair64 tree64(const std::vector<Pair64>& v, int sh) {
+  return tree(v, pair64_id(), [&](Pair64 a, Pair64 b) { return then64(a, b, sh); });
+}
+Pair32 tree32(const std::vector<Pair32>& v, int sh) {
+  return tree(v, pair32_id(), [&](Pair32 a, Pair32 b) { return then32(a, b, sh); });
 }
 
-// Composite of items [a, b) the way a 256-thread block forms it: each
-// thread folds a contiguous chunk in order, then an ordered tree.
+// A composite of items [a, b) the way a walk block forms it: thread t of
+// kWalkThreads folds items [a + t*c, a + t*c + c) in order (c = ceil((b -
+// a) / kWalkThreads)), then the threads' composites go through a balanced
+// tree (64 lanes a wave, then the waves).
 template <class PairOf>
 Pair64 block_compose(int a, int b, int sh, PairOf pair_of) {
-  const int n = b - a;
-  const int c = (n + 255) / 256;
-  std::vector<Pair64> leaves(256, pair64_id());
-  for (int t = 0; t < 256; ++t) {
+  const int c = (b - a + kWalkThreads - 1) / kWalkThreads;
+  std::vector<Pair64> leaves(kWalkThreads, pair64_id());
+  for (int t = 0; t < kWalkThreads; ++t) {
     Pair64 acc = pair64_id();
     for (int k = a + t * c; k < a + (t + 1) * c && k < b; ++k) acc = then64(acc, pair_of(k), sh);
     leaves[t] = acc;
@@ -75,28 +85,31 @@ Pair64 block_compose(int a, int b, int sh, PairOf pair_of) {
 struct Emu {
   Plane pl;
   unsigned dbg;
-  std::vector<uint64_t> R, P, C;
+  std::vector<uint64_t> R, C;
   std::vector<int> plan;
   std::vector<Pair64> pair;
 
   uint32_t T(int i, int j) const { return fsq_units(pl.x(i, j)); }
 
-  // Row pair under binade e.  In the binades of 2^53 and 2^54 it follows
-  // from the row's exact sum and its count of odd float squares (every
-  // float square in units is 0 or 1 mod 4: see the walk kernel); otherwise
-  // 64 lane runs of ceil(w/64) terms, each a two-trajectory fold, joined by
-  // an ordered tree and widened with R.
+  // Row pair under binade e: the closed form in the binades of 2^53 and
+  // 2^54; otherwise the row pair kernel's: segments of kPairSeg samples,
+  // each split into kPairLanes runs of ceil(n / kPairLanes) terms (two
+  // trajectories each) joined by a balanced tree, the segments joined in
+  // row order, widened with the row's exact sum.
   Pair64 row_pair(int i, int e) const {
     if (e <= 54 && !(dbg & BEF_DBG_NO_CLOSED_FORM)) return closed_pair(R[i], C[i], e);
-    const int sh = e - 52;
-    const int L = (pl.w + 63) / 64;
-    std::vector<Pair32> lanes(64);
-    for (int l = 0; l < 64; ++l) {
-      const int s0 = l * L;
-      const int n = s0 >= pl.w ? 0 : (s0 + L <= pl.w ? L : pl.w - s0);
-      lanes[l] = run_pair([&](int j) { return T(i, s0 + j); }, n, sh);
+    const int sh = e - 52, w = pl.w;
+    Pair32 acc = pair32_id();
+    for (int s0 = 0; s0 < w; s0 += kPairSeg) {
+      const int n = std::min(kPairSeg, w - s0), L = (n + kPairLanes - 1) / kPairLanes;
+      std::vector<Pair32> lanes(kPairLanes);
+      for (int l = 0; l < kPairLanes; ++l) {
+        const int j0 = std::min(l * L, n), j1 = std::min(j0 + L, n);
+        lanes[l] = run_pair([&](int j) { return T(i, s0 + j0 + j); }, j1 - j0, sh);
+      }
+      acc = then32(acc, tree32(lanes, sh), sh);
     }
-    return widen_pair(tree32(lanes, sh), R[i]);
+    return widen_pair(acc, R[i]);
   }
 
   uint64_t terms(uint64_t s, int i, int j0, int j1) const {
@@ -104,59 +117,142 @@ struct Emu {
     return s;
   }
 
-  // Generic walk over items with plans (stretches first, then item steps).
-  template <class PlanOf, class EOf, class PairOf, class Step>
-  uint64_t walk(uint64_t s, int n, PlanOf plan_of_item, EOf e_of, PairOf pair_of,
-                Step step) const {
-    int i = 0;
-    while (i < n) {
-      const int e = plan_of_item(i);
-      int j = i + 1;
-      while (j < n && plan_of_item(j) == e) ++j;
+  // Items [0, n) with plans, exact sums and odd counts, from s: stretches
+  // of equal plan (at most kWalkMaxSeg of them, else item by item), a
+  // stretch exact, or one pair inside its binade (closed form, or the
+  // items' pairs composed as a block does), else item by item.
+  template <class PlanOf, class EOf, class COf, class PairOf, class Step>
+  uint64_t walk_items(uint64_t s, int n, PlanOf plan_at, EOf e_at, COf c_at, PairOf pair_at,
+                      Step step) const {
+    std::vector<int> starts;
+    for (int k = 0; k < n; ++k)
+      if (k == 0 || plan_at(k) != plan_at(k - 1)) starts.push_back(k);
+    if ((int)starts.size() > kWalkMaxSeg) {
+      for (int k = 0; k < n; ++k) s = step(s, k);
+      return s;
+    }
+    starts.push_back(n);
+    for (size_t g = 0; g + 1 < starts.size(); ++g) {
+      const int a = starts[g], b = starts[g + 1], e = plan_at(a);
+      uint64_t E = 0, Cn = 0;
+      for (int k = a; k < b; ++k) E += e_at(k), Cn += c_at(k);
       bool done = false;
       if (e == kPlanExact) {
-        uint64_t E = 0;
-        for (int k = i; k < j; ++k) E += e_of(k);
         done = try_exact(&s, E);
       } else if (e >= 53 && !(dbg & BEF_DBG_NO_STRETCH)) {
-        done = try_apply(&s, block_compose(i, j, e - 52, pair_of), e);
+        const Pair64 p = (e <= 54 && !(dbg & BEF_DBG_NO_CLOSED_FORM))
+                             ? closed_pair(E, Cn, e)
+                             : block_compose(a, b, e - 52, [&](int k) { return pair_at(k, e); });
+        done = try_apply(&s, p, e);
       }
       if (!done)
-        for (int k = i; k < j; ++k) s = step(s, k);
-      i = j;
+        for (int k = a; k < b; ++k) s = step(s, k);
     }
     return s;
   }
 
-  // A row the plan does not fit: 256 runs under the binade S is in and the
-  // next one, planned from their own exact prefix; unfit runs by terms.
-  uint64_t fallback_row(uint64_t s, int i) const {
-    if (dbg & BEF_DBG_TERMS_ONLY) return terms(s, i, 0, pl.w);
-    const int eA = (s < kTwo53) ? 53 : binade(s);
-    const int eB = eA + 1;
-    const int L = (pl.w + 255) / 256;
-    std::vector<uint64_t> E(256), Q(256);
-    std::vector<Pair64> pA(256), pB(256);
-    std::vector<int> rp(256);
-    std::vector<int> j0(256), j1(256);
-    uint64_t q = s;
-    const uint64_t Mr = (uint64_t)pl.w << (eB - 53);
-    for (int t = 0; t < 256; ++t) {
-      j0[t] = t * L < pl.w ? t * L : pl.w;
-      j1[t] = t * L + L < pl.w ? t * L + L : pl.w;
-      uint64_t e = 0;
-      for (int j = j0[t]; j < j1[t]; ++j) e += T(i, j);
-      E[t] = e;
-      auto tt = [&](int j) { return T(i, j0[t] + j); };
-      pA[t] = widen_pair(run_pair(tt, j1[t] - j0[t], eA - 52), e);
-      pB[t] = widen_pair(run_pair(tt, j1[t] - j0[t], eB - 52), e);
-      Q[t] = q;
-      rp[t] = plan_of(q, e, Mr);
-      q += e;
+  // A row that leaves its plan, by groups of runs: kWalkThreads runs of
+  // ceil(w / kWalkThreads) terms, each given a group from its plan (exact
+  // sum, exact prefix from S, the row's margin); the runs of groups in a
+  // binade from 2^55 up give pairs joined as the walk block joins them (a
+  // balanced tree per wave, then the waves in order); apply_groups does
+  // the rest.  False when the runs do not form the groups in order.
+  bool row_groups(uint64_t* sp, int i) const {
+    const int w = pl.w;
+    const uint64_t s0 = *sp;
+    const bool low = s0 < kTwo53;
+    const int eA = low ? 53 : binade(s0), eB = eA + 1, e2 = low ? eA : eB;
+    const int L = (w + kWalkThreads - 1) / kWalkThreads, nr = (w + L - 1) / L;
+    std::vector<uint64_t> E(kWalkThreads), c(kWalkThreads), Q(kWalkThreads), QC(kWalkThreads);
+    std::vector<int> g(kWalkThreads, 3);
+    uint64_t tot = 0, totc = 0;
+    for (int t = 0; t < kWalkThreads; ++t) {
+      const int j0 = std::min(t * L, w), j1 = std::min(j0 + L, w);
+      E[t] = c[t] = 0;
+      for (int j = j0; j < j1; ++j) E[t] += T(i, j), c[t] += T(i, j) & 1u;
+      Q[t] = tot;
+      QC[t] = totc;
+      tot += E[t];
+      totc += c[t];
     }
-    return walk(
-        s, 256, [&](int t) { return rp[t]; }, [&](int t) { return E[t]; },
-        [&](int t) { return rp[t] == eA ? pA[t] : pB[t]; },
+    for (int t = 0; t < nr; ++t) {
+      const int p = plan_of(s0 + Q[t], E[t], (uint64_t)w << (eB - 53));
+      g[t] = p == kPlanCross ? 1 : (p == (low ? kPlanExact : eA)) ? 0 : p == e2 ? 2 : 3;
+    }
+    GroupStart G[4] = {{0, 0, -1}, {0, 0, -1}, {0, 0, -1}, {tot, totc, nr}};
+    for (int t = 0; t < nr; ++t) {
+      const int gp = t > 0 ? g[t - 1] : -1;
+      if (g[t] == 3 || gp > g[t]) return false;
+      if (gp != g[t]) G[g[t]] = GroupStart{Q[t], QC[t], t};
+    }
+    const bool tree0 = !low && eA >= 55, tree2 = e2 >= 55;
+    Pair64 c0 = pair64_id(), c2 = pair64_id();
+    if (tree0 || tree2) {
+      std::vector<Pair64> l0(kWalkThreads, pair64_id()), l2(kWalkThreads, pair64_id());
+      for (int t = 0; t < kWalkThreads; ++t) {
+        if (!((g[t] == 0 && tree0) || (g[t] == 2 && tree2))) continue;
+        const int e = g[t] == 0 ? eA : e2, j0 = std::min(t * L, w), j1 = std::min(j0 + L, w);
+        const Pair64 pr =
+            widen_pair(run_pair([&](int j) { return T(i, j0 + j); }, j1 - j0, e - 52), E[t]);
+        (g[t] == 0 ? l0 : l2)[t] = pr;
+      }
+      for (int wv = 0; wv < kWalkThreads / 64; ++wv) {
+        const std::vector<Pair64> w0(l0.begin() + 64 * wv, l0.begin() + 64 * wv + 64);
+        const std::vector<Pair64> w2(l2.begin() + 64 * wv, l2.begin() + 64 * wv + 64);
+        // a wave composes only the groups it has a tree for
+        const Pair64 q0 = tree0 ? tree64(w0, eA - 52) : pair64_id();
+        const Pair64 q2 = tree2 ? tree64(w2, e2 - 52) : pair64_id();
+        c0 = wv == 0 ? q0 : then64(c0, q0, eA - 52);
+        c2 = wv == 0 ? q2 : then64(c2, q2, e2 - 52);
+      }
+    }
+    return apply_groups(
+        sp, G, low, eA,
+        [&](uint64_t s, int ra, int rb) { return terms(s, i, ra * L, std::min(rb * L, w)); },
+        [&](int k, int e, uint64_t Eg, uint64_t Cg) {
+          return e <= 54 ? closed_pair(Eg, Cg, e) : (k == 0 ? c0 : c2);
+        });
+  }
+
+  // A row that leaves its plan: its terms one by one (test flag), else its
+  // groups of runs, else its kWalkThreads runs planned from their own exact
+  // prefix with pairs under the binade S is in (eA) and the next (eB),
+  // walked as stretches; a run that fits neither goes term by term.
+  uint64_t fallback_row(uint64_t s, int i) const {
+    const int w = pl.w;
+    if (dbg & BEF_DBG_TERMS_ONLY) return terms(s, i, 0, w);
+    if (!(dbg & (BEF_DBG_NO_STRETCH | BEF_DBG_NO_CLOSED_FORM))) {
+      uint64_t s2 = s;
+      if (row_groups(&s2, i)) return s2;
+    }
+    const int eA = s < kTwo53 ? 53 : binade(s), eB = eA + 1;
+    const int L = (w + kWalkThreads - 1) / kWalkThreads;
+    std::vector<uint64_t> E(kWalkThreads), c(kWalkThreads);
+    std::vector<Pair64> pA(kWalkThreads), pB(kWalkThreads);
+    std::vector<int> rp(kWalkThreads), j0(kWalkThreads), j1(kWalkThreads);
+    uint64_t q = s;
+    const uint64_t Mr = (uint64_t)w << (eB - 53);
+    for (int t = 0; t < kWalkThreads; ++t) {
+      j0[t] = std::min(t * L, w);
+      j1[t] = std::min(j0[t] + L, w);
+      E[t] = c[t] = 0;
+      for (int j = j0[t]; j < j1[t]; ++j) E[t] += T(i, j), c[t] += T(i, j) & 1u;
+      for (int qq = 0; qq < 2; ++qq) {
+        const int e = qq ? eB : eA;
+        const Pair64 p =
+            (e <= 54 && !(dbg & BEF_DBG_NO_CLOSED_FORM))
+                ? closed_pair(E[t], c[t], e)
+                : widen_pair(run_pair([&](int j) { return T(i, j0[t] + j); }, j1[t] - j0[t],
+                                      e - 52),
+                             E[t]);
+        (qq ? pB : pA)[t] = p;
+      }
+      rp[t] = plan_of(q, E[t], Mr);
+      q += E[t];
+    }
+    return walk_items(
+        s, kWalkThreads, [&](int t) { return rp[t]; }, [&](int t) { return E[t]; },
+        [&](int t) { return c[t]; }, [&](int t, int e) { return e == eA ? pA[t] : pB[t]; },
         [&](uint64_t s2, int t) {
           if (try_exact(&s2, E[t])) return s2;
           if (try_apply(&s2, pA[t], eA)) return s2;
@@ -168,23 +264,19 @@ struct Emu {
   void run(uint64_t out[3]) {
     const int h = pl.h, w = pl.w;
     R.assign(h, 0);
-    P.assign(h, 0);
     C.assign(h, 0);
     plan.assign(h, kPlanExact);
     pair.assign(h, pair64_id());
+    std::vector<uint64_t> P(h, 0);
     uint64_t s1 = 0, tot = 0;
     for (int i = 0; i < h; ++i) {
-      uint64_t r = 0;
-      uint64_t c = 0;
       for (int j = 0; j < w; ++j) {
         s1 += pl.x(i, j);
-        r += T(i, j);
-        c += T(i, j) & 1u;
+        R[i] += T(i, j);
+        C[i] += T(i, j) & 1u;
       }
-      R[i] = r;
-      C[i] = c;
       P[i] = tot;
-      tot += r;
+      tot += R[i];
     }
     out[0] = s1;
     out[1] = tot;
@@ -198,16 +290,32 @@ struct Emu {
       if (e >= 53 && (dbg & BEF_DBG_PLAN_NONE)) e = kPlanCross;
       if (e >= 53 && (dbg & BEF_DBG_PLAN_WRONG)) e = (i & 1) ? (e > 53 ? e - 1 : e + 2) : e + 1;
       plan[i] = e;
-      if (e >= 53) pair[i] = row_pair(i, e);
+      if (e >= 55 || (e >= 53 && (dbg & BEF_DBG_NO_CLOSED_FORM))) pair[i] = row_pair(i, e);
     }
-    out[2] = walk(
-        0, h, [&](int i) { return plan[i]; }, [&](int i) { return R[i]; },
-        [&](int i) { return pair[i]; },
-        [&](uint64_t s, int i) {
-          if (try_exact(&s, R[i])) return s;
-          if (try_apply(&s, pair[i], plan[i])) return s;
-          return fallback_row(s, i);
-        });
+    // the walk block takes the plane kWalkChunk rows at a time
+    uint64_t s = 0;
+    for (int a = 0; a < h; a += kWalkChunk) {
+      const int n = std::min(kWalkChunk, h - a);
+      s = walk_items(
+          s, n, [&](int k) { return plan[a + k]; }, [&](int k) { return R[a + k]; },
+          [&](int k) { return C[a + k]; },
+          [&](int k, int e) {
+            return (e <= 54 && !(dbg & BEF_DBG_NO_CLOSED_FORM)) ? closed_pair(R[a + k], C[a + k], e)
+                                                                : pair[a + k];
+          },
+          [&](uint64_t s2, int k) {
+            const int i = a + k, e = plan[i];
+            if (try_exact(&s2, R[i])) return s2;
+            if (e >= 53 &&
+                try_apply(&s2,
+                          (e <= 54 && !(dbg & BEF_DBG_NO_CLOSED_FORM)) ? closed_pair(R[i], C[i], e)
+                                                                       : pair[i],
+                          e))
+              return s2;
+            return fallback_row(s2, i);
+          });
+    }
+    out[2] = s;
   }
 };
 
@@ -379,7 +487,7 @@ bool bad(const void* a, int w, int h, ptrdiff_t stride, int bpc) {
 extern "C" int bef_host_plane_units(const void* plane, int w, int h, ptrdiff_t stride, int bpc,
                                     unsigned dbg_flags, uint64_t out[3]) {
   if (bad(plane, w, h, stride, bpc) || !out) return -EINVAL;
-  Emu em{Plane{plane, w, h, stride, bpc}, dbg_flags, {}, {}, {}, {}, {}};
+  Emu em{Plane{plane, w, h, stride, bpc}, dbg_flags, {}, {}, {}, {}};
   em.run(out);
   return 0;
 }
@@ -423,6 +531,13 @@ extern "C" int bef_host_fast_noise(const void* ref, const void* dis, int w, int 
 }
 
 extern "C" uint64_t bef_host_rne53_add(uint64_t s, uint64_t t) { return rne53_add(s, t); }
+
+extern "C" int bef_host_load_shape(const void* ref, const void* dis, int w, ptrdiff_t stride,
+                                   ptrdiff_t frame_pitch, int nframes, int out[2]) {
+  if (!out || w <= 0 || nframes <= 0) return -EINVAL;
+  load_shape(ref, dis, w, stride, frame_pitch, nframes, &out[0], &out[1]);
+  return 0;
+}
 
 extern "C" int bef_host_run_pair(const uint32_t* terms, int n, int e, uint64_t out[2]) {
   if (!terms || n < 0 || n > 32768 || e < 53 || e > 62 || !out) return -EINVAL;

@@ -22,8 +22,9 @@
 // the exact sum restores them); across rows they are full 64-bit values.
 //
 // BEF_MUTANT (host test builds only) plants one of the breaks the pages list
-// for this header (ADR-1497, Consequences) so that the host tests can show
-// each one is caught.  0 = none.
+// for this header (ADR-1497, Consequences), or a break in the group step of
+// a crossing row, so that the host tests can show each one is caught.
+// 0 = none.
 #pragma once
 
 #include <stdint.h>
@@ -42,6 +43,14 @@
 namespace bef {
 
 static constexpr uint64_t kTwo53 = 1ull << 53;
+
+// Shape of the ordered kernels' decomposition, shared with the host
+// emulation of their steps so that the two cannot drift apart.
+static constexpr int kWalkThreads = 512;  // threads of a walk block; runs of a crossing row
+static constexpr int kWalkChunk = 4352;   // rows of a plane a walk block holds at a time
+static constexpr int kWalkMaxSeg = 64;    // segments of equal plan a walk takes as segments
+static constexpr int kPairSeg = 4096;     // samples of a row a pair wave stages at a time
+static constexpr int kPairLanes = 64;     // runs of a staged segment, one per lane
 
 // Plan codes for a row or a run.
 static constexpr int kPlanExact = -1;  // every add stays at or below 2^53
@@ -271,6 +280,56 @@ BEF_HD bool fast_apply(uint64_t* s, int g, uint64_t Eg, uint64_t Cg) {
   if (e == kPlanExact) return try_exact(s, Eg);
   if (e == 53 || e == 54) return try_apply(s, closed_pair(Eg, Cg, e), e);
   return false;
+}
+
+// A row the plan does not fit, as at most three groups of consecutive runs
+// (a row adds less than 2^47 units, so it meets at most one binade edge):
+// group 0 exact (S below 2^53: low) or inside binade eA, the binade S is
+// in; group 1 across the edge; group 2 inside e2, eA when low and eA + 1
+// otherwise.  G[k].start is group k's first run (-1 when empty), G[k].P
+// and G[k].PC the exact sum and odd count of the row's terms before it;
+// G[3] is the row's end.  terms(s, a, b) adds the terms of runs [a, b) to
+// s one at a time with the CPU's step; pair_of(k, e, E, C) is group k's
+// pair inside binade e given its exact sum E and odd count C.  Returns
+// false (S untouched) when a group's step does not apply.
+struct GroupStart {
+  uint64_t P, PC;
+  int start;
+};
+
+template <class Terms, class PairOf>
+BEF_HD bool apply_groups(uint64_t* sp, const GroupStart* G, bool low, int eA, Terms terms,
+                         PairOf pair_of) {
+  const int e2 = low ? eA : eA + 1;
+  uint64_t s = *sp;
+  for (int k = 0; k < 3; ++k) {
+    const GroupStart A = G[k];
+    if (A.start < 0) continue;
+    // the group ends where the next non-empty group (or the row) starts
+    const GroupStart B =
+        G[k + 1].start >= 0 ? G[k + 1] : (k == 0 && G[2].start >= 0) ? G[2] : G[3];
+    if (k == 1) {
+#if BEF_MUTANT == 10
+      s += B.P - A.P;  // mutant: the terms across the edge added as one exact sum
+#else
+      s = terms(s, A.start, B.start);
+#endif
+      continue;
+    }
+    if (k == 0 && low) {
+      if (!try_exact(&s, B.P - A.P)) return false;
+      continue;
+    }
+    const int e = k == 0 ? eA : e2;
+#if BEF_MUTANT == 11
+    const uint64_t C = B.PC - G[0].PC;  // mutant: the odd count taken from the row's first group
+#else
+    const uint64_t C = B.PC - A.PC;
+#endif
+    if (!try_apply(&s, pair_of(k, e, B.P - A.P, C), e)) return false;
+  }
+  *sp = s;
+  return true;
 }
 
 // Pair of a run of terms t[0..n) inside binade e: the two trajectories of S

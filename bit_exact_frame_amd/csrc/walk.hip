@@ -37,7 +37,7 @@ namespace {
 // waves).  Every thread calls them with the same arguments; results are
 // uniform.
 
-constexpr int kT = 512;
+constexpr int kT = kWalkThreads;
 constexpr int kWaves = kT / 64;
 
 struct BlockScratch {
@@ -168,7 +168,7 @@ __device__ int debug_plan(int e, int i, unsigned dbg) {
   return e;
 }
 
-constexpr int kChunk = 4352;  // rows held in LDS by the walk
+constexpr int kChunk = kWalkChunk;  // rows held in LDS by the walk
 
 struct RowLds {
   uint64_t R[kChunk];
@@ -313,8 +313,6 @@ __global__ void __launch_bounds__(kT) k_plan(Geometry g, RowArrays ra, unsigned 
 __device__ __forceinline__ bool needs_pair(int e, unsigned dbg) {
   return e >= 55 || (e >= 53 && (dbg & BEF_DBG_NO_CLOSED_FORM));
 }
-
-constexpr int kPairSeg = 4096;  // samples of a row staged per wave at a time
 
 // Samples [s0, s0 + n) of a row into buf (n <= kPairSeg) by one wave: every
 // load is issued before the first store.
@@ -554,7 +552,7 @@ __global__ void __launch_bounds__(256) k_pairs_pipe(Geometry g, RowArrays ra, un
 
 constexpr int kStage = 4096;  // samples of one row staged in LDS by the fast walk
 constexpr int kRowMax = 32768;  // samples of one row staged in LDS by the general walk (max w)
-constexpr int kMaxSeg = 64;   // segments a walk handles as segments
+constexpr int kMaxSeg = kWalkMaxSeg;  // segments a walk handles as segments
 
 struct Seg {
   uint64_t P;   // exact sum of the items before the segment
@@ -785,32 +783,16 @@ struct Walker {
     }
     __syncthreads();
     if (sm.iv[0]) return false;
-    Seg G[4];  // the three groups' starts (start -1: empty), then the end
+    GroupStart G[4];  // the three groups' starts (start -1: empty), then the end
 #pragma unroll
-    for (int k = 0; k < 3; ++k) G[k] = useg[k];
-    G[3] = Seg{tot, totc, nr, 3};
-    uint64_t s = s0;
-#pragma unroll
-    for (int k = 0; k < 3; ++k) {
-      const Seg A = G[k];
-      if (A.start < 0) continue;
-      const Seg B = G[k + 1].start >= 0 ? G[k + 1] : (k == 0 && G[2].start >= 0) ? G[2] : G[3];
-      const uint64_t P1 = B.P, PC1 = B.PC;
-      const int b = B.start;
-      if (k == 1) {
-        s = terms(s, i, A.start * L, min(b * L, w));
-        continue;
-      }
-      if (k == 0 && low) {
-        if (!try_exact(&s, P1 - A.P)) return false;
-        continue;
-      }
-      const int e = k == 0 ? eA : e2;
-      const Pair64 pr = e <= 54 ? closed_pair(P1 - A.P, PC1 - A.PC, e) : (k == 0 ? c0 : c2);
-      if (!try_apply(&s, pr, e)) return false;
-    }
-    *sp = s;
-    return true;
+    for (int k = 0; k < 3; ++k) G[k] = GroupStart{useg[k].P, useg[k].PC, useg[k].start};
+    G[3] = GroupStart{tot, totc, nr};
+    return apply_groups(
+        sp, G, low, eA,
+        [&](uint64_t s, int ra, int rb) { return terms(s, i, ra * L, min(rb * L, w)); },
+        [&](int k, int e, uint64_t Eg, uint64_t Cg) {
+          return e <= 54 ? closed_pair(Eg, Cg, e) : (k == 0 ? c0 : c2);
+        });
   }
 
   // A row the plan does not fit, from S: kT runs of ceil(w/kT) terms, each
@@ -1031,7 +1013,8 @@ struct WEdges {
 // value elast; item_at(k, &e, &cnt) gives any single item.  Each condition
 // is monotone in the item index, so an edge lies in the one lane whose
 // chunk starts false and ends true; that lane's items are then spread one
-// per lane (c <= 64) and scanned again to find the edge's item.
+// per lane, 64 at a time, and scanned again: the first item that meets the
+// condition is the edge.
 template <class ItemAt>
 __device__ __forceinline__ WEdges wave_edges(int n, int c, uint64_t le, uint32_t lc,
                                              uint64_t elast, uint64_t base, uint64_t M,
@@ -1066,25 +1049,36 @@ __device__ __forceinline__ WEdges wave_edges(int n, int c, uint64_t le, uint32_t
     const int owner = __builtin_ctzll(om);
     const unsigned owned = rdl32(own, owner) & pending;
     const int b0 = owner * c, cnt = min(c, n - b0);
-    uint64_t e = 0;
-    uint32_t cc = 0;
-    if (lane < cnt) item_at(b0 + lane, &e, &cc);
-    const uint64_t q = rdl64(P, owner) + wave_excl_scan_u64(e);
-    const uint32_t qc = rdl32(PC, owner) + wave_excl_scan_u32(cc);
-    const unsigned now = lane < cnt ? edge_conds(q, q + e, M) : 0u;
+    uint64_t q0 = rdl64(P, owner);
+    uint32_t qc0 = rdl32(PC, owner);
+    unsigned todo = owned;
+    for (int p0 = 0; p0 < cnt && todo; p0 += 64) {  // the owner's items, 64 at a time
+      const int k = p0 + lane;
+      uint64_t e = 0;
+      uint32_t cc = 0;
+      if (k < cnt) item_at(b0 + k, &e, &cc);
+      const uint64_t q = q0 + wave_excl_scan_u64(e);
+      const uint32_t qc = qc0 + wave_excl_scan_u32(cc);
+      const unsigned now = k < cnt ? edge_conds(q, q + e, M) : 0u;
 #pragma unroll
-    for (int j = 0; j < kEdges; ++j) {
-      if ((owned >> j) & 1u) {
-        const uint64_t m = wave_ballot((now >> j) & 1u);
-        if (m == 0) {
-          r.ok = false;
-          return r;
+      for (int j = 0; j < kEdges; ++j) {
+        if ((todo >> j) & 1u) {
+          const uint64_t m = wave_ballot((now >> j) & 1u);
+          if (m != 0) {
+            const int kk = __builtin_ctzll(m);
+            r.x[j] = b0 + p0 + kk;
+            r.P[j] = rdl64(q, kk);
+            r.PC[j] = rdl32(qc, kk);
+            todo &= ~(1u << j);
+          }
         }
-        const int k = __builtin_ctzll(m);
-        r.x[j] = b0 + k;
-        r.P[j] = rdl64(q, k);
-        r.PC[j] = rdl32(qc, k);
       }
+      q0 = rdl64(q + e, 63);
+      qc0 = rdl32(qc + cc, 63);
+    }
+    if (todo) {  // an owned edge not met: not the premise
+      r.ok = false;
+      return r;
     }
     pending &= ~owned;
   }
@@ -1505,6 +1499,7 @@ __global__ void __launch_bounds__(kT) k_walk(Geometry g, RowArrays ra, double* r
       results[6 * f + 5] = noise / n;
       units[8 * f + 6] = ex;
       units[8 * f + 7] = __builtin_bit_cast(uint64_t, d);
+      ra.paths[3 * f + 2] = fast ? kPathFast : g.may_round ? kPathChain : kPathSums;
     }
     return;
   }
@@ -1513,6 +1508,7 @@ __global__ void __launch_bounds__(kT) k_walk(Geometry g, RowArrays ra, double* r
   const char* plane =
       (const char*)(pl == 0 ? g.ref : g.dis) + (long)f * g.pitch * (g.bpc == 8 ? 1 : 2);
   uint64_t S = 0, E = 0, s1 = 0;
+  uint8_t path = kPathSums;
   if (!g.may_round) {
     uint64_t a = 0, b = 0;
     for (int i = threadIdx.x; i < g.h; i += kT) {
@@ -1562,6 +1558,7 @@ __global__ void __launch_bounds__(kT) k_walk(Geometry g, RowArrays ra, double* r
       __syncthreads();
       fast = fast_ok != 0;
     }
+    path = fast ? kPathFast : kPathGeneral;
     if (!fast) {
       general_walk(plane, g.stride, g.w, g.h, g.bpc == 8, ra.r2 + off, ra.codd + off,
                    ra.r1 + off, ra.plan + off, ra.pairs + 2 * off,
@@ -1580,6 +1577,7 @@ __global__ void __launch_bounds__(kT) k_walk(Geometry g, RowArrays ra, double* r
     units[8 * f + pl] = s1;
     units[8 * f + 2 + pl] = E;
     units[8 * f + 4 + pl] = S;
+    ra.paths[3 * f + pl] = path;
   }
 }
 

@@ -129,6 +129,15 @@ int bef_frames_units(const void *ref, const void *dis, int w, int h,
                      ptrdiff_t stride, ptrdiff_t frame_pitch, int nframes,
                      int bpc, void *stream, uint64_t *units);
 
+/* Diagnostics: the path the walk took for each frame of the last
+ * synchronous batch (bef_frames, bef_frames_units, moment_frame,
+ * psnr_noise) in the process: out[3f + j] for j = 0 ref moments, 1 dis
+ * moments, 2 noise, with 0 = exact sums only (no sum can pass 2^53), 1 =
+ * the one-wave fast path, 2 = the general walk, 3 = the row-by-row double
+ * chain (noise).  Copies min(n, count) bytes to out (HOST; may be NULL)
+ * and returns count = 3 * nframes of that batch (0 before any). */
+int bef_walk_paths(uint8_t *out, int n);
+
 /* Thread-local text of the last failure ("" if none). */
 const char *bef_last_error(void);
 
@@ -177,38 +186,6 @@ void bef_timing_reset(void);
 
 /* Free the device scratch of every device. */
 void bef_release(void);
-
-/* ---- host-only test entry points (no GPU needed) ----
- * They run the steps of the device algorithm (row sums, plan, row pairs by
- * lane runs and an ordered tree, stretch and row walk with fallbacks to runs
- * and terms) on the host, with the same integer step functions as the
- * kernels, on HOST planes.  For tests only. */
-
-/* out = {S1, S2_exact, S2_cpu} of one plane, in units. */
-int bef_host_plane_units(const void *plane, int w, int h, ptrdiff_t stride,
-                         int bpc, unsigned dbg_flags, uint64_t out[3]);
-/* The fast path's decisions on one plane: out = {1 if the fast path
- * applies (else 0, and the general walk takes the plane), S_cpu, S_exact}. */
-int bef_host_fast_units(const void *plane, int w, int h, ptrdiff_t stride,
-                        int bpc, uint64_t out[3]);
-/* The fast noise: out = {1 if it applies, bits of the noise double in
- * units, exact sum}. */
-int bef_host_fast_noise(const void *ref, const void *dis, int w, int h,
-                        ptrdiff_t stride, int bpc, uint64_t out[3]);
-/* *bits = bit pattern of the noise double in units; *exact = exact sum. */
-int bef_host_noise_units(const void *ref, const void *dis, int w, int h,
-                         ptrdiff_t stride, int bpc, uint64_t *bits,
-                         uint64_t *exact);
-/* The one-term step: fl64(s + t) in units. */
-uint64_t bef_host_rne53_add(uint64_t s, uint64_t t);
-/* The 16-bit row kernel's load shape for planes at these addresses (only
- * their alignment is used; nothing is read): out = {bytes per load (16, 8,
- * 4, or 0 for sample by sample), load slots per lane per group}. */
-int bef_host_load_shape(const void *ref, const void *dis, int w,
-                        ptrdiff_t stride, ptrdiff_t frame_pitch, int nframes,
-                        int out[2]);
-/* Pair of a run of terms inside binade e: out = {inc_even, inc_odd}. */
-int bef_host_run_pair(const uint32_t *terms, int n, int e, uint64_t out[2]);
 
 #ifdef __cplusplus
 }

@@ -294,6 +294,32 @@ def test_one_chunk_of_rows_past_2_53(api, orc, h):
     units = api.bef_frames_units(dev(ref), dev(dis), 16)
     assert (units[:, 2] > 1 << 53).all() and (units[:, 2] < 1 << 55).all()
     check_batch(api, orc, ref, dis, 16, label=f"2048x{h}")
+    # at 4352 rows a lane of the fast walk owns 72 rows (more than a wave
+    # scans at once): the edges are still found and the fast path holds
+    paths = api.bef_walk_paths()
+    want = 1 if h <= 4352 else 2
+    assert (paths[:, :2] == want).all(), paths
+
+
+def test_walk_paths(api):
+    """Which path each walk block takes: the one-wave fast path on 16-bit
+    3840x2160 frames (full and half range), exact sums only on 10-bit
+    frames that cannot pass 2^53, the general walk past 2^55 and under a
+    test flag."""
+    cases = [(4, 2, [[1, 1, 1]]), (5, 2, [[1, 1, 1]]), (2, 2, [[0, 0, 0]]), (6, 1, [[2, 2, 1]])]
+    for key, nf, want in cases:
+        ref, dis = synth.make_frames(key, frames=nf)
+        say(f"[gpu] walk paths of workload {key}")
+        api.bef_frames(dev(ref), dev(dis), synth.WORKLOADS[key].bpc, w=synth.WORKLOADS[key].w)
+        paths = api.bef_walk_paths()
+        assert paths.shape == (nf, 3) and (paths == np.array(want)).all(), (key, paths)
+    ref, dis = synth.make_frames(4, frames=1)
+    old = api.bef_debug_set(api.DBG_PLAN_WRONG)
+    try:
+        api.bef_frames(dev(ref), dev(dis), 16)
+    finally:
+        api.bef_debug_set(old)
+    assert (api.bef_walk_paths() == np.array([[2, 2, 3]])).all(), api.bef_walk_paths()
 
 
 def test_tall_plane_past_2_53(api, orc):

@@ -1,12 +1,16 @@
-"""The C-ABI library on the CPU: exported symbols, the integer step functions,
-and the device algorithm's steps run on the host against the oracle.
+"""The C-ABI library and the host emulation on the CPU (no GPU call).
 
-No GPU call is made here: libbef.so is loaded (it links the HIP runtime,
-which loads without a GPU) and only its bef_host_* entry points are called.
-Those run the kernels' decomposition serially with the same step header
-(ADR-1497, Decision: the host test runs the kernels' steps against the CPU
-loop, with real and deliberately wrong plans, and checks the one-term step
-against the double add on 400 000 random pairs and every boundary pair).
+- libbef.so loads (it links the HIP runtime, which loads without a GPU) and
+  exports every symbol include/bef.h declares, and no test entry point.
+- The host emulation library (host_emu.h, built from host_emu.cpp with the
+  kernels' step header and shape constants) runs the kernels' decomposition
+  serially: its one-term step is checked against the hardware double add,
+  its run pairs against brute force, and its walks against the oracle, with
+  real plans and with the test flags' wrong or missing plans (the pages' own
+  host test does the same for their twins: ADR-1497, Decision).
+- Breaks planted in the step header (ADR-1497, Consequences lists most of
+  them) and in the group step of a crossing row each make the emulation
+  disagree with the oracle.
 """
 from __future__ import annotations
 
@@ -31,8 +35,8 @@ HEADER = os.path.join(ROOT, "include", "bef.h")
 
 @pytest.fixture(scope="module")
 def api():
-    from bit_exact_frame_amd import api as _api
-    return _api
+    import emu
+    return emu.Emu()
 
 
 @pytest.fixture(scope="module")
@@ -40,16 +44,28 @@ def orc():
     return oracle.Oracle()
 
 
-def test_every_declared_symbol_is_exported():
-    from bit_exact_frame_amd import api
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+def declared(header):
+    text = re.sub(r"/\*.*?\*/", "", open(header).read(), flags=re.S)
     names = re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)
-    decl = sorted({n for n in names if n not in ("defined",)})
+    return sorted({n for n in names if n not in ("defined",)})
+
+
+def test_every_declared_symbol_is_exported():
+    """libbef.so exports every entry point of include/bef.h and none of the
+    test entry points; the emulation library exports those of host_emu.h."""
+    import emu
+    from bit_exact_frame_amd import api
+    decl = declared(HEADER)
     assert "moment_frame" in decl and "psnr_noise" in decl and "bef_frames" in decl
+    assert "bef_frames_noalloc" in decl
     lib = ctypes.CDLL(api.LIB_PATH)
     missing = [n for n in decl if not hasattr(lib, n)]
     assert not missing, missing
+    test_decl = declared(emu.HEADER)
+    assert test_decl and all(n.startswith("bef_host_") for n in test_decl), test_decl
+    assert not [n for n in test_decl if hasattr(lib, n)]
+    em = emu.Emu()
+    assert not [n for n in test_decl if not hasattr(em.lib, n)]
 
 
 # --------------------------------------------------------------- one step --
@@ -65,14 +81,14 @@ def test_one_term_step_against_double_add(api):
     s = np.maximum(np.round(s), 1.0)
     t = rng.integers(0, 1 << 32, size=n, dtype=np.int64)
     want = (s + t.astype(np.float64))  # IEEE double add, round to nearest even
-    f = api.lib().bef_host_rne53_add
+    f = api.lib.bef_host_rne53_add
     for k in range(n):
         assert f(int(s[k]), int(t[k])) == int(want[k]), (int(s[k]), int(t[k]))
 
 
 def test_one_term_step_boundary_pairs(api):
     """Every pair around the binade edges 2^53..2^58 and around the ties."""
-    f = api.bef_host_rne53_add
+    f = api.rne53_add
     for e in range(53, 59):
         u = 1 << (e - 52)
         for base in (1 << e, (1 << e) - u // 2 if u > 1 else (1 << e) - 1, (1 << (e + 1)) - u):
@@ -115,7 +131,7 @@ def test_run_pair_brute_force(api):
         else:  # small codewords: dense ties and parity flips
             x = rng.integers(0, 9000, size=n)
         terms = tt[x].astype(np.uint32)
-        assert api.bef_host_run_pair(terms, e) == brute_pair(terms.tolist(), e), (e, n)
+        assert api.run_pair(terms, e) == brute_pair(terms.tolist(), e), (e, n)
 
 
 def test_closed_form_premise():
@@ -139,8 +155,8 @@ def test_closed_form_against_runs(api):
         terms = tt[x].astype(np.uint32)
         E = int(terms.astype(np.uint64).sum())
         c = int((terms & 1).sum())
-        assert api.bef_host_run_pair(terms, 53) == [E - c, E - c + (2 if c else 0)]
-        assert api.bef_host_run_pair(terms, 54) == [E - c, E - c]
+        assert api.run_pair(terms, 53) == [E - c, E - c + (2 if c else 0)]
+        assert api.run_pair(terms, 54) == [E - c, E - c]
 
 
 # ------------------------------------------------- host emulation vs oracle --
@@ -181,7 +197,7 @@ FLAGS = [0, 1, 2, 8, 16, 32, 1 | 16 | 32, 2 | 32]
 def test_host_emulation_matches_oracle(api, flags):
     for name, p in planes():
         s1, s2 = oracle_units(name)
-        got = api.bef_host_plane_units(p, 16, dbg=flags)
+        got = api.plane_units(p, 16, dbg=flags)
         assert got[0] == s1, name
         assert got[1] == int(checkers.terms_moment(p).sum(dtype=np.uint64)), name
         assert got[2] == s2, (name, flags, got[2], s2)
@@ -190,7 +206,7 @@ def test_host_emulation_matches_oracle(api, flags):
 def test_host_emulation_terms_only(api):
     """Rows that leave the plan go term by term (a slow path: two frames)."""
     for name, p in planes()[:4]:
-        assert api.bef_host_plane_units(p, 16, dbg=4 | 2)[2] == oracle_units(name)[1], name
+        assert api.plane_units(p, 16, dbg=4 | 2)[2] == oracle_units(name)[1], name
 
 
 @functools.lru_cache(maxsize=None)
@@ -208,7 +224,7 @@ def test_fast_emulation_matches_oracle(api):
     hand the planes past 2^55 to the general walk."""
     cases = list(planes()) + [("letterbox", letterbox_plane())]
     for name, p in cases:
-        got = api.bef_host_fast_units(p, 16)
+        got = api.fast_units(p, 16)
         exact = int(checkers.terms_moment(p).sum(dtype=np.uint64))
         assert got[2] == exact, name
         if exact >= 1 << 55:
@@ -231,11 +247,11 @@ def test_emulation_random_crossings(api, orc, k):
     acc = orc.moment_sums(ref, dis, bpc, w=w)
     want = int(math.ldexp(acc[2], 2 * (bpc - 8)))
     exact = int(checkers.terms_moment(ref[:, :w]).sum(dtype=np.uint64))
-    got = api.bef_host_plane_units(ref, bpc, w=w)
+    got = api.plane_units(ref, bpc, w=w)
     assert got[1] == exact and got[2] == want, (label, got, want)
-    fast = api.bef_host_fast_units(ref, bpc, w=w)
+    fast = api.fast_units(ref, bpc, w=w)
     assert fast[0] == 1 and fast[1] == want and fast[2] == exact, (label, fast, want)
-    fn = api.bef_host_fast_noise(ref, dis, bpc, w=w)
+    fn = api.fast_noise(ref, dis, bpc, w=w)
     noise = orc.psnr_sum(ref, dis, bpc, w=w)
     assert fn[0] == 1, label
     assert np.array([fn[1]], np.uint64).view(np.float64)[0] == math.ldexp(noise, 2 * (bpc - 8)), label
@@ -254,7 +270,7 @@ def noise_pairs():
 
 def test_fast_noise_emulation_matches_oracle(api, orc):
     for name, r, d in noise_pairs():
-        got = api.bef_host_fast_noise(r, d, 16)
+        got = api.fast_noise(r, d, 16)
         noise = orc.psnr_sum(r, d, 16)
         assert got[0] == 1, name
         assert np.array([got[1]], np.uint64).view(np.float64)[0] == math.ldexp(noise, 16), name
@@ -263,7 +279,7 @@ def test_fast_noise_emulation_matches_oracle(api, orc):
 def test_host_noise_matches_oracle(api, orc):
     for key in (4, 5):
         r, d = synth.make_frames(key, frames=1)
-        bits, ex = api.bef_host_noise_units(r[0], d[0], 16)
+        bits, ex = api.noise_units(r[0], d[0], 16)
         noise = orc.psnr_sum(r[0], d[0], 16)
         assert np.array([bits], np.uint64).view(np.float64)[0] == math.ldexp(noise, 16)
         assert ex == checkers.psnr_units(r[0], d[0])[1]
@@ -288,7 +304,7 @@ def test_load_shape_choice(api):
             for extra in (0, 1, 3):
                 stride = w + extra
                 ref = 0x100000 + base_align
-                cb, ng = api.bef_host_load_shape(ref, ref + 0x4000000, w, stride, stride * 9, 2)
+                cb, ng = api.load_shape(ref, ref + 0x4000000, w, stride, stride * 9, 2)
                 assert (cb, ng) in LAUNCHED, (w, base_align, extra, cb, ng)
                 align = 16
                 for v in (ref, ref + 0x4000000, stride * 2, stride * 18):
@@ -319,14 +335,18 @@ MUTANTS = {
     7: "a lane's run order reversed",
     8: "the closed form's +2 from an odd start forgotten",
     9: "a noise row's ties rounded to odd",
+    10: "a crossing row's terms across the edge added as one exact sum",
+    11: "a crossing row group's odd count taken from the row's first group",
 }
 
 
 @pytest.mark.parametrize("mutant", sorted(MUTANTS))
 def test_header_break_is_caught(tmp_path, mutant):
-    """Each of the breaks the pages list for the step header (ADR-1497,
-    Consequences), plus a reversed run order, makes the host emulation
-    disagree with the oracle on at least one frame."""
+    """Each break planted in the step header makes the host emulation
+    disagree with the oracle on at least one frame: the breaks the pages
+    list for their header (ADR-1497, Consequences), a reversed run order, a
+    closed form without its +2, noise ties to odd, and two breaks of the
+    group step of a crossing row."""
     from bit_exact_frame_amd import build as b
     so = b.build_host_emu(os.path.join(tmp_path, f"libemu_m{mutant}.so"), mutant)
     lib = ctypes.CDLL(so)
