@@ -231,7 +231,7 @@ def bef_read_ceiling(ref, dis, out, w: int | None = None, stream=None):
            "bef_read_ceiling")
 
 
-PATHS = {0: "sums", 1: "fast", 2: "general", 3: "chain"}
+PATHS = {0: "sums", 1: "fast", 2: "general", 3: "chain", 4: "skipped"}
 
 
 def bef_walk_paths():

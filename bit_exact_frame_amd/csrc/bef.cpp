@@ -241,6 +241,8 @@ int setup(Call& c, const void* ref, const void* dis, int w, int h, ptrdiff_t str
   const bool force = (g_dbg & BEF_DBG_FORCE_ROUND) != 0;
   g.may_round = (maxsum > kTwo53) || force;
   g.need_odd = g.may_round && bpc != 8;
+  g.job0 = 0;
+  g.njobs = 3;
   c.need_pairs = g.may_round && (maxsum >= (1ull << 55) || g_dbg != 0);
   g.planned = c.need_pairs;
   c.L = layout(nframes, h);
@@ -315,6 +317,14 @@ int run_sync(const void* ref, const void* dis, int w, int h, ptrdiff_t stride, p
   Call c;
   int rc = prepare(c, ref, dis, w, h, stride, pitch, nframes, bpc);
   if (rc) return rc;
+  if (!units && !psnr) {  // the moments alone: no noise walk
+    c.g.njobs = 2;
+  } else if (!units && !moments) {  // the noise alone: no moment walk, plan or pairs
+    c.g.job0 = 2;
+    c.g.njobs = 1;
+    c.need_pairs = false;
+    c.g.planned = 0;
+  }
   hipStream_t st = (hipStream_t)stream;
   if ((rc = check_stream(c, st)) || (rc = enqueue(c, st, c.d_results))) return rc;
   // results, units and walk paths lie together in the scratch: one copy

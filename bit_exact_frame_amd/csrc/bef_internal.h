@@ -24,6 +24,7 @@ struct Geometry {
   int need_odd;  // count odd squares per row (frames that can pass 2^53)
   int may_round; // some frame can pass 2^53 units (or forced)
   int planned;   // k_plan runs before the walk (plan and psum filled)
+  int job0, njobs;  // walk jobs [job0, job0 + njobs) of 0 ref moments, 1 dis moments, 2 noise
 };
 
 // Device scratch, [plane][frame][row] (plane 0 = ref, 1 = dis) unless noted.
@@ -43,6 +44,7 @@ constexpr uint8_t kPathSums = 0;     // no sum can pass 2^53: exact sums only
 constexpr uint8_t kPathFast = 1;     // the one-wave fast path (moments or noise)
 constexpr uint8_t kPathGeneral = 2;  // the general walk (moments)
 constexpr uint8_t kPathChain = 3;    // the row-by-row double chain (noise)
+constexpr uint8_t kPathSkipped = 4;  // the call asked for no result of this job
 
 // Each launch goes out with hipExtLaunchKernel; ev0 / ev1 (or null) are
 // recorded by the dispatch itself at the kernel's start and end.

@@ -17,9 +17,8 @@
 //  - the fast path: the plan as five threshold edges, exact and
 //    closed-form stretches, the rows and terms at an edge one by one, and
 //    noise stretches as composed row pairs.
-// The pages' own host test does the same with the twins' steps (ADR-1497,
-// Decision: the kernels' steps run on the host against the CPU loop, with
-// real and with deliberately wrong plans).
+// The pages' own host test checks their twins' steps the same way, under
+// correct plans and under plans broken on purpose (ADR-1497, Decision).
 #include <errno.h>
 #include <stdint.h>
 #include <stdlib.h>

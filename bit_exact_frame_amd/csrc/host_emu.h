@@ -7,9 +7,9 @@
  * row sums, the per-row plan, row pairs from lane runs of staged segments
  * joined by ordered trees, stretches of rows with one plan, a crossing row
  * as at most three groups of runs, else its runs one by one, else its
- * terms.  The pages' own host test runs the kernels' steps against the CPU
- * loop the same way, with real and with deliberately wrong plans (ADR-1497,
- * Decision).  Arguments as in bef.h, on host pointers; every int function
+ * terms.  The pages' own host test checks their twins' steps against the
+ * CPU loop the same way, under correct plans and plans broken on purpose
+ * (ADR-1497, Decision).  Arguments as in bef.h, on host pointers; every int function
  * returns 0 or -EINVAL.
  */
 #ifndef BEF_HOST_EMU_H

@@ -1429,7 +1429,8 @@ __device__ __noinline__ void general_walk(const char* plane, long stride, int w,
 }
 
 // One 512-thread block per (frame, job): jobs 0 and 1 the moments of ref and
-// dis, job 2 the PSNR noise.  Fast path: every thread loads the rows' sums
+// dis, job 2 the PSNR noise (a call may ask for the moments or the noise
+// alone: jobs [job0, job0 + njobs)).  Fast path: every thread loads the rows' sums
 // into LDS (coalesced), then wave 0 alone walks the plane while the other
 // waves wait at the next barrier (the wave's code has no block barrier);
 // when it does not apply, the whole block takes the general walk.
@@ -1445,7 +1446,10 @@ __global__ void __launch_bounds__(kT) k_walk(Geometry g, RowArrays ra, double* r
   __shared__ __attribute__((aligned(16))) uint16_t wide_row[kRowMax];  // a row the general walk leaves its plan in
   __shared__ int staged, fast_ok;
   __shared__ uint64_t res[3];
-  const int f = blockIdx.x / 3, job = blockIdx.x % 3;
+  const int f = blockIdx.x / g.njobs, job = g.job0 + blockIdx.x % g.njobs;
+  if (threadIdx.x == 0 && job == g.job0)  // jobs the call did not ask for
+    for (int j = 0; j < 3; ++j)
+      if (j < g.job0 || j >= g.job0 + g.njobs) ra.paths[3 * f + j] = kPathSkipped;
   const int k = g.bpc - 8;
   const double n = (double)g.w * (double)g.h;
   const int wave = threadIdx.x >> 6;
@@ -1618,7 +1622,8 @@ hipError_t launch_pairs(const Geometry& g, const RowArrays& ra, unsigned dbg, hi
 
 hipError_t launch_walk(const Geometry& g, const RowArrays& ra, double* results, uint64_t* units,
                        unsigned dbg, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
-  hipExtLaunchKernelGGL(k_walk, dim3(3 * g.nframes), dim3(kT), 0, st, ev0, ev1, 0, g, ra, results, units, dbg);
+  hipExtLaunchKernelGGL(k_walk, dim3(g.njobs * g.nframes), dim3(kT), 0, st, ev0, ev1, 0, g, ra,
+                        results, units, dbg);
   return hipGetLastError();
 }
 

@@ -62,9 +62,13 @@ int moment_frame(const void *ref, const void *dis, int w, int h,
 int psnr_noise(const void *ref, const void *dis, int w, int h,
                ptrdiff_t stride, int bpc, double out[2]);
 
-/* Fused, batched: nframes frames, frame_pitch samples apart (frames are
- * only read, so a pitch below h*stride, i.e. overlapping frames, is
- * allowed).  Each plane is read once for both reductions.
+/* Fused, batched: the float_moment and float_psnr results of nframes
+ * frames, each frame as the CPU extractors compute it once per frame
+ * (ADR-1497, Context; ADR-1499, Context and Decision).  Frames lie
+ * frame_pitch samples apart (frames are only read, so a pitch below
+ * h*stride, i.e. overlapping frames, is allowed).  Each plane is read once
+ * for both reductions; a call with moments or psnr NULL skips the other's
+ * ordered part.
  * stream: a hipStream_t of the planes' device (NULL = that device's default
  * stream; a stream of another device is -EINVAL).  The call enqueues its
  * kernels on that stream and waits once at the end for the results.
@@ -121,7 +125,11 @@ int bef_frames_host(const void *ref, const void *dis, int w, int h,
                     ptrdiff_t stride, ptrdiff_t frame_pitch, int nframes,
                     int bpc, int device, double *moments, double *psnr);
 
-/* Diagnostics: per-frame integer sums in units, synchronously.
+/* Diagnostics: per-frame integer sums in units, synchronously.  In units
+ * of 1/s (first moments) and 1/s^2 (squares) every term and every running
+ * sum of the CPU's double loop is an integer, each step rounding the exact
+ * integer sum to 53 significant bits (ADR-1497, Decision; ADR-1499,
+ * Decision, argument step 1).
  * units (HOST, [nframes][8]) = {S1_ref, S1_dis, S2_ref_exact, S2_dis_exact,
  * S2_ref_cpu, S2_dis_cpu, noise_exact, bits of the noise double in units}.
  * The *_cpu values are the CPU's rounded running sums (integers). */
@@ -134,7 +142,7 @@ int bef_frames_units(const void *ref, const void *dis, int w, int h,
  * psnr_noise) in the process: out[3f + j] for j = 0 ref moments, 1 dis
  * moments, 2 noise, with 0 = exact sums only (no sum can pass 2^53), 1 =
  * the one-wave fast path, 2 = the general walk, 3 = the row-by-row double
- * chain (noise).  Copies min(n, count) bytes to out (HOST; may be NULL)
+ * chain (noise), 4 = not run (the call asked for no result of that job).  Copies min(n, count) bytes to out (HOST; may be NULL)
  * and returns count = 3 * nframes of that batch (0 before any). */
 int bef_walk_paths(uint8_t *out, int n);
 
@@ -142,7 +150,10 @@ int bef_walk_paths(uint8_t *out, int n);
 const char *bef_last_error(void);
 
 /* Test hooks (process-wide, default 0).  Every setting must return the
- * same bits; they only change which path forms them.
+ * same bits; they only change which path forms them: a plan, right or
+ * wrong, decides only whether a row is added as one pair or falls back to
+ * its runs and then its terms (ADR-1497, Decision), so forcing wrong or
+ * missing plans and the fallbacks must leave every result unchanged.
  *   BEF_DBG_PLAN_WRONG  shift every planned binade by one
  *   BEF_DBG_PLAN_NONE   plan no row: every row past 2^53 goes to its runs
  *   BEF_DBG_TERMS_ONLY  rows that leave the plan are added term by term

@@ -1,9 +1,10 @@
 """Seed-built 16-bit frames whose exact second-moment sum sits on 2^53 or
 2^54 units (tests only).
 
-The pages test the twins on frames whose exact sum is 2^53 - 1, 2^53, 2^53
-followed by three dropped ties, and 2^54 followed by seven dropped terms
-(ADR-1497, Decision; ADR-1499, Consequences).  They do not say how those
+The pages check their twins on four such frames: exact sums one unit below
+2^53, exactly 2^53, 2^53 and then three ties the CPU drops, and 2^54 and
+then seven unit terms it drops (ADR-1497, Decision; ADR-1499,
+Consequences).  They do not say how those
 frames were made; this builder is one reading: fill pixels in raster order
 with seeded uniform samples while the remaining distance to the target is
 large, then greedily place the largest sample whose float square (in units)

@@ -180,6 +180,27 @@ def test_single_frame_entry_points(api, orc):
     assert bits(p).tolist() == bits(orc.psnr_noise(ref[0], dis[0], 12, w=wl.w)).tolist()
 
 
+def test_single_output_calls_run_their_walk_only(api, orc):
+    """moment_frame runs no noise walk and psnr_noise no moment walk (nor
+    plan or row pairs), on frames past 2^53 and past 2^55, with the
+    oracle's bits."""
+    for key in (5, 6):
+        wl = synth.WORKLOADS[key]
+        ref, dis = synth.make_frames(key, frames=1)
+        r, d = dev(ref[0]), dev(dis[0])
+        say(f"[gpu] single-output calls on workload {key}")
+        m = api.moment_frame(r, d, 16)
+        assert api.bef_walk_paths()[0, 2] == 4, api.bef_walk_paths()
+        assert (api.bef_walk_paths()[0, :2] != 4).all()
+        p = api.psnr_noise(r, d, 16)
+        assert (api.bef_walk_paths()[0, :2] == 4).all() and api.bef_walk_paths()[0, 2] != 4
+        assert bits(m).tolist() == bits(orc.moment_frame(ref[0], dis[0], 16, w=wl.w)).tolist()
+        assert bits(p).tolist() == bits(orc.psnr_noise(ref[0], dis[0], 16, w=wl.w)).tolist()
+        mom, ps = api.bef_frames(r[None], d[None], 16)
+        assert (api.bef_walk_paths() != 4).all()
+        assert bits(mom[0]).tolist() == bits(m).tolist() and bits(ps[0]).tolist() == bits(p).tolist()
+
+
 DEBUG = [1, 2, 4, 8, 16, 32, 1 | 16, 2 | 32, 8 | 32, 32 | 64]
 
 
@@ -187,7 +208,7 @@ DEBUG = [1, 2, 4, 8, 16, 32, 1 | 16, 2 | 32, 8 | 32, 32 | 64]
 def test_debug_paths_same_bits(api, orc, flags):
     """Wrong plans, no plans, terms only, forced rounding, no stretches, no
     closed form, row pairs in many small dispatches: every path must give
-    the CPU's bits (ADR-1497, Decision: any plan, even a wrong one, only
+    the CPU's bits (ADR-1497, Decision: a plan, right or wrong, only
     changes which increments are used)."""
     r4, d4 = synth.make_frames(4, frames=2)
     r5, d5 = synth.make_frames(5, frames=1)

@@ -71,7 +71,7 @@ def test_every_declared_symbol_is_exported():
 # --------------------------------------------------------------- one step --
 
 def test_one_term_step_against_double_add(api):
-    """fl64(S + t) in units for 400 000 random pairs: S a double holding an
+    """fl64(S + t) in units for 400 000 random (S, t): S a double holding an
     integer between 2^50 and 2^58, t below 2^32."""
     rng = np.random.Generator(np.random.PCG64(53))
     n = 400_000
