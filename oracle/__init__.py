@@ -26,6 +26,7 @@ LIB = os.path.join(HERE, "liboracle.so")
 # arithmetic in float, double in double, round to nearest even.
 CFLAGS = ["-std=c99", "-O2", "-fno-fast-math", "-ffp-contract=off",
           "-fPIC", "-shared", "-Wall", "-Wextra"]
+LIBS = ["-lm"]
 
 _lock = threading.Lock()
 _lib = None
@@ -33,7 +34,7 @@ _lib = None
 
 def build(out: str = LIB, mutant: int = 0) -> str:
     """Compile oracle.c into ``out``; ``mutant`` plants a test mistake."""
-    cmd = ["gcc", *CFLAGS, f"-DORACLE_MUTANT={int(mutant)}", SRC, "-o", out]
+    cmd = ["gcc", *CFLAGS, f"-DORACLE_MUTANT={int(mutant)}", SRC, "-o", out, *LIBS]
     subprocess.run(cmd, check=True, cwd=HERE)
     return out
 
@@ -54,6 +55,8 @@ def _bind(lib):
     lib.oracle_psnr_sum.restype = i
     lib.oracle_frames.argtypes = [vp, vp, i, i, pd, pd, i, i, dp, dp]
     lib.oracle_frames.restype = i
+    lib.oracle_psnr_db.argtypes = [ctypes.c_double, i]
+    lib.oracle_psnr_db.restype = ctypes.c_double
     return lib
 
 
@@ -91,6 +94,10 @@ class Oracle:
     def _geom(plane: np.ndarray, w: int | None, stride: int | None):
         h, s = plane.shape[-2], plane.shape[-1]
         return (s if w is None else w), h, (s if stride is None else stride)
+
+    def psnr_db(self, mse: float, bpc: int) -> float:
+        """PSNR in dB from an MSE (a reading; parity unpinned)."""
+        return float(self.lib.oracle_psnr_db(float(mse), int(bpc)))
 
     def fsq(self, x: int, bpc: int) -> float:
         return float(self.lib.oracle_fsq(int(x), int(bpc)))

@@ -32,6 +32,7 @@
 #include "oracle.h"
 
 #include <float.h>
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 
@@ -288,3 +289,21 @@ int oracle_frames(const void *ref, const void *dis, int w, int h,
     }
     return 0;
 }
+
+/* PSNR in dB of a plane from its MSE, as this project reads it (the pages
+ * name the psnr_y / psnr_cb / psnr_cr features of integer_psnr and a
+ * float_psnr score, but print no formula or constant: Metal kernel batch
+ * digest, Feature scope).  Reading: the textbook 10 * log10(peak^2 / MSE)
+ * with peak the largest normalised sample, (2^bpc - 1) / 2^(bpc - 8); no
+ * clamp, so MSE 0 gives +infinity.  PARITY UNPINNED against the pages. */
+double oracle_psnr_db(double mse, int bpc)
+{
+    if (bpc < 8 || bpc > 16) return NAN;
+#if ORACLE_MUTANT == 15
+    const double peak = 255.0; /* mutant: the peak of 8-bit samples at every depth */
+#else
+    const double peak = (double)((1u << bpc) - 1u) / (double)(1u << (bpc - 8));
+#endif
+    return 10.0 * log10(peak * peak / mse);
+}
+

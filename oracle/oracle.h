@@ -62,6 +62,12 @@ int oracle_frames(const void *ref, const void *dis, int w, int h,
                   ptrdiff_t stride, ptrdiff_t frame_pitch, int nframes,
                   int bpc, double *moments, double *psnr);
 
+/* PSNR in dB from an MSE (true scale) at bit depth bpc: 10 log10(peak^2 /
+ * mse), peak = (2^bpc - 1) / 2^(bpc - 8); +infinity for mse 0; NaN for bpc
+ * outside [8, 16].  The pages give no formula: this is a reading, parity
+ * unpinned against them. */
+double oracle_psnr_db(double mse, int bpc);
+
 #ifdef __cplusplus
 }
 #endif

@@ -332,6 +332,40 @@ def check_frames_batch(orc):
                                   float(Fraction(dc, 65536 * n))], (k, ps[k])
 
 
+def _db_exact(mse: float, bpc: int):
+    """10 log10(peak^2 / mse) to 40 digits with the decimal module (no libm),
+    peak = (2^bpc - 1) / 2^(bpc - 8) as an exact rational."""
+    import decimal
+    ctx = decimal.Context(prec=40)
+    peak2 = Fraction((1 << bpc) - 1, 1 << (bpc - 8)) ** 2
+    ratio = peak2 / Fraction(mse)
+    d = ctx.divide(decimal.Decimal(ratio.numerator), decimal.Decimal(ratio.denominator))
+    return ctx.multiply(decimal.Decimal(10), d.log10(ctx))
+
+
+def check_psnr_db(orc):
+    """The dB reading (parity unpinned against the pages, which give no
+    formula): the oracle's 10 log10(peak^2 / MSE) is within the rounding
+    bound of the value computed to 40 digits without libm, for every
+    bit depth and MSEs across the range; MSE 0 gives +infinity; an MSE of
+    peak^2 / 10^k gives 10k dB to within that bound."""
+    rng = np.random.Generator(np.random.PCG64(1010))
+    for bpc in range(8, 17):
+        peak2 = (((1 << bpc) - 1) / (1 << (bpc - 8))) ** 2
+        mses = [float(x) for x in np.exp(rng.uniform(np.log(1e-6), np.log(7e4), size=40))]
+        mses += [peak2 / 10.0 ** k for k in range(0, 7)] + [1.0, peak2]
+        for mse in mses:
+            got = orc.psnr_db(mse, bpc)
+            want = float(_db_exact(mse, bpc))
+            # rounding of peak^2 / mse (relative 2^-53) moves the dB by up to
+            # 10 / ln 10 * 2^-53 < 1e-15 absolute; log10 and the factor 10
+            # add a few units in the last place of the result
+            assert abs(want - got) <= 4 * math.ulp(want) + 1e-15, (bpc, mse, got, want)
+        for k in range(0, 7):
+            assert abs(orc.psnr_db(peak2 / 10.0 ** k, bpc) - 10 * k) < 1e-12, (bpc, k)
+        assert orc.psnr_db(0.0, bpc) == math.inf
+
+
 def check_bad_args(orc):
     """Invalid geometry or bit depth is rejected, not computed."""
     import ctypes
@@ -360,5 +394,6 @@ ALL_CHECKS = [
     check_past_2_53,
     check_boundary_frames,
     check_frames_batch,
+    check_psnr_db,
     check_bad_args,
 ]
