@@ -43,8 +43,9 @@ _lib.bef_frames_noalloc.argtypes = [_vp, _vp, _i, _i, _pd, _pd, _i, _i, _vp, _vp
 _lib.bef_frames_units.argtypes = [_vp, _vp, _i, _i, _pd, _pd, _i, _i, _vp, _u64p]
 _lib.bef_read_ceiling.argtypes = [_vp, _vp, _i, _i, _pd, _pd, _i, _vp, _vp]
 _lib.bef_frames_host.argtypes = [_vp, _vp, _i, _i, _pd, _pd, _i, _i, _i, _dp, _dp]
+_lib.bef_planes.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _dp]
 for _n in ("moment_frame", "psnr_noise", "bef_frames", "bef_frames_async", "bef_frames_noalloc",
-           "bef_frames_units", "bef_read_ceiling", "bef_frames_host"):
+           "bef_frames_units", "bef_read_ceiling", "bef_frames_host", "bef_planes"):
     getattr(_lib, _n).restype = _i
 _lib.bef_last_error.restype = ctypes.c_char_p
 _lib.bef_walk_paths.argtypes = [_vp, _i]
@@ -149,6 +150,33 @@ def bef_frames(ref, dis, bpc: int, w: int | None = None, stream=None):
                            bpc, _stream_ptr(stream), mom.ctypes.data_as(_dp),
                            ps.ctypes.data_as(_dp)), "bef_frames")
     return mom, ps
+
+
+def bef_planes(refs, diss, bpc: int, ws=None, stream=None):
+    """Several planes of each frame (e.g. Y, Cb, Cr), one call: refs[p] and
+    diss[p] are device tensors (F, h_p, stride_p) (or (h_p, stride_p)), with
+    the same F for every plane; ws[p] the width (default stride_p).
+    Returns float64 [P, F, 7]: ref_1st, dis_1st, ref_2nd, dis_2nd, noise,
+    mse, psnr_db (the dB value is a reading: parity unpinned)."""
+    n = len(refs)
+    if n != len(diss) or not 1 <= n <= 4:
+        raise BefError("refs and diss must list the same 1..4 planes")
+    ws = [None] * n if ws is None else list(ws)
+    geo = [_pair(refs[p], diss[p], bpc, ws[p]) for p in range(n)]
+    f = geo[0][0]
+    if any(g[0] != f for g in geo):
+        raise BefError("every plane needs the same number of frames")
+    P = ctypes.c_void_p * n
+    rp = P(*[refs[p].data_ptr() for p in range(n)])
+    dp = P(*[diss[p].data_ptr() for p in range(n)])
+    w = (ctypes.c_int * n)(*[g[3] for g in geo])
+    h = (ctypes.c_int * n)(*[g[1] for g in geo])
+    st = (ctypes.c_ssize_t * n)(*[g[2] for g in geo])
+    pt = (ctypes.c_ssize_t * n)(*[g[1] * g[2] for g in geo])
+    out = np.zeros((n, f, 7), np.float64)
+    _check(_lib.bef_planes(rp, dp, w, h, st, pt, n, f, bpc, _stream_ptr(stream),
+                           out.ctypes.data_as(_dp)), "bef_planes")
+    return out
 
 
 def _host_geom(t, bpc, w):

@@ -35,6 +35,7 @@ thread_local char g_err[512];
 unsigned g_dbg = 0;
 
 constexpr int kMaxDev = 64;
+constexpr int kMaxPlanes = 4;  // planes of one bef_planes call
 struct Arena {
   void* base = nullptr;
   size_t cap = 0;
@@ -514,6 +515,55 @@ int bef_frames_noalloc(const void* ref, const void* dis, int w, int h, ptrdiff_t
   }
   bind(c, (char*)ptr);
   return enqueue(c, (hipStream_t)stream, dev_results, false);
+}
+
+int bef_planes(const void* const* refs, const void* const* diss, const int* ws, const int* hs,
+               const ptrdiff_t* strides, const ptrdiff_t* frame_pitches, int nplanes,
+               int nframes, int bpc, void* stream, double* out) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  clear_err();
+  if (!refs || !diss || !ws || !hs || !strides || !frame_pitches || !out)
+    return fail(-EINVAL, "NULL argument array or output");
+  if (nplanes < 1 || nplanes > kMaxPlanes)
+    return fail(-EINVAL, "nplanes %d outside 1..%d", nplanes, kMaxPlanes);
+  DevGuard dg;
+  Call c[kMaxPlanes];
+  size_t rows_bytes = 0;
+  for (int p = 0; p < nplanes; ++p) {
+    int rc = setup(c[p], refs[p], diss[p], ws[p], hs[p], strides[p], frame_pitches[p], nframes,
+                   bpc);
+    if (rc) return rc;
+    if (c[p].dev != c[0].dev) return fail(-EINVAL, "plane %d on another device", p);
+    rows_bytes = std::max(rows_bytes, c[p].L.total);
+  }
+  const hipStream_t st = (hipStream_t)stream;
+  int rc = check_stream(c[0], st);
+  if (rc) return rc;
+  // the planes run one after another on the stream and share the row arrays;
+  // each plane's results, then every dB value, lie after them
+  const size_t nres = (size_t)nplanes * nframes;
+  const size_t res_off = up256(rows_bytes), db_off = res_off + up256(nres * 6 * 8);
+  const size_t total = db_off + up256(nres * 8);
+  if ((rc = ensure(c[0].dev, total, total - res_off))) return rc;
+  char* base = (char*)g_arena[c[0].dev].base;
+  double* d_res = (double*)(base + res_off);
+  double* d_db = (double*)(base + db_off);
+  for (int p = 0; p < nplanes; ++p) {
+    bind(c[p], base);
+    if ((rc = enqueue(c[p], st, d_res + (size_t)p * nframes * 6))) return rc;
+  }
+  BEF_HIP(launch_psnr_db(d_res, (int)nres, bpc, d_db, st));
+  char* hb = (char*)g_arena[c[0].dev].host;
+  BEF_HIP(hipMemcpyAsync(hb, d_res, total - res_off, hipMemcpyDeviceToHost, st));
+  BEF_HIP(hipStreamSynchronize(st));
+  if (g_timing) ev_collect();
+  const double* hres = (const double*)hb;
+  const double* hdb = (const double*)(hb + (db_off - res_off));
+  for (size_t k = 0; k < nres; ++k) {
+    for (int j = 0; j < 6; ++j) out[7 * k + j] = hres[6 * k + j];
+    out[7 * k + 6] = hdb[k];
+  }
+  return 0;
 }
 
 int bef_read_ceiling(const void* ref, const void* dis, int w, int h, ptrdiff_t stride,

@@ -56,6 +56,7 @@ hipError_t launch_pairs(const Geometry& g, const RowArrays& ra, unsigned dbg, hi
                         hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_read_ceiling(const Geometry& g, uint32_t* out, hipStream_t st, hipEvent_t ev0,
                                hipEvent_t ev1);
+hipError_t launch_psnr_db(const double* results, int n, int bpc, double* db, hipStream_t st);
 hipError_t launch_walk(const Geometry& g, const RowArrays& ra, double* results, uint64_t* units,
                        unsigned dbg, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
 

@@ -1585,9 +1585,28 @@ __global__ void __launch_bounds__(kT) k_walk(Geometry g, RowArrays ra, double* r
   }
 }
 
+// PSNR in dB of n planes-frames from their MSE (results[6 * k + 5]), read
+// as 10 log10(peak^2 / MSE) with peak the largest normalised sample,
+// (2^bpc - 1) / 2^(bpc - 8); MSE 0 gives +infinity.  The pages name the
+// per-plane PSNR scores but give no formula (Metal kernel batch digest,
+// Feature scope): this is the project's reading.
+__global__ void __launch_bounds__(256) k_psnr_db(const double* results, int n, int bpc,
+                                                 double* db) {
+  const int k = (int)(blockIdx.x * 256 + threadIdx.x);
+  if (k >= n) return;
+  const double peak = (double)((1u << bpc) - 1u) / (double)(1u << (bpc - 8));
+  db[k] = 10.0 * log10(peak * peak / results[6 * (long)k + 5]);
+}
+
 }  // namespace
 
 namespace bef {
+
+hipError_t launch_psnr_db(const double* results, int n, int bpc, double* db, hipStream_t st) {
+  hipLaunchKernelGGL(k_psnr_db, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, results, n,
+                     bpc, db);
+  return hipGetLastError();
+}
 
 hipError_t launch_plan(const Geometry& g, const RowArrays& ra, unsigned dbg, hipStream_t st,
                        hipEvent_t ev0, hipEvent_t ev1) {

@@ -196,3 +196,30 @@ def widened_frames(mode: str, frames: int, h: int = 2160, w: int = 3840):
             d = (d8 << 8) | rng.integers(0, 256, size=(h, w))
         ref[k], dis[k] = r, d
     return ref, dis
+
+
+def yuv420_frames(seed: int, frames: int, w: int, h: int, bpc: int, pad: int = 0,
+                  lo: int = 0, hi: int | None = None, noise: float | None = None):
+    """Seeded 4:2:0 pictures: a luma plane of w x h and two chroma planes of
+    ceil(w/2) x ceil(h/2), each row padded by ``pad`` samples of the
+    container's top value.  ref is uniform [lo, hi); dis is independent
+    uniform, or ref plus rint(N(0, noise^2)) clipped to [0, 2^bpc - 1] when
+    ``noise`` is given.  Returns [(ref, dis)] per plane, arrays (F, h_p, w_p + pad)."""
+    dtype = np.uint8 if bpc == 8 else np.uint16
+    top = np.iinfo(dtype).max
+    hi = (1 << bpc) if hi is None else hi
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([SEED, 420, seed])))
+    out = []
+    for (pw, ph) in ((w, h), ((w + 1) // 2, (h + 1) // 2), ((w + 1) // 2, (h + 1) // 2)):
+        ref = np.full((frames, ph, pw + pad), top, dtype=dtype)
+        dis = np.full((frames, ph, pw + pad), top, dtype=dtype)
+        r = rng.integers(lo, hi, size=(frames, ph, pw))
+        if noise is None:
+            d = rng.integers(lo, hi, size=(frames, ph, pw))
+        else:
+            d = np.clip(r + np.rint(rng.normal(0.0, noise, size=r.shape)), 0, (1 << bpc) - 1)
+        ref[:, :, :pw] = r
+        dis[:, :, :pw] = d
+        out.append((ref, dis))
+    return out
+

@@ -110,6 +110,25 @@ int bef_frames_noalloc(const void *ref, const void *dis, int w, int h,
                        ptrdiff_t stride, ptrdiff_t frame_pitch, int nframes,
                        int bpc, void *stream, double *dev_results);
 
+/* Several planes of each frame (luma and chroma, e.g. Y, Cb, Cr of 4:2:0
+ * pictures, or any up to 4 planes), each with its own geometry, in one
+ * synchronous call: per plane the float_moment and float_psnr results of
+ * every frame (each plane as bef_frames computes it), and the plane's PSNR
+ * in dB (the Metal kernel batch digest, Feature scope, names per-plane
+ * PSNR features psnr_y / psnr_cb / psnr_cr without a formula; the dB value
+ * here is the reading 10 log10(peak^2 / MSE), peak = (2^bpc - 1) /
+ * 2^(bpc - 8), +infinity when MSE is 0 -- PARITY UNPINNED against the
+ * pages).
+ * refs[p], diss[p]: DEVICE planes of plane p; ws, hs, strides,
+ * frame_pitches: per-plane geometry (samples), each as in bef_frames; all
+ * planes on one device, common nframes and bpc; 1 <= nplanes <= 4.
+ * out (HOST, [nplanes][nframes][7]) = {ref_1st, dis_1st, ref_2nd, dis_2nd,
+ * noise, mse, psnr_db}.  The planes run one after another on stream. */
+int bef_planes(const void *const *refs, const void *const *diss,
+               const int *ws, const int *hs, const ptrdiff_t *strides,
+               const ptrdiff_t *frame_pitches, int nplanes, int nframes,
+               int bpc, void *stream, double *out);
+
 /* As bef_frames, for frames in HOST memory (ref, dis: host pointers, same
  * layout and limits), on device `device`, synchronously.  The library
  * streams the frames through two device slots of up to 64 MiB per plane:

@@ -88,3 +88,20 @@ def test_width_beyond_the_planes_is_refused(api):
         api.bef_frames(ref, dis, 16, w=17)
     with pytest.raises(api.BefError, match="outside"):
         api.bef_frames(ref, dis, 16, w=0)
+
+
+def test_planes_binding_checks(api):
+    """bef_planes refuses planes with different frame counts, more than four
+    planes, and a mismatched dis in any plane, before any C call."""
+    y = DevPlane(torch.zeros((2, 8, 16), dtype=torch.uint16))
+    c = DevPlane(torch.zeros((2, 4, 8), dtype=torch.uint16))
+    c1 = DevPlane(torch.zeros((1, 4, 8), dtype=torch.uint16))
+    with pytest.raises(api.BefError, match="frames"):
+        api.bef_planes([y, c1], [y, c1], 16)
+    with pytest.raises(api.BefError):
+        api.bef_planes([y, c, c, c, c], [y, c, c, c, c], 16)
+    with pytest.raises(api.BefError):
+        api.bef_planes([y, c], [y, DevPlane(torch.zeros((2, 4, 7), dtype=torch.uint16))], 16)
+    with pytest.raises(api.BefError):
+        api.bef_planes([y, c], [y], 16)
+
