@@ -92,9 +92,9 @@ struct Emu {
 
   // Row pair under binade e: the closed form in the binades of 2^53 and
   // 2^54; otherwise the row pair kernel's: segments of kPairSeg samples,
-  // each split into kPairLanes runs of ceil(n / kPairLanes) terms (two
-  // trajectories each) joined by a balanced tree, the segments joined in
-  // row order, widened with the row's exact sum.
+  // each split into kPairLanes runs of ceil(n / kPairLanes) terms (each
+  // added from both starts with the double add) joined by a balanced tree,
+  // the segments joined in row order, widened with the row's exact sum.
   Pair64 row_pair(int i, int e) const {
     if (e <= 54 && !(dbg & BEF_DBG_NO_CLOSED_FORM)) return closed_pair(R[i], C[i], e);
     const int sh = e - 52, w = pl.w;
@@ -104,7 +104,7 @@ struct Emu {
       std::vector<Pair32> lanes(kPairLanes);
       for (int l = 0; l < kPairLanes; ++l) {
         const int j0 = std::min(l * L, n), j1 = std::min(j0 + L, n);
-        lanes[l] = run_pair([&](int j) { return T(i, s0 + j0 + j); }, j1 - j0, sh);
+        lanes[l] = run_pair([&](int j) { return (double)T(i, s0 + j0 + j); }, j1 - j0, e);
       }
       acc = then32(acc, tree32(lanes, sh), sh);
     }
@@ -192,7 +192,7 @@ struct Emu {
         if (!((g[t] == 0 && tree0) || (g[t] == 2 && tree2))) continue;
         const int e = g[t] == 0 ? eA : e2, j0 = std::min(t * L, w), j1 = std::min(j0 + L, w);
         const Pair64 pr =
-            widen_pair(run_pair([&](int j) { return T(i, j0 + j); }, j1 - j0, e - 52), E[t]);
+            widen_pair(run_pair([&](int j) { return (double)T(i, j0 + j); }, j1 - j0, e), E[t]);
         (g[t] == 0 ? l0 : l2)[t] = pr;
       }
       for (int wv = 0; wv < kWalkThreads / 64; ++wv) {
@@ -241,8 +241,8 @@ struct Emu {
         const Pair64 p =
             (e <= 54 && !(dbg & BEF_DBG_NO_CLOSED_FORM))
                 ? closed_pair(E[t], c[t], e)
-                : widen_pair(run_pair([&](int j) { return T(i, j0[t] + j); }, j1[t] - j0[t],
-                                      e - 52),
+                : widen_pair(run_pair([&](int j) { return (double)T(i, j0[t] + j); }, j1[t] - j0[t],
+                                      e),
                              E[t]);
         (qq ? pB : pA)[t] = p;
       }
@@ -542,7 +542,7 @@ extern "C" int bef_host_run_pair(const uint32_t* terms, int n, int e, uint64_t o
   if (!terms || n < 0 || n > 32768 || e < 53 || e > 62 || !out) return -EINVAL;
   uint64_t E = 0;
   for (int j = 0; j < n; ++j) E += terms[j];
-  const Pair64 p = widen_pair(run_pair([&](int j) { return terms[j]; }, n, e - 52), E);
+  const Pair64 p = widen_pair(run_pair([&](int j) { return (double)terms[j]; }, n, e), E);
   out[0] = p.a0;
   out[1] = p.a1;
   return 0;

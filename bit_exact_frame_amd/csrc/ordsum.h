@@ -71,7 +71,11 @@ BEF_HD uint64_t rne53_add(uint64_t s, uint64_t t) {
   const uint64_t r = n & ((1ull << sh) - 1);
   uint64_t q = n - r;
   const uint64_t half = 1ull << (sh - 1);
+#if BEF_MUTANT == 1
+  if (r > half || (r == half && !((q >> sh) & 1))) q += 1ull << sh;  // mutant: a tie to the odd value
+#else
   if (r > half || (r == half && ((q >> sh) & 1))) q += 1ull << sh;
+#endif
   return q;
 #endif
 }
@@ -88,21 +92,23 @@ BEF_HD uint32_t fsq_units(uint32_t x) {
 #endif
 }
 
-// One term of a run inside binade e (sh = e - 52, u = 2^sh): v holds S
-// modulo 2^32 (a multiple of u); returns S + t rounded to a multiple of u,
-// ties to the even multiple, modulo 2^32.
-BEF_HD uint32_t traj_step(uint32_t v, uint32_t t, int sh) {
-#if BEF_MUTANT == 4
-  sh = sh - 1;  // mutant: the run's units taken from the wrong binade
-#endif
-  const uint32_t u = 1u << sh;
-  const uint32_t z = v + t;
-#if BEF_MUTANT == 1
-  const uint32_t lsb = 1u - ((z >> sh) & 1u);  // mutant: ties to odd
+// The same float square as a double (exact: it has 24 significant bits).
+BEF_HD double fsq_f64(uint32_t x) {
+  const float f = (float)x;
+#if defined(__HIP_DEVICE_COMPILE__)
+  return (double)__fmul_rn(f, f);
 #else
-  const uint32_t lsb = (z >> sh) & 1u;
+  volatile float p = f * f;  // a float multiply, never contracted
+  return (double)p;
 #endif
-  return (z + ((u >> 1) - 1u) + lsb) & ~(u - 1u);
+}
+
+// 2^e as a double (-1022 <= e <= 1023).
+BEF_HD double pow2(int e) {
+  const uint64_t b = (uint64_t)(e + 1023) << 52;
+  double d;
+  __builtin_memcpy(&d, &b, 8);
+  return d;
 }
 
 struct Pair32 {
@@ -332,22 +338,47 @@ BEF_HD bool apply_groups(uint64_t* sp, const GroupStart* G, bool low, int eA, Te
   return true;
 }
 
-// Pair of a run of terms t[0..n) inside binade e: the two trajectories of S
-// modulo 2^32 from an even and from an odd start.
-template <class Terms>
-BEF_HD Pair32 run_pair(const Terms& terms, int n, int sh) {
-  const uint32_t u = 1u << sh;
-  uint32_t v0 = 0u, v1 = u;
-#if BEF_MUTANT == 7
-  for (int j = n - 1; j >= 0; --j) {  // mutant: run order reversed in a lane
-#else
-  for (int j = 0; j < n; ++j) {
+// A run of terms added inside binade e (e >= 53), with the double add
+// itself.  Inside a binade a term's move depends on S only through the
+// parity of S/u, u = 2^(e-52) (ADR-1497, Decision), so the two starts S = 2^e
+// (S/u even) and 2^e + u (odd) stand for every S of the binade.  From each,
+// every term is added as the CPU adds it: the double add rounds the exact
+// sum to a multiple of u, the ulp there, ties to the even multiple.  The
+// sums stay inside the binade while the run adds less than 2^e - u: a run
+// of at most 2^15 terms adds less than 2^47.  The pair is the two moves,
+// kept modulo 2^32 like every lane-level pair.
+struct RunF64 {
+  double v0, v1;
+};
+BEF_HD RunF64 run_start(int e) {
+#if BEF_MUTANT == 4
+  e = e - 1;  // mutant: the run's units taken from the wrong binade
 #endif
-    const uint32_t t = terms(j);
-    v0 = traj_step(v0, t, sh);
-    v1 = traj_step(v1, t, sh);
-  }
-  return Pair32{v0, v1 - u};
+  const double b = pow2(e);
+  return RunF64{b, b + pow2(e - 52)};
+}
+BEF_HD void run_add(RunF64& r, double t) {
+  r.v0 = r.v0 + t;
+  r.v1 = r.v1 + t;
+}
+BEF_HD Pair32 run_end(const RunF64& r, int e) {
+#if BEF_MUTANT == 4
+  e = e - 1;
+#endif
+  const double b = pow2(e), u = pow2(e - 52);
+  return Pair32{(uint32_t)(uint64_t)(r.v0 - b), (uint32_t)(uint64_t)(r.v1 - b - u)};
+}
+
+// Pair of a run of n terms (terms(j): each term as a double) inside binade e.
+template <class Terms>
+BEF_HD Pair32 run_pair(const Terms& terms, int n, int e) {
+  RunF64 r = run_start(e);
+#if BEF_MUTANT == 7
+  for (int j = n - 1; j >= 0; --j) run_add(r, terms(j));  // mutant: run order reversed in a lane
+#else
+  for (int j = 0; j < n; ++j) run_add(r, terms(j));
+#endif
+  return run_end(r, e);
 }
 
 }  // namespace bef

@@ -380,21 +380,16 @@ __global__ void __launch_bounds__(256) k_pairs(Geometry g, RowArrays ra, unsigne
     Pair32 p;
     if ((L & 7) == 0 && (j1 - j0) == L) {
       // a whole run of 8-sample chunks: one 16-byte LDS read per 8 terms,
-      // the two trajectories stepped term by term in order
-      const uint32_t u = 1u << sh;
-      uint32_t v0 = 0u, v1 = u;
+      // each term added from both starts with the double add, in order
+      RunF64 r = run_start(e);
       for (int c = j0 >> 3; c < (j0 + L) >> 3; ++c) {
         const v4u x = ((const v4u*)buf)[c];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const uint32_t t = fsq_units((x[q >> 1] >> (16 * (q & 1))) & 0xFFFFu);
-          v0 = traj_step(v0, t, sh);
-          v1 = traj_step(v1, t, sh);
-        }
+        for (int q = 0; q < 8; ++q) run_add(r, fsq_f64((x[q >> 1] >> (16 * (q & 1))) & 0xFFFFu));
       }
-      p = Pair32{v0, v1 - u};
+      p = run_end(r, e);
     } else {
-      p = run_pair([&](int j) { return fsq_units(buf[j0 + j]); }, j1 - j0, sh);
+      p = run_pair([&](int j) { return fsq_f64(buf[j0 + j]); }, j1 - j0, e);
     }
     for (int off = 1; off < 64; off <<= 1) {
       Pair32 o;
@@ -491,20 +486,15 @@ __global__ void __launch_bounds__(256) k_pairs_pipe(Geometry g, RowArrays ra, un
     const int j0 = min(lane * L, n), j1 = min(j0 + L, n);
     Pair32 p;
     if ((L & 7) == 0 && (j1 - j0) == L) {
-      const uint32_t u = 1u << sh;
-      uint32_t v0 = 0u, v1 = u;
+      RunF64 r = run_start(sh + 52);
       for (int c = j0 >> 3; c < (j0 + L) >> 3; ++c) {
         const v4u x = ((const v4u*)buf)[c];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const uint32_t t = fsq_units((x[q >> 1] >> (16 * (q & 1))) & 0xFFFFu);
-          v0 = traj_step(v0, t, sh);
-          v1 = traj_step(v1, t, sh);
-        }
+        for (int q = 0; q < 8; ++q) run_add(r, fsq_f64((x[q >> 1] >> (16 * (q & 1))) & 0xFFFFu));
       }
-      p = Pair32{v0, v1 - u};
+      p = run_end(r, sh + 52);
     } else {
-      p = run_pair([&](int j) { return fsq_units(buf[j0 + j]); }, j1 - j0, sh);
+      p = run_pair([&](int j) { return fsq_f64(buf[j0 + j]); }, j1 - j0, sh + 52);
     }
     for (int off = 1; off < 64; off <<= 1) {
       Pair32 o;
@@ -733,23 +723,17 @@ struct Walker {
     if (tree0 || tree2) {
       const int e = g == 0 ? eA : e2;
       if ((g == 0 && tree0) || (g == 2 && tree2)) {
-        // the run's two trajectories (run_pair's steps), terms read eight at a time
-        const int sh = e - 52;
-        const uint32_t u = 1u << sh;
-        uint32_t v0 = 0u, v1 = u;
+        // the run from both starts with the double add (run_pair's steps),
+        // terms read eight at a time (a zero term moves nothing)
+        RunF64 r = run_start(e);
         for (int j = j0; j < j1; j += 8) {
           uint32_t x[8];
 #pragma unroll
           for (int q = 0; q < 8; ++q) x[q] = j + q < j1 ? term(i, j + q) : 0u;
 #pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            if (j + q < j1) {
-              v0 = traj_step(v0, x[q], sh);
-              v1 = traj_step(v1, x[q], sh);
-            }
-          }
+          for (int q = 0; q < 8; ++q) run_add(r, (double)x[q]);
         }
-        const Pair64 pr = widen_pair(Pair32{v0, v1 - u}, E);
+        const Pair64 pr = widen_pair(run_end(r, e), E);
         if (g == 0) c0 = pr;
         else c2 = pr;
       }
@@ -864,7 +848,7 @@ struct Walker {
         d[2 * q] = (int32_t)(p.a0 - E);
         d[2 * q + 1] = (int32_t)(p.a1 - E);
       } else {
-        const Pair32 p = run_pair([&](int j) { return term(i, j0 + j); }, j1 - j0, e - 52);
+        const Pair32 p = run_pair([&](int j) { return (double)term(i, j0 + j); }, j1 - j0, e);
         d[2 * q] = (int32_t)(p.a0 - (uint32_t)E);
         d[2 * q + 1] = (int32_t)(p.a1 - (uint32_t)E);
       }

@@ -134,6 +134,21 @@ def test_run_pair_brute_force(api):
         assert api.run_pair(terms, e) == brute_pair(terms.tolist(), e), (e, n)
 
 
+def test_run_pair_long_runs_stay_in_their_binade(api):
+    """Runs of up to 2^15 terms, the largest a row holds, at the top of the
+    term range: the double-add pair still equals the brute-force integer
+    fold in binades 53 to 62 (every add stays inside the binade)."""
+    rng = np.random.Generator(np.random.PCG64(15))
+    tt = checkers.t_table()
+    for e in (53, 55, 58, 62):
+        for n in (4096, 32768):
+            x = rng.integers(60000, 65536, size=n)
+            small = rng.random(n) < 0.1  # small codewords: odd terms, ties
+            x[small] = rng.integers(0, 4096, size=int(small.sum()))
+            terms = tt[x].astype(np.uint32)
+            assert api.run_pair(terms, e) == brute_pair(terms.tolist(), e), (e, n)
+
+
 def test_closed_form_premise():
     """Every float square in units is 0 or 1 modulo 4, and odd exactly when
     the codeword is odd and below 4096 (exhaustive over 16-bit samples)."""
@@ -326,7 +341,7 @@ def test_load_shape_choice(api):
 # ------------------------------------------------ planted breaks (header) --
 
 MUTANTS = {
-    1: "a tie to the odd value",
+    1: "a tie to the odd value in the one-term step",
     2: "the parity ignored",
     3: "the tree composed in reverse",
     4: "a run's units under the wrong binade",
