@@ -8,17 +8,23 @@ frames already resident in HBM.  Batches rotate through a ring of device
 copies larger than the 256 MB Infinity Cache, so every step reads its
 frames from HBM.  Prints ONE JSON line.
 
-value          frames per second over the K timed steps that follow the W
-               warmup steps (torch events on the launch stream, bracketed by
-               synchronisations; no per-kernel events inside)
-config         the run's figures; for the 16-bit 3840x2160 full-range
-               workload (the default) also config.halfrange, the half-range
-               workload (8 frames a step) measured the same way in the same
-               run
+value          frames per second over K timed pipelined steps
+               (bef_pipe_submit, then one bef_pipe_join; torch events on the
+               submitting stream, bracketed by synchronisations), after
+               their own warm-up; each step is one batch through the whole
+               path, and a batch's ordered part overlaps the next batches'
+               row passes on the library's streams
+config         the run's figures, among them the one-stream figures
+               (bef_frames_async, every kernel of a step after the one
+               before on one stream: one_stream_*); for the 16-bit
+               3840x2160 full-range workload (the default) also
+               config.halfrange, the half-range workload (8 frames a step)
+               measured the same way in the same run
 roofline       the row-sum kernel (the dominant one): algorithmic bytes per
                launch (2 planes x w x h x 2 B x frames) over its average
-               duration, measured over a second pass of K steps with HIP
-               events that each dispatch records on the launch stream;
+               duration, measured over a pass of K one-stream steps with HIP
+               events that each dispatch records on the launch stream (one
+               launch at a time: pipelined row passes overlap in pairs);
                peak = MI355X HBM3E 8 TB/s
 cpu_baseline   the CPU oracle (plain loops) on host copies of the same frames:
                one core (frames one after another, warm) and all of this
@@ -134,12 +140,13 @@ def cpu_baseline(ref, dis, bpc, w, bytes_per_frame, budget_s=20.0, one_core_fram
             "nproc": nproc, "usable_cpus": usable, "cpu_model": model}
 
 
-def measure(api, key, steps, warmup, ring=0, ceiling=True):
+def measure(api, key, steps, warmup, ring=0, ceiling=True, pipe=True):
     """Whole-path throughput of workload ``key``: batches rotate through a
     ring of device copies of at least 1 GB, W warm-up steps (plus settle
     steps until the warm-up has lasted 50 ms), K timed steps bracketed by
     events on the launch stream, then K more steps with per-kernel events
-    for the kernels' averages.  Returns a dict of figures and the frames."""
+    for the kernels' averages; before those (``pipe``), K pipelined steps
+    after their own warm-up.  Returns a dict of figures and the frames."""
     import numpy as np
     import torch
 
@@ -157,7 +164,61 @@ def measure(api, key, steps, warmup, ring=0, ceiling=True):
 
     # correctness of this very configuration, outside the timed region
     api.bef_debug_set(0)
-    mom, ps = api.bef_frames(refs[0], diss[0], wl.bpc, w=wl.w)
+    want_mom, want_ps = api.bef_frames(refs[0], diss[0], wl.bpc, w=wl.w)
+
+    # Pipelined batches (bef_pipe_submit): the same K steps, each one batch
+    # through the whole path, with a batch's ordered part overlapping the
+    # next batches' row passes on the library's own streams.  Submitted from
+    # a stream of torch's pool (non-blocking: the legacy NULL stream would
+    # wait for the library's streams), joined at the end, timed by events on
+    # that stream.
+    pipe_ms = None
+    pipe_settle = 0
+    if pipe:
+        pstream = torch.cuda.Stream()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        # the warm-up writes pwarm, the timed steps pout (filled beforehand:
+        # any host pause between the warm-up and the timed steps lets the
+        # clocks drop, and the next few hundred steps run up to 25% slower)
+        pwarm = torch.empty((F, 6), dtype=torch.float64, device="cuda")
+        pout = torch.full((F, 6), -1.0, dtype=torch.float64, device="cuda")
+
+        def prun(n, o):
+            for k in range(n):
+                api.bef_pipe_submit(refs[k % ring], diss[k % ring], wl.bpc, o, w=wl.w,
+                                    stream=pstream)
+            api.bef_pipe_join(0, pstream)
+
+        # Warm-up, then settle: chunks of 100 pipelined steps, each timed,
+        # until two in a row agree within 1% after at least 100 ms, at most
+        # 2 s.
+        torch.cuda.synchronize()
+        t_warm = time.perf_counter()
+        prun(warmup, pwarm)
+        torch.cuda.synchronize()
+        last = None
+        while True:
+            ev0.record(pstream)
+            prun(100, pwarm)
+            ev1.record(pstream)
+            torch.cuda.synchronize()
+            pipe_settle += 100
+            rate = ev0.elapsed_time(ev1)
+            waited = time.perf_counter() - t_warm
+            if waited > 2.0 or (waited > 0.1 and last is not None and
+                                abs(rate - last) <= 0.01 * last):
+                break
+            last = rate
+        ev0.record(pstream)
+        prun(steps, pout)
+        ev1.record(pstream)
+        torch.cuda.synchronize()
+        pipe_ms = ev0.elapsed_time(ev1)
+        got = pout.cpu().numpy()
+        assert (got[:, :4].view(np.uint64) == want_mom.view(np.uint64)).all()
+        assert (got[:, 4:].view(np.uint64) == want_ps.view(np.uint64)).all()
+        del pout, pwarm
 
     def run(n):
         for k in range(n):
@@ -183,8 +244,8 @@ def measure(api, key, steps, warmup, ring=0, ceiling=True):
     torch.cuda.synchronize()
     clean_ms = ev0.elapsed_time(ev1)
     got = out.cpu().numpy()
-    assert (got[:, :4].view(np.uint64) == mom.view(np.uint64)).all()
-    assert (got[:, 4:].view(np.uint64) == ps.view(np.uint64)).all()
+    assert (got[:, :4].view(np.uint64) == want_mom.view(np.uint64)).all()
+    assert (got[:, 4:].view(np.uint64) == want_ps.view(np.uint64)).all()
 
     # the same K steps again, each kernel timed by HIP events that its own
     # dispatch records on the launch stream
@@ -216,11 +277,17 @@ def measure(api, key, steps, warmup, ring=0, ceiling=True):
         api.bef_timing_enable(False)
         c_ms, c_n = api.bef_timing_read("ceiling")
         ceil_gbps = batch_bytes / (c_ms / c_n / 1e3) / 1e9
+
     del refs, diss
     gbps = batch_bytes * steps / (clean_ms / 1e3) / 1e9
-    return {"wl": wl, "F": F, "ring": ring, "settle": settle, "clean_ms": clean_ms,
-            "total_ms": total_ms, "kern": kern, "ceiling": ceil_gbps, "batch_bytes": batch_bytes,
-            "fps": F * steps / (clean_ms / 1e3), "gbps": gbps, "ref_h": ref_h, "dis_h": dis_h}
+    res = {"wl": wl, "F": F, "ring": ring, "settle": settle, "clean_ms": clean_ms,
+           "total_ms": total_ms, "kern": kern, "ceiling": ceil_gbps, "batch_bytes": batch_bytes,
+           "fps": F * steps / (clean_ms / 1e3), "gbps": gbps, "ref_h": ref_h, "dis_h": dis_h,
+           "pipe_ms": pipe_ms, "pipe_settle": pipe_settle}
+    if pipe_ms is not None:
+        res["pipe_fps"] = F * steps / (pipe_ms / 1e3)
+        res["pipe_gbps"] = batch_bytes * steps / (pipe_ms / 1e3) / 1e9
+    return res
 
 
 def main():
@@ -287,24 +354,32 @@ def main():
         r5 = h5["kern"].get("rows")
         half = {"workload": h5["wl"].name, "frames_per_step": h5["F"],
                 "recipe": h5["wl"].recipe, "ring_copies": h5["ring"],
-                "fps": round(h5["fps"], 1),
-                "ms_per_step": round(h5["clean_ms"] / args.steps, 5),
-                "whole_path_GBps": round(h5["gbps"], 1),
-                "whole_path_frac": round(h5["gbps"] / PEAK_HBM_GBS, 4),
+                "fps": round(h5["pipe_fps"], 1),
+                "ms_per_step": round(h5["pipe_ms"] / args.steps, 5),
+                "whole_path_GBps": round(h5["pipe_gbps"], 1),
+                "whole_path_frac": round(h5["pipe_gbps"] / PEAK_HBM_GBS, 4),
+                "one_stream_fps": round(h5["fps"], 1),
+                "one_stream_ms_per_step": round(h5["clean_ms"] / args.steps, 5),
+                "one_stream_whole_path_frac": round(h5["gbps"] / PEAK_HBM_GBS, 4),
                 "rows_avg_us": None if r5 is None else round(r5, 2),
                 "rows_frac": None if r5 is None else
                 round(h5["batch_bytes"] / (r5 / 1e6) / 1e9 / PEAK_HBM_GBS, 4),
                 "walk_avg_us": round(h5["kern"].get("walk", 0.0), 2),
                 "read_ceiling_GBps": None if h5["ceiling"] is None else round(h5["ceiling"], 1),
-                "settle_steps_after_warmup": h5["settle"]}
+                "settle_steps_after_warmup": h5["settle"],
+                "pipelined_settle_steps_after_warmup": h5["pipe_settle"]}
 
     rows_us = m["kern"]["rows"]
     achieved = batch_bytes / (rows_us / 1e6) / 1e9
     ceiling = m["ceiling"]
     config = {"workload": wl.name, "frames_per_step": F, "w": wl.w, "h": wl.h,
               "bpc": wl.bpc, "recipe": wl.recipe, "ring_copies": m["ring"],
-              "whole_path_GBps": round(m["gbps"], 1),
-              "whole_path_frac": round(m["gbps"] / PEAK_HBM_GBS, 4),
+              "path": f"bef_pipe_submit, {api.bef_pipe_walk_cus()} walk CUs",
+              "whole_path_GBps": round(m["pipe_gbps"], 1),
+              "whole_path_frac": round(m["pipe_gbps"] / PEAK_HBM_GBS, 4),
+              "one_stream_fps": round(m["fps"], 1),
+              "one_stream_ms_per_step": round(m["clean_ms"] / args.steps, 5),
+              "one_stream_whole_path_frac": round(m["gbps"] / PEAK_HBM_GBS, 4),
               "walk_avg_us": round(m["kern"].get("walk", 0.0), 2)}
     for name in ("plan", "pairs"):  # only where a plane can pass 2^55
         if name in m["kern"]:
@@ -314,17 +389,18 @@ def main():
         "host_pipeline_fps_pcie_inclusive": None if host_fps is None else round(host_fps, 1),
         "rows_over_read_ceiling": None if ceiling is None else round(achieved / ceiling, 4),
         "timed_with_events_ms_per_step": round(m["total_ms"] / args.steps, 5),
-        "settle_steps_after_warmup": m["settle"]})
+        "settle_steps_after_warmup": m["settle"],
+        "pipelined_settle_steps_after_warmup": m["pipe_settle"]})
     if half is not None:
         config["halfrange"] = half
     rec = {
         "metric": "frames/sec and achieved HBM GB/s (% of peak), 16-bit 3840x2160, 1 MI355X",
-        "value": round(m["fps"], 1),
+        "value": round(m["pipe_fps"], 1),
         "unit": "frames/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(m["clean_ms"] / args.steps, 5),
+        "ms_per_step": round(m["pipe_ms"] / args.steps, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -44,8 +44,12 @@ _lib.bef_frames_units.argtypes = [_vp, _vp, _i, _i, _pd, _pd, _i, _i, _vp, _u64p
 _lib.bef_read_ceiling.argtypes = [_vp, _vp, _i, _i, _pd, _pd, _i, _vp, _vp]
 _lib.bef_frames_host.argtypes = [_vp, _vp, _i, _i, _pd, _pd, _i, _i, _i, _dp, _dp]
 _lib.bef_planes.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _dp]
+_lib.bef_pipe_submit.argtypes = [_vp, _vp, _i, _i, _pd, _pd, _i, _i, _vp, _vp]
+_lib.bef_pipe_join.argtypes = [_i, _vp]
+_lib.bef_pipe_set_walk_cus.argtypes = [_i]
 for _n in ("moment_frame", "psnr_noise", "bef_frames", "bef_frames_async", "bef_frames_noalloc",
-           "bef_frames_units", "bef_read_ceiling", "bef_frames_host", "bef_planes"):
+           "bef_frames_units", "bef_read_ceiling", "bef_frames_host", "bef_planes",
+           "bef_pipe_submit", "bef_pipe_join", "bef_pipe_set_walk_cus"):
     getattr(_lib, _n).restype = _i
 _lib.bef_last_error.restype = ctypes.c_char_p
 _lib.bef_walk_paths.argtypes = [_vp, _i]
@@ -233,6 +237,35 @@ def bef_frames_noalloc(ref, dis, bpc: int, out, w: int | None = None, stream=Non
     _check(_lib.bef_frames_noalloc(ref.data_ptr(), dis.data_ptr(), w, h, stride, h * stride,
                                    f, bpc, _stream_ptr(stream), ctypes.c_void_p(out.data_ptr())),
            "bef_frames_noalloc")
+
+
+def bef_pipe_submit(ref, dis, bpc: int, out, w: int | None = None, stream=None):
+    """Pipelined batch into the float64 device tensor ``out`` [F,6]: complete
+    once ``stream`` has passed a later bef_pipe_join."""
+    import torch
+    f, h, stride, w = _pair(ref, dis, bpc, w)
+    if out.dtype != torch.float64 or not out.is_cuda or out.numel() < 6 * f:
+        raise BefError("out must be a float64 device tensor of at least 6*F")
+    _check(_lib.bef_pipe_submit(ref.data_ptr(), dis.data_ptr(), w, h, stride, h * stride,
+                                f, bpc, _stream_ptr(stream), ctypes.c_void_p(out.data_ptr())),
+           "bef_pipe_submit")
+
+
+def bef_pipe_join(device: int = 0, stream=None):
+    """Makes ``stream`` wait for every pipelined batch of ``device``."""
+    _check(_lib.bef_pipe_join(int(device), _stream_ptr(stream)), "bef_pipe_join")
+
+
+def bef_pipe_set_walk_cus(n: int) -> int:
+    """Sets the walk stream's CUs (0: unchanged); returns the previous count."""
+    rc = _lib.bef_pipe_set_walk_cus(int(n))
+    if rc < 0:
+        raise BefError(f"bef_pipe_set_walk_cus returned {rc}: {last_error()}")
+    return rc
+
+
+def bef_pipe_walk_cus() -> int:
+    return bef_pipe_set_walk_cus(0)
 
 
 def bef_frames_units(ref, dis, bpc: int, w: int | None = None, stream=None):

@@ -36,6 +36,25 @@ unsigned g_dbg = 0;
 
 constexpr int kMaxDev = 64;
 constexpr int kMaxPlanes = 4;  // planes of one bef_planes call
+constexpr int kPipeRowQ = 2;   // row streams of pipelined batches
+constexpr int kPipeSlots = 4;  // scratch slots of pipelined batches
+
+struct Layout {
+  size_t r1, r2, rn, codd, plan, pairs, psum, results, units, paths, total;
+  // results, units and paths are copied back together: bytes from results
+  size_t readback() const { return total - results; }
+};
+
+struct Call {
+  Geometry g;
+  int dev;
+  Layout L;
+  RowArrays ra;
+  double* d_results;
+  uint64_t* d_units;
+  bool need_pairs;
+};
+
 struct Arena {
   void* base = nullptr;
   size_t cap = 0;
@@ -46,8 +65,21 @@ struct Arena {
   size_t pipe_cap = 0;
   hipStream_t copy_st = nullptr, comp_st = nullptr;
   hipEvent_t copied[2] = {nullptr, nullptr}, done[2] = {nullptr, nullptr};
+  // pipelined batches: row streams on most CUs, a walk stream on the
+  // others, scratch slots used in turn
+  hipStream_t prow[kPipeRowQ] = {};
+  hipStream_t pwalk = nullptr;
+  int pwalk_cus = 0;
+  hipEvent_t penter = nullptr, pjoin = nullptr;
+  hipEvent_t prowdone[kPipeSlots] = {}, pwalkdone[kPipeSlots] = {};
+  void* pslot = nullptr;  // kPipeSlots slots
+  size_t pslot_cap = 0;   // bytes per slot
+  unsigned long long pn = 0;  // batches submitted
 };
 Arena g_arena[kMaxDev];
+
+// CUs reserved for the walk stream of pipelined batches.
+int g_pipe_walk_cus = 16;
 
 // Walk paths of the last synchronous batch (bef_walk_paths).
 std::vector<uint8_t> g_paths;
@@ -96,12 +128,6 @@ int validate(const void* ref, const void* dis, int w, int h, ptrdiff_t stride,
 }
 
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-struct Layout {
-  size_t r1, r2, rn, codd, plan, pairs, psum, results, units, paths, total;
-  // results, units and paths are copied back together: bytes from results
-  size_t readback() const { return total - results; }
-};
 
 Layout layout(int F, int h) {
   const size_t rows = (size_t)F * h;
@@ -202,16 +228,6 @@ hipError_t timed(int kernel, F launch) {
   return e;
 }
 
-struct Call {
-  Geometry g;
-  int dev;
-  Layout L;
-  RowArrays ra;
-  double* d_results;
-  uint64_t* d_units;
-  bool need_pairs;
-};
-
 // Arguments, device and geometry of a call; allocates nothing.
 int setup(Call& c, const void* ref, const void* dis, int w, int h, ptrdiff_t stride,
           ptrdiff_t pitch, int nframes, int bpc) {
@@ -286,15 +302,16 @@ int check_stream(const Call& c, hipStream_t st) {
   return 0;
 }
 
-int enqueue(const Call& c, hipStream_t st, double* d_results, bool may_time = true) {
+// The row pass, then (batches that can pass 2^55 units) the plan and the
+// row pairs; may_time false: no event is created or recorded.
+int enqueue_rows(const Call& c, hipStream_t st, bool may_time) {
   const unsigned dbg = g_dbg;
-  if (!may_time) {  // no event is created or recorded
+  if (!may_time) {
     BEF_HIP(launch_rows(c.g, c.ra, st, nullptr, nullptr));
     if (c.need_pairs) {
       BEF_HIP(launch_plan(c.g, c.ra, dbg, st, nullptr, nullptr));
       BEF_HIP(launch_pairs(c.g, c.ra, dbg, st, nullptr, nullptr));
     }
-    BEF_HIP(launch_walk(c.g, c.ra, d_results, c.d_units, dbg, st, nullptr, nullptr));
     return 0;
   }
   BEF_HIP(timed(0, [&](hipEvent_t a, hipEvent_t b) { return launch_rows(c.g, c.ra, st, a, b); }));
@@ -306,10 +323,25 @@ int enqueue(const Call& c, hipStream_t st, double* d_results, bool may_time = tr
       return launch_pairs(c.g, c.ra, dbg, st, a, b);
     }));
   }
+  return 0;
+}
+
+// The walks, which write the frames' results to d_results.
+int enqueue_walk(const Call& c, hipStream_t st, double* d_results, bool may_time) {
+  const unsigned dbg = g_dbg;
+  if (!may_time) {
+    BEF_HIP(launch_walk(c.g, c.ra, d_results, c.d_units, dbg, st, nullptr, nullptr));
+    return 0;
+  }
   BEF_HIP(timed(3, [&](hipEvent_t a, hipEvent_t b) {
     return launch_walk(c.g, c.ra, d_results, c.d_units, dbg, st, a, b);
   }));
   return 0;
+}
+
+int enqueue(const Call& c, hipStream_t st, double* d_results, bool may_time = true) {
+  int rc = enqueue_rows(c, st, may_time);
+  return rc ? rc : enqueue_walk(c, st, d_results, may_time);
 }
 
 // Synchronous batch: results and units copied back to the host.
@@ -456,9 +488,162 @@ int run_host(const void* ref, const void* dis, int w, int h, ptrdiff_t stride, p
   return rc;
 }
 
+// Pipelined batches.  Batch n's rows (and plan and pairs) run on row
+// stream n % kPipeRowQ, its walks on the walk stream once its rows are
+// done.  The row streams take turns, so one batch's row pass overlaps the
+// tail of the one before (and the few microseconds a stream stalls after
+// a dispatch that signals an event), and the walks overlap later row
+// passes.  Slot n % kPipeSlots is rewritten by batch n + kPipeSlots only
+// after batch n's walks have read it.  The walks get CUs of their own: a
+// walk block needs a whole CU's LDS, which a busy row pass never frees.
+void ovl_drain(Arena& a) {
+  for (hipStream_t q : a.prow)
+    if (q) (void)hipStreamSynchronize(q);
+  if (a.pwalk) (void)hipStreamSynchronize(a.pwalk);
+}
+
+// Streams and events go only once the whole device is idle: a caller's
+// stream may still hold a wait on a join event.
+void ovl_destroy(Arena& a) {
+  ovl_drain(a);
+  (void)hipDeviceSynchronize();
+  for (hipStream_t& q : a.prow) {
+    if (q) (void)hipStreamDestroy(q);
+    q = nullptr;
+  }
+  if (a.pwalk) (void)hipStreamDestroy(a.pwalk);
+  a.pwalk = nullptr;
+  std::vector<hipEvent_t*> evs = {&a.penter, &a.pjoin};
+  for (int k = 0; k < kPipeSlots; ++k) {
+    evs.push_back(&a.prowdone[k]);
+    evs.push_back(&a.pwalkdone[k]);
+  }
+  for (hipEvent_t* e : evs) {
+    if (*e) (void)hipEventDestroy(*e);
+    *e = nullptr;
+  }
+  if (a.pslot) (void)hipFree(a.pslot);
+  a.pslot = nullptr;
+  a.pslot_cap = 0;
+  a.pwalk_cus = 0;
+  a.pn = 0;
+}
+
+int ovl_setup(int dev, size_t slot_bytes, int walk_cus) {
+  Arena& a = g_arena[dev];
+  if (a.pwalk && a.pwalk_cus != walk_cus) ovl_destroy(a);
+  if (!a.pwalk) {
+    int ncu = 0;
+    BEF_HIP(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev));
+    if (walk_cus < 1 || walk_cus >= ncu)
+      return fail(-EINVAL, "%d walk CUs outside 1..%d", walk_cus, ncu - 1);
+    // the walk stream takes the last walk_cus CUs, the row streams the rest
+    std::vector<uint32_t> mrow((ncu + 31) / 32, 0u), mwalk((ncu + 31) / 32, 0u);
+    for (int i = 0; i < ncu; ++i) (i >= ncu - walk_cus ? mwalk : mrow)[i / 32] |= 1u << (i % 32);
+    for (hipStream_t& q : a.prow)
+      BEF_HIP(hipExtStreamCreateWithCUMask(&q, (uint32_t)mrow.size(), mrow.data()));
+    BEF_HIP(hipExtStreamCreateWithCUMask(&a.pwalk, (uint32_t)mwalk.size(), mwalk.data()));
+    a.pwalk_cus = walk_cus;
+    // the handoffs stay on this device: no system-scope fence
+    const unsigned local = hipEventDisableTiming | hipEventDisableSystemFence;
+    BEF_HIP(hipEventCreateWithFlags(&a.penter, hipEventDisableTiming));
+    BEF_HIP(hipEventCreateWithFlags(&a.pjoin, hipEventDisableTiming));
+    for (int k = 0; k < kPipeSlots; ++k) {
+      BEF_HIP(hipEventCreateWithFlags(&a.prowdone[k], local));
+      BEF_HIP(hipEventCreateWithFlags(&a.pwalkdone[k], local));
+    }
+  }
+  if (a.pslot_cap < slot_bytes) {  // after the batches that use the slots
+    ovl_drain(a);
+    if (a.pslot) BEF_HIP(hipFree(a.pslot));
+    a.pslot = nullptr;
+    a.pslot_cap = 0;
+    if (hipMalloc(&a.pslot, kPipeSlots * slot_bytes) != hipSuccess) {
+      (void)hipGetLastError();
+      a.pslot = nullptr;
+      return fail(-ENOMEM, "hipMalloc of %zu bytes of pipeline slots failed",
+                  kPipeSlots * slot_bytes);
+    }
+    a.pslot_cap = slot_bytes;
+  }
+  return 0;
+}
+
+int ovl_submit(const void* ref, const void* dis, int w, int h, ptrdiff_t stride,
+               ptrdiff_t pitch, int nframes, int bpc, hipStream_t st, double* dev_results) {
+  Call c;
+  int rc = setup(c, ref, dis, w, h, stride, pitch, nframes, bpc);
+  if (rc || (rc = check_stream(c, st))) return rc;
+  if ((rc = ovl_setup(c.dev, c.L.total, g_pipe_walk_cus))) return rc;
+  Arena& a = g_arena[c.dev];
+  const int s = (int)(a.pn % kPipeSlots);
+  const hipStream_t rq = a.prow[a.pn % kPipeRowQ];
+  bind(c, (char*)a.pslot + (size_t)s * a.pslot_cap);
+  // the batch's reads follow the caller's earlier work on its stream
+  if (hipStreamQuery(st) != hipSuccess) {
+    (void)hipGetLastError();
+    BEF_HIP(hipEventRecord(a.penter, st));
+    BEF_HIP(hipStreamWaitEvent(rq, a.penter, 0));
+  }
+  if (a.pn >= kPipeSlots) BEF_HIP(hipStreamWaitEvent(rq, a.pwalkdone[s], 0));
+  // the handoff events are the last dispatches' own completion (no
+  // separate marker packet on either queue)
+  const unsigned dbg = g_dbg;
+  if (c.need_pairs) {
+    BEF_HIP(launch_rows(c.g, c.ra, rq, nullptr, nullptr));
+    BEF_HIP(launch_plan(c.g, c.ra, dbg, rq, nullptr, nullptr));
+    BEF_HIP(launch_pairs(c.g, c.ra, dbg, rq, nullptr, a.prowdone[s]));
+  } else {
+    BEF_HIP(launch_rows(c.g, c.ra, rq, nullptr, a.prowdone[s]));
+  }
+  BEF_HIP(hipStreamWaitEvent(a.pwalk, a.prowdone[s], 0));
+  BEF_HIP(launch_walk(c.g, c.ra, dev_results, c.d_units, dbg, a.pwalk, nullptr, a.pwalkdone[s]));
+  a.pn += 1;
+  return 0;
+}
+
 }  // namespace
 
 extern "C" {
+
+int bef_pipe_submit(const void* ref, const void* dis, int w, int h, ptrdiff_t stride,
+                    ptrdiff_t frame_pitch, int nframes, int bpc, void* stream,
+                    double* dev_results) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  clear_err();
+  if (!dev_results) return fail(-EINVAL, "NULL dev_results");
+  DevGuard dg;
+  return ovl_submit(ref, dis, w, h, stride, frame_pitch, nframes, bpc, (hipStream_t)stream,
+                     dev_results);
+}
+
+int bef_pipe_join(int device, void* stream) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  clear_err();
+  if (device < 0 || device >= kMaxDev) return fail(-EINVAL, "device %d out of range", device);
+  Arena& a = g_arena[device];
+  if (!a.pwalk) return 0;  // nothing submitted on this device
+  DevGuard dg;
+  BEF_HIP(hipSetDevice(device));
+  const hipStream_t st = (hipStream_t)stream;
+  if (st) {
+    hipDevice_t sd = -1;
+    BEF_HIP(hipStreamGetDevice(st, &sd));
+    if (sd != device) return fail(-EINVAL, "stream of device %d, joining device %d", (int)sd, device);
+  }
+  BEF_HIP(hipEventRecord(a.pjoin, a.pwalk));
+  BEF_HIP(hipStreamWaitEvent(st, a.pjoin, 0));
+  return 0;
+}
+
+int bef_pipe_set_walk_cus(int n) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  clear_err();
+  if (n < 0 || n > 128) return fail(-EINVAL, "%d walk CUs outside 1..128", n);
+  const int old = g_pipe_walk_cus;
+  if (n) g_pipe_walk_cus = n;
+  return old;
+}
 
 int bef_frames(const void* ref, const void* dis, int w, int h, ptrdiff_t stride,
                ptrdiff_t frame_pitch, int nframes, int bpc, void* stream, double* moments,
@@ -654,8 +839,9 @@ void bef_release(void) {
   DevGuard dg;
   for (int d = 0; d < kMaxDev; ++d) {
     Arena& a = g_arena[d];
-    if (!a.base && !a.host && !a.pipe && !a.copy_st) continue;
+    if (!a.base && !a.host && !a.pipe && !a.copy_st && !a.pwalk) continue;
     (void)hipSetDevice(d);
+    ovl_destroy(a);
     if (a.base) (void)hipFree(a.base);
     if (a.host) (void)hipHostFree(a.host);
     if (a.pipe) (void)hipFree(a.pipe);

@@ -110,6 +110,48 @@ int bef_frames_noalloc(const void *ref, const void *dis, int w, int h,
                        ptrdiff_t stride, ptrdiff_t frame_pitch, int nframes,
                        int bpc, void *stream, double *dev_results);
 
+/* Pipelined batches: bef_frames_async's reductions with one batch's
+ * ordered part overlapping later batches' plane reads.  The pages'
+ * dispatch keeps two frames in flight, collecting frame N - 1 after frame
+ * N is uploaded (ADR-1497, Context); here the library keeps several
+ * batches in flight on streams of its own per device: batch n's row pass
+ * (and plan and pairs) on row stream n % 2, so that consecutive row passes
+ * overlap, and its per-plane walks on a walk stream once its rows are
+ * done.  The row streams run on all but n_walk of the device's CUs, the
+ * walk stream on the other n_walk (bef_pipe_set_walk_cus, default 16).
+ * Each batch's scratch is one of four slots, reused in turn.
+ * Arguments and limits as bef_frames_async; dev_results (DEVICE,
+ * [nframes][6] doubles, caller-owned) receives the same bits.  The batch's
+ * reads start after the work enqueued on `stream` before the call.  The
+ * call returns after enqueueing (a batch larger than any before first
+ * waits, on the host, for the batches in flight, then grows the slots).
+ * Results are complete, and the planes may be changed again, only once
+ * `stream` has passed a later bef_pipe_join(device, stream), which makes
+ * `stream` wait (on the device, not the host) for every batch submitted
+ * so far on that device.  The library's streams are blocking streams:
+ * work on the legacy NULL stream waits for them, so a caller on the NULL
+ * stream gets the same results without the overlap.  Batches of successive
+ * calls may share dev_results (their walks run in submission order).  Not
+ * for graph capture. */
+int bef_pipe_submit(const void *ref, const void *dis, int w, int h,
+                    ptrdiff_t stride, ptrdiff_t frame_pitch, int nframes,
+                    int bpc, void *stream, double *dev_results);
+
+/* Makes `stream` (NULL = the legacy default stream; else a stream of
+ * `device`) wait for every batch bef_pipe_submit has enqueued on `device`
+ * so far.  Returns at once; 0 when nothing was submitted there, -EINVAL
+ * for a device outside 0..63 or a stream of another device. */
+int bef_pipe_join(int device, void *stream);
+
+/* CUs (1..128, fewer than the device has) reserved for the walk stream of
+ * pipelined batches; n = 0 changes nothing.  Returns the count in effect
+ * before the call, -EINVAL for n outside 0..128.  A new count takes effect
+ * at the next bef_pipe_submit on each device, which first waits for that
+ * device to go idle and then rebuilds its streams.  The runtime spreads a
+ * stream's CUs over the device's XCDs and refuses a count it cannot
+ * spread (on MI355X, fewer than 8). */
+int bef_pipe_set_walk_cus(int n);
+
 /* Several planes of each frame (luma and chroma, e.g. Y, Cb, Cr of 4:2:0
  * pictures, or any up to 4 planes), each with its own geometry, in one
  * synchronous call: per plane the float_moment and float_psnr results of
