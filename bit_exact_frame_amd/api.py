@@ -11,6 +11,7 @@ C-contiguous; ``w`` defaults to the last dimension.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
 
@@ -59,6 +60,10 @@ _lib.bef_debug_set.restype = _u
 _lib.bef_timing_enable.argtypes = [_i]
 _lib.bef_timing_read.argtypes = [_i, _dp, ctypes.POINTER(ctypes.c_long)]
 _lib.bef_release.restype = None
+
+# The library's streams, events and device memory go before the HIP runtime
+# is torn down at exit.
+atexit.register(_lib.bef_release)
 _lib.bef_timing_reset.restype = None
 
 DBG_PLAN_WRONG = 1

@@ -37,7 +37,7 @@ unsigned g_dbg = 0;
 constexpr int kMaxDev = 64;
 constexpr int kMaxPlanes = 4;  // planes of one bef_planes call
 constexpr int kPipeRowQ = 2;   // row streams of pipelined batches
-constexpr int kPipeSlots = 4;  // scratch slots of pipelined batches
+constexpr int kPipeSlots = 8;  // scratch slots of pipelined batches
 
 struct Layout {
   size_t r1, r2, rn, codd, plan, pairs, psum, results, units, paths, total;
@@ -585,7 +585,12 @@ int ovl_submit(const void* ref, const void* dis, int w, int h, ptrdiff_t stride,
     BEF_HIP(hipEventRecord(a.penter, st));
     BEF_HIP(hipStreamWaitEvent(rq, a.penter, 0));
   }
-  if (a.pn >= kPipeSlots) BEF_HIP(hipStreamWaitEvent(rq, a.pwalkdone[s], 0));
+  // the slot's previous batch must have been walked; a wait costs the host
+  // several microseconds, so it is skipped when that walk has already ended
+  if (a.pn >= kPipeSlots && hipEventQuery(a.pwalkdone[s]) != hipSuccess) {
+    (void)hipGetLastError();
+    BEF_HIP(hipStreamWaitEvent(rq, a.pwalkdone[s], 0));
+  }
   // the handoff events are the last dispatches' own completion (no
   // separate marker packet on either queue)
   const unsigned dbg = g_dbg;
