@@ -49,6 +49,7 @@ def calls(api):
         "bef_frames_units": lambda r, d, b: api.bef_frames_units(r, d, b),
         "bef_frames_async": lambda r, d, b: api.bef_frames_async(r, d, b, out),
         "bef_frames_noalloc": lambda r, d, b: api.bef_frames_noalloc(r, d, b, out),
+        "bef_pipe_submit": lambda r, d, b: api.bef_pipe_submit(r, d, b, out),
         "bef_read_ceiling": lambda r, d, b: api.bef_read_ceiling(r, d, ceil_out),
     }
 
@@ -68,7 +69,8 @@ def bad_dis():
 
 
 @pytest.mark.parametrize("entry", ["moment_frame", "psnr_noise", "bef_frames", "bef_frames_units",
-                                   "bef_frames_async", "bef_frames_noalloc", "bef_read_ceiling"])
+                                   "bef_frames_async", "bef_frames_noalloc", "bef_pipe_submit",
+                                   "bef_read_ceiling"])
 def test_mismatched_dis_is_refused(api, entry):
     ref = DevPlane(torch.zeros((3, 8, 16), dtype=torch.uint16))
     fn = calls(api)[entry]
