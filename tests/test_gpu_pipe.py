@@ -233,3 +233,38 @@ def test_pipe_bad_arguments(api):
     with pytest.raises(api.BefError):
         api.bef_pipe_join(-1)
     torch.cuda.synchronize()
+
+
+def test_pipe_random_batches_match_oracle(api, orc):
+    """Forty seeded batches of random geometry submitted back to back (1-5
+    frames, widths 1-2500 with padded strides, 1-300 rows, every bit depth
+    from 8 to 16, uniform or near-maximum content), so that slots, row
+    streams and slot growth interleave in many orders; each against the
+    oracle."""
+    import torch
+    rng = np.random.default_rng(20261202)
+    st = torch.cuda.Stream()
+    batches, want = [], []
+    for n in range(40):
+        bpc = int(rng.integers(8, 17))
+        f = int(rng.integers(1, 6))
+        w = int(rng.integers(1, 2501))
+        h = int(rng.integers(1, 301))
+        stride = w + int(rng.integers(0, 40))
+        top = (1 << bpc) - 1
+        dt = np.uint8 if bpc == 8 else np.uint16
+        lo = 0 if rng.random() < 0.5 else top - top // 8
+        ref = rng.integers(lo, top + 1, size=(f, h, stride)).astype(dt)
+        dis = rng.integers(0, top + 1, size=(f, h, stride)).astype(dt)
+        ref[:, :, w:] = top
+        dis[:, :, w:] = top
+        batches.append((dev(ref), dev(dis), bpc, w, out_for(f)))
+        want.append((n, ref, dis, bpc, w))
+    torch.cuda.synchronize()
+    say("[gpu] pipe random: 40 batches, seed 20261202")
+    run(api, batches, st)
+    for (n, ref, dis, bpc, w), b in zip(want, batches):
+        emom, eps = orc.frames(ref, dis, bpc, w=w)
+        g = b[4].cpu().numpy()
+        assert (bits(g[:, :4]) == bits(emom)).all() and (bits(g[:, 4:]) == bits(eps)).all(), (
+            n, ref.shape, bpc, w, g, emom, eps)
