@@ -529,28 +529,39 @@ void ovl_destroy(Arena& a) {
   a.pn = 0;
 }
 
+// The streams and events of pipelined batches.  The walk stream is created
+// last: the arena counts as set up only once it exists.
+int ovl_create(Arena& a, int dev, int walk_cus) {
+  int ncu = 0;
+  BEF_HIP(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev));
+  if (walk_cus < 1 || walk_cus >= ncu)
+    return fail(-EINVAL, "%d walk CUs outside 1..%d", walk_cus, ncu - 1);
+  // the walk stream takes the last walk_cus CUs, the row streams the rest
+  std::vector<uint32_t> mrow((ncu + 31) / 32, 0u), mwalk((ncu + 31) / 32, 0u);
+  for (int i = 0; i < ncu; ++i) (i >= ncu - walk_cus ? mwalk : mrow)[i / 32] |= 1u << (i % 32);
+  // the handoffs stay on this device: no system-scope fence
+  const unsigned local = hipEventDisableTiming | hipEventDisableSystemFence;
+  BEF_HIP(hipEventCreateWithFlags(&a.penter, hipEventDisableTiming));
+  BEF_HIP(hipEventCreateWithFlags(&a.pjoin, hipEventDisableTiming));
+  for (int k = 0; k < kPipeSlots; ++k) {
+    BEF_HIP(hipEventCreateWithFlags(&a.prowdone[k], local));
+    BEF_HIP(hipEventCreateWithFlags(&a.pwalkdone[k], local));
+  }
+  for (hipStream_t& q : a.prow)
+    BEF_HIP(hipExtStreamCreateWithCUMask(&q, (uint32_t)mrow.size(), mrow.data()));
+  BEF_HIP(hipExtStreamCreateWithCUMask(&a.pwalk, (uint32_t)mwalk.size(), mwalk.data()));
+  a.pwalk_cus = walk_cus;
+  return 0;
+}
+
 int ovl_setup(int dev, size_t slot_bytes, int walk_cus) {
   Arena& a = g_arena[dev];
   if (a.pwalk && a.pwalk_cus != walk_cus) ovl_destroy(a);
   if (!a.pwalk) {
-    int ncu = 0;
-    BEF_HIP(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev));
-    if (walk_cus < 1 || walk_cus >= ncu)
-      return fail(-EINVAL, "%d walk CUs outside 1..%d", walk_cus, ncu - 1);
-    // the walk stream takes the last walk_cus CUs, the row streams the rest
-    std::vector<uint32_t> mrow((ncu + 31) / 32, 0u), mwalk((ncu + 31) / 32, 0u);
-    for (int i = 0; i < ncu; ++i) (i >= ncu - walk_cus ? mwalk : mrow)[i / 32] |= 1u << (i % 32);
-    for (hipStream_t& q : a.prow)
-      BEF_HIP(hipExtStreamCreateWithCUMask(&q, (uint32_t)mrow.size(), mrow.data()));
-    BEF_HIP(hipExtStreamCreateWithCUMask(&a.pwalk, (uint32_t)mwalk.size(), mwalk.data()));
-    a.pwalk_cus = walk_cus;
-    // the handoffs stay on this device: no system-scope fence
-    const unsigned local = hipEventDisableTiming | hipEventDisableSystemFence;
-    BEF_HIP(hipEventCreateWithFlags(&a.penter, hipEventDisableTiming));
-    BEF_HIP(hipEventCreateWithFlags(&a.pjoin, hipEventDisableTiming));
-    for (int k = 0; k < kPipeSlots; ++k) {
-      BEF_HIP(hipEventCreateWithFlags(&a.prowdone[k], local));
-      BEF_HIP(hipEventCreateWithFlags(&a.pwalkdone[k], local));
+    const int rc = ovl_create(a, dev, walk_cus);
+    if (rc) {  // release whatever was made; the error text stays
+      ovl_destroy(a);
+      return rc;
     }
   }
   if (a.pslot_cap < slot_bytes) {  // after the batches that use the slots

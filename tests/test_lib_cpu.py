@@ -149,6 +149,51 @@ def test_run_pair_long_runs_stay_in_their_binade(api):
             assert api.run_pair(terms, e) == brute_pair(terms.tolist(), e), (e, n)
 
 
+def test_run_pair_first_tie(api):
+    """Binades 55 to 60: the two moves of a run differ only from its first
+    tie on (a term whose remainder modulo u is u/2).  Before it the even and
+    odd starts take the same steps, u apart; the tie rounds both to an even
+    multiple of u, one down and one up, so from then on they are equal or 2u
+    apart and take the same steps again.  So the moves are equal when no term
+    is a tie, and differ by exactly u otherwise; the direction is that of the
+    even start's parity at the first tie (ADR-1497, Decision: a run of terms
+    is an even-start and an odd-start increment).  Checked on runs with no
+    tie (terms that are multiples of u), with ties only in the last term, and
+    with dense ties, against the double-add pair and the integer fold."""
+    rng = np.random.Generator(np.random.PCG64(55))
+    tt = checkers.t_table().astype(np.int64)
+    for trial in range(600):
+        e = int(rng.integers(55, 61))
+        u = 1 << (e - 52)
+        n = int(rng.integers(1, 120))
+        kind = trial % 3
+        if kind == 0:  # no tie: every term a multiple of u
+            x = rng.integers(0, 65536, size=n)
+            terms = tt[x] & ~(u - 1)
+        elif kind == 1:  # one tie, at the end
+            x = rng.integers(0, 65536, size=n)
+            terms = tt[x] & ~(u - 1)
+            terms[-1] = terms[-1] | (u // 2)
+        else:  # small codewords: ties all along
+            terms = tt[rng.integers(0, 9000, size=n)]
+        terms = terms.astype(np.uint32)
+        tl = [int(t) for t in terms]
+        a0, a1 = brute_pair(tl, e)
+        assert api.run_pair(terms, e) == [a0, a1], (e, n, kind)
+        ties = [k for k, t in enumerate(tl) if t % u == u // 2]
+        if not ties:
+            assert a1 == a0, (e, n, kind)
+            continue
+        # the even start's position (in units of u) just before the first tie
+        pos = ((1 << e) + (1 << (e - 2))) // u
+        for t in tl[: ties[0]]:
+            pos += (t + u // 2) // u  # no tie here: the nearest multiple
+        q = tl[ties[0]] // u
+        # the even start rounds down when pos + q is even, the odd start
+        # (one further) then rounds up: one u more
+        assert a1 - a0 == (u if (pos + q) % 2 == 0 else -u), (e, n, kind)
+
+
 def test_closed_form_premise():
     """Every float square in units is 0 or 1 modulo 4, and odd exactly when
     the codeword is odd and below 4096 (exhaustive over 16-bit samples)."""
