@@ -14,9 +14,11 @@
 //    at most three groups of its kWalkThreads runs (apply_groups), else
 //    its runs one by one under the binade S is in and the next, else its
 //    terms with the one-term step;
-//  - the fast path: the plan as five threshold edges, exact and
-//    closed-form stretches, the rows and terms at an edge one by one, and
-//    noise stretches as composed row pairs.
+//  - the fast path: the plan as five threshold edges (seven for planes
+//    whose sum lies in the binade of 2^55), exact and closed-form
+//    stretches, stretches in the binade of 2^55 as joined pairs (of rows
+//    as k_pairs forms them, or of a row's lane runs), the rows and terms at
+//    an edge one by one, and noise stretches as composed row pairs.
 // The pages' own host test checks their twins' steps the same way, under
 // correct plans and under plans broken on purpose (ADR-1497, Decision).
 #include <errno.h>
@@ -81,6 +83,25 @@ Pair64 block_compose(int a, int b, int sh, PairOf pair_of) {
   return tree64(leaves, sh);
 }
 
+// Row i's pair under binade e as k_pairs forms it: segments of kPairSeg
+// samples, each split into kPairLanes runs of ceil(n / kPairLanes) terms
+// (each added from both starts with the double add) joined by a balanced
+// tree, the segments joined in row order, widened with the row's exact sum.
+Pair64 kpairs_row_pair(const Plane& pl, int i, int e, uint64_t Ri) {
+  const int sh = e - 52, w = pl.w;
+  Pair32 acc = pair32_id();
+  for (int s0 = 0; s0 < w; s0 += kPairSeg) {
+    const int n = std::min(kPairSeg, w - s0), L = (n + kPairLanes - 1) / kPairLanes;
+    std::vector<Pair32> lanes(kPairLanes);
+    for (int l = 0; l < kPairLanes; ++l) {
+      const int j0 = std::min(l * L, n), j1 = std::min(j0 + L, n);
+      lanes[l] = run_pair([&](int j) { return (double)fsq_units(pl.x(i, s0 + j0 + j)); }, j1 - j0, e);
+    }
+    acc = then32(acc, tree32(lanes, sh), sh);
+  }
+  return widen_pair(acc, Ri);
+}
+
 struct Emu {
   Plane pl;
   unsigned dbg;
@@ -97,18 +118,7 @@ struct Emu {
   // the segments joined in row order, widened with the row's exact sum.
   Pair64 row_pair(int i, int e) const {
     if (e <= 54 && !(dbg & BEF_DBG_NO_CLOSED_FORM)) return closed_pair(R[i], C[i], e);
-    const int sh = e - 52, w = pl.w;
-    Pair32 acc = pair32_id();
-    for (int s0 = 0; s0 < w; s0 += kPairSeg) {
-      const int n = std::min(kPairSeg, w - s0), L = (n + kPairLanes - 1) / kPairLanes;
-      std::vector<Pair32> lanes(kPairLanes);
-      for (int l = 0; l < kPairLanes; ++l) {
-        const int j0 = std::min(l * L, n), j1 = std::min(j0 + L, n);
-        lanes[l] = run_pair([&](int j) { return (double)T(i, s0 + j0 + j); }, j1 - j0, e);
-      }
-      acc = then32(acc, tree32(lanes, sh), sh);
-    }
-    return widen_pair(acc, R[i]);
+    return kpairs_row_pair(pl, i, e, R[i]);
   }
 
   uint64_t terms(uint64_t s, int i, int j0, int j1) const {
@@ -325,27 +335,28 @@ struct Emu {
 // The device finds the same first items with lane chunks and a second
 // scan; the decisions and every arithmetic step are these.
 
+template <int NE = kEdges>
 struct Edges {
-  int x[kEdges + 1];
-  uint64_t P[kEdges + 1], PC[kEdges + 1];
+  int x[NE + 1];
+  uint64_t P[NE + 1], PC[NE + 1];
 };
 
-template <class EAt, class CAt>
-Edges first_items(int n, uint64_t base, uint64_t M, EAt e_at, CAt c_at) {
-  Edges r;
+template <int NE = kEdges, class EAt, class CAt>
+Edges<NE> first_items(int n, uint64_t base, uint64_t M, EAt e_at, CAt c_at) {
+  Edges<NE> r;
   uint64_t q = base, qc = 0;
   unsigned seen = 0;
-  for (int j = 0; j <= kEdges; ++j) r.x[j] = n;
+  for (int j = 0; j <= NE; ++j) r.x[j] = n;
   for (int k = 0; k < n; ++k) {
     const uint64_t e = e_at(k);
-    const unsigned now = edge_conds(q, q + e, M), fresh = now & ~seen;
-    for (int j = 0; j < kEdges; ++j)
+    const unsigned now = edge_conds<NE>(q, q + e, M), fresh = now & ~seen;
+    for (int j = 0; j < NE; ++j)
       if ((fresh >> j) & 1u) r.x[j] = k, r.P[j] = q, r.PC[j] = qc;
     seen |= now;
     q += e;
     qc += c_at(k);
   }
-  for (int j = 0; j <= kEdges; ++j)
+  for (int j = 0; j <= NE; ++j)
     if (r.x[j] == n) r.P[j] = q, r.PC[j] = qc;
   return r;
 }
@@ -357,23 +368,39 @@ struct Fast {
   uint32_t T(int i, int j) const { return fsq_units(pl.x(i, j)); }
 
   // A row across an edge: its terms' edges from the actual S with margin
-  // w * u/2, closed forms, and the terms at an edge by the one-term step.
+  // w * u/2, closed forms, and the terms at an edge by the one-term step;
+  // with seven edges, the row's part inside the binade of 2^55 as the pair
+  // of the lanes' runs of the staged row (lane l: 8-sample chunks [l*cpl,
+  // l*cpl + cpl)) joined by a balanced tree.
+  template <int NE>
   bool cross_row(uint64_t* sp, int i) const {
     const uint64_t s0 = *sp;
     const int eB = (s0 < kTwo53 ? 53 : binade(s0)) + 1;
     const uint64_t Mr = (uint64_t)pl.w << (eB - 53);
-    const Edges ed = first_items(
+    const Edges<NE> ed = first_items<NE>(
         pl.w, s0, Mr, [&](int k) { return (uint64_t)T(i, k); },
         [&](int k) { return (uint64_t)(T(i, k) & 1u); });
     uint64_t s = s0, Pa = s0, PCa = 0;
     int a = 0;
-    for (int g = 0; g <= kEdges; ++g) {
+    for (int g = 0; g <= NE; ++g) {
       const int b = ed.x[g];
       if (b < a) return false;
       if (b > a) {
-        if (g == 1 || g == 3) {
+        if (g == 1 || g == 3 || (NE == kEdges56 && g == 5)) {
           for (int k = a; k < b; ++k) s = rne53_add(s, T(i, k));
-        } else if (!fast_apply(&s, g, ed.P[g] - Pa, ed.PC[g] - PCa)) {
+        } else if (NE == kEdges56 && g == 6) {
+          const int L = 8 * ((((pl.w + 7) >> 3) + 63) >> 6);
+          std::vector<Pair64> lanes(64, pair64_id());
+          for (int l = 0; l < 64; ++l) {
+            const int j0 = std::max(std::min(l * L, pl.w), a);
+            const int j1 = std::min(std::min(l * L + L, pl.w), b);
+            if (j1 <= j0) continue;
+            uint64_t E = 0;
+            for (int k = j0; k < j1; ++k) E += T(i, k);
+            lanes[l] = widen_pair(run_pair([&](int j) { return (double)T(i, j0 + j); }, j1 - j0, 55), E);
+          }
+          if (!try_apply(&s, tree64(lanes, 3), 55)) return false;
+        } else if (!fast_apply<NE>(&s, g, ed.P[g] - Pa, ed.PC[g] - PCa)) {
           return false;
         }
       }
@@ -385,38 +412,41 @@ struct Fast {
     return true;
   }
 
-  // out = {handled, S_cpu, S_exact}
-  void run(uint64_t out[3]) {
+  // The walk with NE edges; the stretch inside the binade of 2^55 composes
+  // the rows' pairs as k_pairs forms them, lane l joining rows [a + l*rs,
+  // ...) in order, then a balanced tree over the lanes.
+  template <int NE>
+  void walk(uint64_t out[3]) const {
     const int h = pl.h, w = pl.w;
-    R.assign(h, 0);
-    C.assign(h, 0);
-    for (int i = 0; i < h; ++i)
-      for (int j = 0; j < w; ++j) {
-        R[i] += T(i, j);
-        C[i] += T(i, j) & 1u;
-      }
-    const Edges ed = first_items(
-        h, 0, 2ull * (uint64_t)w * (uint64_t)h, [&](int k) { return R[k]; },
-        [&](int k) { return C[k]; });
+    const uint64_t M = (NE == kEdges56 ? 4ull : 2ull) * (uint64_t)w * (uint64_t)h;
+    const Edges<NE> ed = first_items<NE>(
+        h, 0, M, [&](int k) { return R[k]; }, [&](int k) { return C[k]; });
     out[0] = 0;
-    out[2] = ed.P[kEdges];
-    if (ed.P[kEdges] >= (1ull << 55)) return;
+    out[2] = ed.P[NE];
+    if (ed.P[NE] >= (NE == kEdges56 ? (1ull << 56) : (1ull << 55))) return;
     uint64_t s = 0, Pa = 0, PCa = 0;
     int a = 0;
-    for (int g = 0; g <= kEdges; ++g) {
+    for (int g = 0; g <= NE; ++g) {
       const int b = ed.x[g];
       if (b < a) return;
       if (b > a) {
-        if (g == 1 || g == 3) {
+        if (g == 1 || g == 3 || (NE == kEdges56 && g == 5)) {
           for (int i = a; i < b; ++i) {
             if (try_exact(&s, R[i])) continue;
             if (s >= kTwo53) {
               const int e = binade(s);
               if (e <= 54 && try_apply(&s, closed_pair(R[i], C[i], e), e)) continue;
             }
-            if (!cross_row(&s, i)) return;
+            if (!cross_row<NE>(&s, i)) return;
           }
-        } else if (!fast_apply(&s, g, ed.P[g] - Pa, ed.PC[g] - PCa)) {
+        } else if (NE == kEdges56 && g == 6) {
+          const int rs = (b - a + 63) >> 6;
+          std::vector<Pair64> lanes(64, pair64_id());
+          for (int l = 0; l < 64; ++l)
+            for (int i = std::min(a + l * rs, b); i < std::min(a + l * rs + rs, b); ++i)
+              lanes[l] = then64(lanes[l], kpairs_row_pair(pl, i, 55, R[i]), 3);
+          if (!try_apply(&s, tree64(lanes, 3), 55)) return;
+        } else if (!fast_apply<NE>(&s, g, ed.P[g] - Pa, ed.PC[g] - PCa)) {
           return;
         }
       }
@@ -426,6 +456,25 @@ struct Fast {
     }
     out[0] = 1;
     out[1] = s;
+  }
+
+  // out = {handled, S_cpu, S_exact}: five edges below 2^55, seven for a
+  // plane whose exact sum lies in [2^55, 2^56), as the device chooses from
+  // the plan kernel's plane sum.
+  void run(uint64_t out[3]) {
+    const int h = pl.h, w = pl.w;
+    R.assign(h, 0);
+    C.assign(h, 0);
+    uint64_t total = 0;
+    for (int i = 0; i < h; ++i) {
+      for (int j = 0; j < w; ++j) {
+        R[i] += T(i, j);
+        C[i] += T(i, j) & 1u;
+      }
+      total += R[i];
+    }
+    if (total >= (1ull << 55)) walk<kEdges56>(out);
+    else walk<kEdges>(out);
   }
 };
 

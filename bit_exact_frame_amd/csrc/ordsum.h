@@ -262,27 +262,47 @@ BEF_HD Pair64 noise_row_pair(uint64_t t, int sh) {
 //   x4: P + E + M >= 2^55   (first item that may leave that one)
 // The segments, in order: exact [0, x0), across [x0, x1), 53 [x1, x2),
 // across [x2, x3), 54 [x3, x4), beyond [x4, n).
+//
+// Planes whose exact sum lies in [2^55, 2^56) (their rows' pairs in the
+// binade of 2^55 formed beforehand) take seven edges, the same five and
+//   x5: P - M >= 2^55       (first item inside the binade of 2^55)
+//   x6: P + E + M >= 2^56   (first item that may leave it)
+// with the segments exact, across, 53, across, 54, across [x4, x5), 55
+// [x5, x6), beyond [x6, n).
 constexpr int kEdges = 5;
+constexpr int kEdges56 = 7;
 
 // Bit j: whether item k (exact prefix pk before it, pk1 after it) has met
-// the condition of edge j.
+// the condition of edge j (of NE edges).
+template <int NE = kEdges>
 BEF_HD unsigned edge_conds(uint64_t pk, uint64_t pk1, uint64_t M) {
-  constexpr uint64_t T53 = 1ull << 53, T54 = 1ull << 54, T55 = 1ull << 55;
+  constexpr uint64_t T53 = 1ull << 53, T54 = 1ull << 54, T55 = 1ull << 55, T56 = 1ull << 56;
   const uint64_t lo = pk > M ? pk - M : 0;
-  return (unsigned)(pk1 > T53) | (unsigned)(lo >= T53) << 1 | (unsigned)(pk1 + M >= T54) << 2 |
-         (unsigned)(lo >= T54) << 3 | (unsigned)(pk1 + M >= T55) << 4;
+  unsigned c = (unsigned)(pk1 > T53) | (unsigned)(lo >= T53) << 1 |
+               (unsigned)(pk1 + M >= T54) << 2 | (unsigned)(lo >= T54) << 3 |
+               (unsigned)(pk1 + M >= T55) << 4;
+  if constexpr (NE == kEdges56) c |= (unsigned)(lo >= T55) << 5 | (unsigned)(pk1 + M >= T56) << 6;
+  return c;
 }
 
 // Segment g's plan (0 exact, 1 across, 2 the binade of 2^53, 3 across, 4
-// the binade of 2^54, 5 beyond).
+// the binade of 2^54, then 5 beyond with five edges; with seven, 5 across,
+// 6 the binade of 2^55, 7 beyond).
+template <int NE = kEdges>
 BEF_HD int fast_plan(int g) {
-  return g == 0 ? kPlanExact : g == 2 ? 53 : g == 4 ? 54 : (g == 5 ? -2 : kPlanCross);
+  if (g == 0) return kPlanExact;
+  if (g == 2) return 53;
+  if (g == 4) return 54;
+  if (NE == kEdges56 && g == 6) return 55;
+  return g == NE ? -2 : kPlanCross;
 }
 
-// Applies segment g's exact, closed-form or beyond plan to s (Eg, Cg its
-// exact sum and odd count); false when it does not apply.
+// Applies segment g's exact or closed-form plan to s (Eg, Cg its exact sum
+// and odd count); false when it does not apply, and beyond the last edge
+// and in the binade of 2^55, whose pairs the caller composes.
+template <int NE = kEdges>
 BEF_HD bool fast_apply(uint64_t* s, int g, uint64_t Eg, uint64_t Cg) {
-  const int e = fast_plan(g);
+  const int e = fast_plan<NE>(g);
   if (e == kPlanExact) return try_exact(s, Eg);
   if (e == 53 || e == 54) return try_apply(s, closed_pair(Eg, Cg, e), e);
   return false;

@@ -980,18 +980,20 @@ constexpr int kRowsPer = (kChunk + kT - 1) / kT;  // rows per thread when loadin
 
 // ---------------------------------------------------------------------------
 // The fast path: one wave (64 lanes, no block barrier) per plane, with the
-// plan as five threshold edges (edge_conds, fast_plan, fast_apply in the
-// step header).
+// plan as five threshold edges, or seven for planes whose sum lies in the
+// binade of 2^55 (edge_conds, fast_plan, fast_apply in the step header).
 
-// Edges of n items (uniform over the wave): x[j], the exact prefix P[j]
-// (base included) and odd count PC[j] before each edge; entry kEdges is n
-// and the totals.
-struct WEdges {
-  int x[kEdges + 1];
-  uint64_t P[kEdges + 1];
-  uint32_t PC[kEdges + 1];
+// NE edges of n items (uniform over the wave): x[j], the exact prefix P[j]
+// (base included) and odd count PC[j] before each edge; entry NE is n and
+// the totals.
+template <int NE>
+struct WEdgesN {
+  int x[NE + 1];
+  uint64_t P[NE + 1];
+  uint32_t PC[NE + 1];
   bool ok;
 };
+using WEdges = WEdgesN<kEdges>;
 
 // Lane l owns items [l*c, l*c + c) with sum le, odd count lc and last item
 // value elast; item_at(k, &e, &cnt) gives any single item.  Each condition
@@ -999,10 +1001,10 @@ struct WEdges {
 // chunk starts false and ends true; that lane's items are then spread one
 // per lane, 64 at a time, and scanned again: the first item that meets the
 // condition is the edge.
-template <class ItemAt>
-__device__ __forceinline__ WEdges wave_edges(int n, int c, uint64_t le, uint32_t lc,
-                                             uint64_t elast, uint64_t base, uint64_t M,
-                                             ItemAt item_at) {
+template <int NE = kEdges, class ItemAt>
+__device__ __forceinline__ WEdgesN<NE> wave_edges(int n, int c, uint64_t le, uint32_t lc,
+                                                  uint64_t elast, uint64_t base, uint64_t M,
+                                                  ItemAt item_at) {
   const int lane = threadIdx.x & 63;
   const int a = min(lane * c, n), cl = min(c, n - a);
   const uint64_t P = base + wave_excl_scan_u64(le);
@@ -1010,19 +1012,19 @@ __device__ __forceinline__ WEdges wave_edges(int n, int c, uint64_t le, uint32_t
   const uint64_t T = rdl64(P + le, 63);
   const uint32_t TC = rdl32(PC + lc, 63);
   const uint64_t ep = lane_before_u64(elast);
-  const unsigned before = (cl > 0 && a > 0) ? edge_conds(P - ep, P, M) : 0u;
-  const unsigned last = cl > 0 ? edge_conds(P + le - elast, P + le, M) : 0u;
+  const unsigned before = (cl > 0 && a > 0) ? edge_conds<NE>(P - ep, P, M) : 0u;
+  const unsigned last = cl > 0 ? edge_conds<NE>(P + le - elast, P + le, M) : 0u;
   const unsigned own = last & ~before;
   const unsigned occurs = rdl32(last, (n - 1) / c);  // conditions at item n - 1
-  WEdges r;
+  WEdgesN<NE> r;
   r.ok = true;
 #pragma unroll
-  for (int j = 0; j <= kEdges; ++j) {
+  for (int j = 0; j <= NE; ++j) {
     r.x[j] = n;
     r.P[j] = T;
     r.PC[j] = TC;
   }
-  unsigned pending = occurs & 31u;
+  unsigned pending = occurs & ((1u << NE) - 1u);
   while (pending) {
     const int j0 = __builtin_ctz(pending);
     const uint64_t om = wave_ballot((own >> j0) & 1u);
@@ -1043,9 +1045,9 @@ __device__ __forceinline__ WEdges wave_edges(int n, int c, uint64_t le, uint32_t
       if (k < cnt) item_at(b0 + k, &e, &cc);
       const uint64_t q = q0 + wave_excl_scan_u64(e);
       const uint32_t qc = qc0 + wave_excl_scan_u32(cc);
-      const unsigned now = k < cnt ? edge_conds(q, q + e, M) : 0u;
+      const unsigned now = k < cnt ? edge_conds<NE>(q, q + e, M) : 0u;
 #pragma unroll
-      for (int j = 0; j < kEdges; ++j) {
+      for (int j = 0; j < NE; ++j) {
         if ((todo >> j) & 1u) {
           const uint64_t m = wave_ballot((now >> j) & 1u);
           if (m != 0) {
@@ -1139,10 +1141,36 @@ __device__ void wave_stage_row(RowStage& st, int i, const void* plane, long stri
   st.runC[lane] = c;
 }
 
+// The pair, inside the binade of 2^55, of the terms [ia, b) of a row staged
+// in st: lane l adds its share of its run (8-sample chunks [l*cpl, l*cpl +
+// cpl), read 16 bytes at a time; a term outside [ia, b) counts as 0, which
+// moves nothing) from both starts with the double add, and the lanes'
+// pairs are joined in order.  Uniform.
+__device__ Pair64 staged_pair55(const RowStage& st, int w, int ia, int b) {
+  const int lane = threadIdx.x & 63;
+  const int cpl = run_chunks(w);
+  RunF64 r = run_start(55);
+  uint64_t E = 0;
+  for (int c = lane * cpl; c < lane * cpl + cpl; ++c) {
+    const v4u x = ((const v4u*)st.x)[c];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int k = 8 * c + q;
+      const uint32_t t =
+          k >= ia && k < b ? fsq_units((x[q >> 1] >> (16 * (q & 1))) & 0xFFFFu) : 0u;
+      E += t;
+      run_add(r, (double)t);
+    }
+  }
+  return wave_then(widen_pair(run_end(r, 55), E), 3);
+}
+
 // Row (staged in st) planned across an edge, from S = *sp: lane l takes
 // the terms of its run, the terms' edges with margin w * u/2 (u the last
 // place of the binade above S), closed forms, and the terms across an edge
-// added with the double add (the CPU's step).
+// added with the double add (the CPU's step).  With seven edges (NE) the
+// row's part inside the binade of 2^55 adds its pair from staged_pair55.
+template <int NE = kEdges>
 __device__ bool wave_cross_row(uint64_t* sp, const RowStage& st, int w) {
   const int lane = threadIdx.x & 63;
   const uint64_t s0 = *sp;
@@ -1153,7 +1181,7 @@ __device__ bool wave_cross_row(uint64_t* sp, const RowStage& st, int w) {
   const uint64_t elast = cl > 0 ? fsq_units(st.x[a + cl - 1]) : 0;
   const int eB = (s0 < kTwo53 ? 53 : binade(s0)) + 1;
   const uint64_t Mr = (uint64_t)w << (eB - 53);
-  const WEdges ed = wave_edges(w, L, le, lc, elast, s0, Mr, [&](int k, uint64_t* e, uint32_t* c) {
+  const WEdgesN<NE> ed = wave_edges<NE>(w, L, le, lc, elast, s0, Mr, [&](int k, uint64_t* e, uint32_t* c) {
     const uint32_t x = fsq_units(st.x[k]);
     *e = x;
     *c = x & 1u;
@@ -1163,15 +1191,17 @@ __device__ bool wave_cross_row(uint64_t* sp, const RowStage& st, int w) {
   int ia = 0;
   uint64_t Pa = s0, PCa = 0;
 #pragma unroll
-  for (int g = 0; g <= kEdges; ++g) {
+  for (int g = 0; g <= NE; ++g) {
     const int b = ed.x[g];
     if (b < ia) return false;  // edges out of order: not the premise
     if (b > ia) {
-      if (g == 1 || g == 3) {
+      if (g == 1 || g == 3 || (NE == kEdges56 && g == 5)) {
         double d = (double)s;  // a value the CPU's double holds: exact
         for (int k = ia; k < b; ++k) d = d + (double)fsq_units(st.x[k]);
         s = (uint64_t)d;
-      } else if (!fast_apply(&s, g, ed.P[g] - Pa, ed.PC[g] - PCa)) {
+      } else if (NE == kEdges56 && g == 6) {
+        if (!try_apply(&s, staged_pair55(st, w, ia, b), 55)) return false;
+      } else if (!fast_apply<NE>(&s, g, ed.P[g] - Pa, ed.PC[g] - PCa)) {
         return false;
       }
     }
@@ -1190,10 +1220,17 @@ __device__ bool wave_cross_row(uint64_t* sp, const RowStage& st, int w) {
 // kStage).  Margin: with every sum below 2^55 the CPU's sum strays from the
 // exact prefix by at most 2 units per term added past 2^53.  Returns false
 // when the plane needs the general walk; *exact is set either way.
+// With seven edges (NE, for a plane whose exact sum k_plan found in
+// [2^55, 2^56)) the margin is 4 units per term (u/2 in the binade of
+// 2^55), the rows across 2^55 are walked like the others (staged in st0
+// when their turn comes), and the stretch inside the binade of 2^55
+// composes the rows' pairs that k_pairs left in rp (global, [row][2]): each
+// lane a run of rows in order, then the lanes in order.
+template <int NE = kEdges>
 __device__ bool wave_walk(uint64_t* out, uint64_t* exact, const uint64_t* lE, const uint16_t* lC,
                           const uint64_t* pe, const uint32_t* pc, int cs, int h,
                           const void* plane, long stride, int w, int bpc8, RowStage& st0,
-                          RowStage& st1) {
+                          RowStage& st1, const uint64_t* rp) {
   const int lane = threadIdx.x & 63;
   constexpr int PER = kT / 64;
   const int c = PER * cs;
@@ -1206,13 +1243,14 @@ __device__ bool wave_walk(uint64_t* out, uint64_t* exact, const uint64_t* lE, co
     lc += pc[lane * PER + q];
   }
   const uint64_t elast = cl > 0 ? lE[a + cl - 1] : 0;
-  const uint64_t M = 2ull * (uint64_t)w * (uint64_t)h;
-  const WEdges ed = wave_edges(h, c, le, lc, elast, 0, M, [&](int k, uint64_t* e, uint32_t* cc) {
+  const uint64_t M = (NE == kEdges56 ? 4ull : 2ull) * (uint64_t)w * (uint64_t)h;
+  const WEdgesN<NE> ed = wave_edges<NE>(h, c, le, lc, elast, 0, M, [&](int k, uint64_t* e, uint32_t* cc) {
     *e = lE[k];
     *cc = lC[k];
   });
-  *exact = ed.P[kEdges];
-  if (!ed.ok || ed.P[kEdges] >= (1ull << 55)) return false;
+  *exact = ed.P[NE];
+  if (!ed.ok || ed.P[NE] >= (NE == kEdges56 ? (1ull << 56) : (1ull << 55))) return false;
+  if (NE == kEdges56 && ed.x[5] < ed.x[6] && !rp) return false;  // no pairs for the binade of 2^55
   // the first row of each stretch across an edge, staged before its turn
   const int ra = ed.x[0] < ed.x[1] ? ed.x[0] : -1, rb = ed.x[2] < ed.x[3] ? ed.x[2] : -1;
   if (ra >= 0) wave_stage_row(st0, ra, plane, stride, w, bpc8);
@@ -1221,12 +1259,13 @@ __device__ bool wave_walk(uint64_t* out, uint64_t* exact, const uint64_t* lE, co
   uint64_t s = 0;
   int ia = 0;
   uint64_t Pa = 0, PCa = 0;
+  int rc = -1;  // the row of the third stretch across an edge held in st0
 #pragma unroll
-  for (int g = 0; g <= kEdges; ++g) {
+  for (int g = 0; g <= NE; ++g) {
     const int b = ed.x[g];
     if (b < ia) return false;  // edges out of order: not the premise
     if (b > ia) {
-      if (g == 1 || g == 3) {
+      if (g == 1 || g == 3 || (NE == kEdges56 && g == 5)) {
         for (int i = ia; i < b; ++i) {
           // a row that, from the actual S, adds exactly or stays inside its
           // binade needs no samples (rows of zeros after a crossing, say)
@@ -1235,15 +1274,30 @@ __device__ bool wave_walk(uint64_t* out, uint64_t* exact, const uint64_t* lE, co
             const int e = binade(s);
             if (e <= 54 && try_apply(&s, closed_pair(lE[i], lC[i], e), e)) continue;
           }
-          RowStage& sg = g == 1 ? st0 : st1;
-          if (i != (g == 1 ? ra : rb)) {  // a further row of the stretch
+          RowStage& sg = g == 3 ? st1 : st0;
+          if (i != (g == 1 ? ra : g == 3 ? rb : rc)) {  // a further row of the stretch
             wave_lds_sync();
             wave_stage_row(sg, i, plane, stride, w, bpc8);
             wave_lds_sync();
+            if (g == 5) rc = i;
           }
-          if (!wave_cross_row(&s, sg, w)) return false;
+          if (!wave_cross_row<NE>(&s, sg, w)) return false;
         }
-      } else if (!fast_apply(&s, g, ed.P[g] - Pa, ed.PC[g] - PCa)) {
+      } else if (NE == kEdges56 && g == 6) {
+        // lane l composes rows [ia + l*rs, ...) in order, eight loads in flight
+        const int rs = (b - ia + 63) >> 6;
+        const int r0 = min(ia + lane * rs, b), r1 = min(r0 + rs, b);
+        Pair64 acc = pair64_id();
+        for (int i0 = r0; i0 < r1; i0 += 8) {
+          Pair64 q[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            q[u] = i0 + u < r1 ? Pair64{rp[2 * (i0 + u)], rp[2 * (i0 + u) + 1]} : pair64_id();
+#pragma unroll
+          for (int u = 0; u < 8; ++u) acc = then64(acc, q[u], 3);
+        }
+        if (!try_apply(&s, wave_then(acc, 3), 55)) return false;
+      } else if (!fast_apply<NE>(&s, g, ed.P[g] - Pa, ed.PC[g] - PCa)) {
         return false;
       }
     }
@@ -1437,11 +1491,13 @@ __global__ void __launch_bounds__(kT) k_walk(Geometry g, RowArrays ra, double* r
   const int k = g.bpc - 8;
   const double n = (double)g.w * (double)g.h;
   const int wave = threadIdx.x >> 6;
-  // the fast path stops below 2^55: a plane k_plan has summed past it goes
-  // straight to the general walk
+  // the fast path stops below 2^56: a plane k_plan has summed past it goes
+  // straight to the general walk, and one it has summed into the binade of
+  // 2^55 takes the fast path's seven-edge form
+  const uint64_t planned_sum =
+      g.planned && job < 2 ? ra.psum[2 * (job * g.nframes + f)] : 0;
   const bool try_fast = dbg == 0 && g.may_round && g.h <= kChunk && g.w <= kStage &&
-                        !(g.planned && job < 2 &&
-                          ra.psum[2 * (job * g.nframes + f)] >= (1ull << 55));
+                        planned_sum < (1ull << 56);
   if (job == 2) {
     uint64_t ex = 0;
     double d = 0.0;
@@ -1535,8 +1591,12 @@ __global__ void __launch_bounds__(kT) k_walk(Geometry g, RowArrays ra, double* r
       pz[threadIdx.x] = z;
       __syncthreads();
       if (wave == 0) {
-        const bool ok = wave_walk(&S, &E, rows.R, rows.C, pe, pc, cs, g.h, plane, g.stride, g.w,
-                                  g.bpc == 8, stage[0], stage[1]);
+        const bool ok =
+            planned_sum >= (1ull << 55)
+                ? wave_walk<kEdges56>(&S, &E, rows.R, rows.C, pe, pc, cs, g.h, plane, g.stride,
+                                      g.w, g.bpc == 8, stage[0], stage[1], ra.pairs + 2 * off)
+                : wave_walk<kEdges>(&S, &E, rows.R, rows.C, pe, pc, cs, g.h, plane, g.stride,
+                                    g.w, g.bpc == 8, stage[0], stage[1], nullptr);
         uint64_t zz = 0;  // the first-moment sum, off the walk's path
 #pragma unroll
         for (int q = 0; q < kT / 64; ++q) zz += pz[(threadIdx.x & 63) * (kT / 64) + q];

@@ -267,6 +267,45 @@ def test_past_2_55_4096x2560(api, orc):
     check_batch(api, orc, ref, dis, 16, label="4096x2560 past 2^55")
 
 
+def binade55_plane(k: int):
+    """Seeded near-maximum 16-bit plane (a fraction of small codewords, some
+    of whose squares tie in the binade of 2^55) of width 3500-4096 and at
+    most 4352 rows, its exact sum in the binade of 2^55; k == 5: its last
+    15% of rows are zeros."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([0xBEF, 5555, k])))
+    w = int(rng.integers(3500, 4097))
+    pad = int(rng.choice([0, 0, 3, 8]))
+    lo = int(rng.integers(50000, 62000))
+    small = float(rng.choice([0.0, 0.02, 0.05, 0.2]))
+    target = float(rng.uniform(55.05, 55.9))
+    sq = np.arange(65536, dtype=np.float32) ** 2  # float squares of every codeword
+    mean = (1 - small) * float(sq[lo:].mean()) + small * float(sq[:8192].mean())
+    h = min(4352, int(2 ** target / (w * mean)))
+    body = synth.nearmax_plane(rng, h, w, lo, small)
+    if k == 5:
+        body[int(h * 0.85):] = 0
+    ref = np.full((1, h, w + pad), 0xFFFF, np.uint16)
+    ref[0, :, :w] = body
+    dis = np.full_like(ref, 0xFFFF)
+    dis[0, :, :w] = 0 if k % 2 else rng.integers(0, 65536, size=(h, w))
+    return ref, dis, w
+
+
+@pytest.mark.parametrize("k", range(6))
+def test_fast_walk_in_the_binade_of_2_55(api, orc, k):
+    """Planes whose exact sum lies in [2^55, 2^56), at most 4096 wide and
+    4352 tall, take the fast walk's seven-edge form (rows across 2^53, 2^54
+    and 2^55 walked term-wise, the stretch inside the binade of 2^55 as the
+    rows' pairs joined in order, a crossing row's part in that binade from
+    its lanes' runs) and give the oracle's bits; case 5 ends in rows of
+    zeros past 2^55 (ADR-1497, Decision: the walk's steps)."""
+    ref, dis, w = binade55_plane(k)
+    u = api.bef_frames_units(dev(ref), dev(dis), 16, w=w)
+    assert (1 << 55) <= int(u[0, 2]) < (1 << 56), int(u[0, 2])
+    check_batch(api, orc, ref, dis, 16, w=w, label=f"binade 55 plane {k}")
+    assert int(api.bef_walk_paths()[0, 0]) == 1  # the ref plane's moments: the fast walk
+
+
 def test_past_2_53_2560x1440_16bit(api, orc):
     """A 16-bit 2560x1440 frame past 2^53, the size on which the twins'
     rounded-once result was measured off (ADR-1497, Context).  High content
@@ -324,10 +363,12 @@ def test_one_chunk_of_rows_past_2_53(api, orc, h):
 
 def test_walk_paths(api):
     """Which path each walk block takes: the one-wave fast path on 16-bit
-    3840x2160 frames (full and half range), exact sums only on 10-bit
-    frames that cannot pass 2^53, the general walk past 2^55 and under a
-    test flag."""
-    cases = [(4, 2, [[1, 1, 1]]), (5, 2, [[1, 1, 1]]), (2, 2, [[0, 0, 0]]), (6, 1, [[2, 2, 1]])]
+    3840x2160 frames (full and half range) and on 4096x2560 frames whose
+    sums lie in the binade of 2^55 (its seven-edge form), exact sums only on
+    10-bit frames that cannot pass 2^53, the general walk on 7680x4320
+    planes (rows wider than the fast path stages) and under a test flag."""
+    cases = [(4, 2, [[1, 1, 1]]), (5, 2, [[1, 1, 1]]), (2, 2, [[0, 0, 0]]), (6, 1, [[2, 2, 1]]),
+             (7, 1, [[1, 1, 1]])]
     for key, nf, want in cases:
         ref, dis = synth.make_frames(key, frames=nf)
         say(f"[gpu] walk paths of workload {key}")

@@ -278,24 +278,38 @@ def letterbox_plane():
     return p
 
 
+@functools.lru_cache(maxsize=None)
+def past_2_56_plane():
+    """5120x4096 near-maximum content (one sample in twenty small): the
+    exact sum passes 2^56, beyond the fast path."""
+    rng = np.random.Generator(np.random.PCG64(2556))
+    return synth.nearmax_plane(rng, 4096, 5120, 60000).astype(np.uint16)
+
+
 def test_fast_emulation_matches_oracle(api):
     """The fast path's decisions (threshold edges, closed forms, rows and
-    terms at an edge) give the oracle's sum on every plane below 2^55, and
-    hand the planes past 2^55 to the general walk."""
-    cases = list(planes()) + [("letterbox", letterbox_plane())]
+    terms at an edge, and for sums in the binade of 2^55 the seven-edge form
+    with its pairs joined in that binade) give the oracle's sum on every
+    plane below 2^56 (8K noise and the 4096x2560 plane reach the binade of
+    2^55), and hand the planes past 2^56 to the general walk."""
+    cases = list(planes()) + [("letterbox", letterbox_plane()), ("past 2^56", past_2_56_plane())]
+    seen55 = 0
     for name, p in cases:
         got = api.fast_units(p, 16)
         exact = int(checkers.terms_moment(p).sum(dtype=np.uint64))
         assert got[2] == exact, name
-        if exact >= 1 << 55:
+        if exact >= 1 << 56:
             assert got[0] == 0, name
             continue
+        seen55 += exact >= 1 << 55
         if name == "letterbox":
             acc = oracle.Oracle().moment_sums(p, np.zeros_like(p), 16)
             want = int(math.ldexp(acc[2], 16))
         else:
             want = oracle_units(name)[1]
         assert got[0] == 1 and got[1] == want, (name, got, want)
+    assert seen55 == 2
+    assert int(checkers.terms_moment(past_2_56_plane()).sum(dtype=np.uint64)) >= 1 << 56
 
 
 @pytest.mark.parametrize("k", range(random_frames.N_CASES))
