@@ -61,9 +61,11 @@ def test_noalloc_matches_async_larger_then_smaller(api):
     """Calls in a row, each against bef_frames_async: 16 frames of 16-bit
     3840x2160 noise (past 2^53), then 3 of the 10-bit 1920x1080 workload
     (smaller), then 2 of 16-bit 7680x4320 noise (past 2^55: plan and row
-    pairs in the scratch), then 1 frame of 8-bit 176x144 (smaller again).
+    pairs in the scratch), then 2 of 16-bit 4096x2560 near-maximum content
+    (in the binade of 2^55: the fast walk's seven-edge form reads the row
+    pairs from the scratch), then 1 frame of 8-bit 176x144 (smaller again).
     The 8-bit frame is also checked against the oracle."""
-    cases = [(4, 16), (2, 3), (6, 2), (1, 1)]
+    cases = [(4, 16), (2, 3), (6, 2), (7, 2), (1, 1)]
     for key, nf in cases:
         wl = synth.WORKLOADS[key]
         ref, dis = synth.make_frames(key, frames=nf)
