@@ -1141,6 +1141,54 @@ __device__ void wave_stage_row(RowStage& st, int i, const void* plane, long stri
   st.runC[lane] = c;
 }
 
+// Rows ia and ib staged into sa and sb as wave_stage_row does, with both
+// rows' loads in flight before either is used (one memory round trip for
+// the two) when both rows hold whole 8-sample chunks on 16-byte
+// boundaries; otherwise one after the other.
+__device__ void wave_stage_rows2(RowStage& sa, int ia, RowStage& sb, int ib, const void* plane,
+                                 long stride, int w, int bpc8) {
+  const int lane = threadIdx.x & 63;
+  const uint16_t* ra = (const uint16_t*)plane + (long)ia * stride;
+  const uint16_t* rb = (const uint16_t*)plane + (long)ib * stride;
+  if (bpc8 || (w & 7) != 0 || (((uintptr_t)ra | (uintptr_t)rb) & 15) != 0) {
+    wave_stage_row(sa, ia, plane, stride, w, bpc8);
+    wave_stage_row(sb, ib, plane, stride, w, bpc8);
+    return;
+  }
+  const int cpl = run_chunks(w), nv = w >> 3;
+  constexpr int U = kStage / 8 / 64;
+  v4u va[U], vb[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {  // every load of both rows issued before the first use
+    const int cidx = lane * cpl + u;
+    const bool in = u < cpl && cidx < nv;
+    va[u] = in ? ((const v4u*)ra)[cidx] : (v4u){0u, 0u, 0u, 0u};
+    vb[u] = in ? ((const v4u*)rb)[cidx] : (v4u){0u, 0u, 0u, 0u};
+  }
+  uint64_t ea = 0, eb = 0;
+  uint32_t ca = 0, cb = 0;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (u < cpl) {
+      ((v4u*)sa.x)[lane * cpl + u] = va[u];
+      ((v4u*)sb.x)[lane * cpl + u] = vb[u];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const uint32_t ta = fsq_units((va[u][q >> 1] >> (16 * (q & 1))) & 0xFFFFu);
+        const uint32_t tb = fsq_units((vb[u][q >> 1] >> (16 * (q & 1))) & 0xFFFFu);
+        ea += ta;
+        ca += ta & 1u;
+        eb += tb;
+        cb += tb & 1u;
+      }
+    }
+  }
+  sa.runE[lane] = ea;
+  sa.runC[lane] = ca;
+  sb.runE[lane] = eb;
+  sb.runC[lane] = cb;
+}
+
 // The pair, inside the binade of 2^55, of the terms [ia, b) of a row staged
 // in st: lane l adds its share of its run (8-sample chunks [l*cpl, l*cpl +
 // cpl), read 16 bytes at a time; a term outside [ia, b) counts as 0, which
@@ -1253,8 +1301,12 @@ __device__ bool wave_walk(uint64_t* out, uint64_t* exact, const uint64_t* lE, co
   if (NE == kEdges56 && ed.x[5] < ed.x[6] && !rp) return false;  // no pairs for the binade of 2^55
   // the first row of each stretch across an edge, staged before its turn
   const int ra = ed.x[0] < ed.x[1] ? ed.x[0] : -1, rb = ed.x[2] < ed.x[3] ? ed.x[2] : -1;
-  if (ra >= 0) wave_stage_row(st0, ra, plane, stride, w, bpc8);
-  if (rb >= 0) wave_stage_row(st1, rb, plane, stride, w, bpc8);
+  if (ra >= 0 && rb >= 0) {
+    wave_stage_rows2(st0, ra, st1, rb, plane, stride, w, bpc8);
+  } else {
+    if (ra >= 0) wave_stage_row(st0, ra, plane, stride, w, bpc8);
+    if (rb >= 0) wave_stage_row(st1, rb, plane, stride, w, bpc8);
+  }
   wave_lds_sync();
   uint64_t s = 0;
   int ia = 0;
