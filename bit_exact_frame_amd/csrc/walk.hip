@@ -540,7 +540,8 @@ __global__ void __launch_bounds__(256) k_pairs_pipe(Geometry g, RowArrays ra, un
 // is 0 or 1 modulo 4, so in the binades of 2^53 and 2^54 a stretch's pair
 // follows from its exact sum and its count of odd squares.
 
-constexpr int kStage = 4096;  // samples of one row staged in LDS by the fast walk
+constexpr int kStage = 8192;  // samples of one row staged in LDS by the fast walk (max w)
+constexpr int kStageRound = 8;  // 16-byte chunks a lane of the fast walk has in flight at once
 constexpr int kRowMax = 32768;  // samples of one row staged in LDS by the general walk (max w)
 constexpr int kMaxSeg = kWalkMaxSeg;  // segments a walk handles as segments
 
@@ -956,11 +957,11 @@ struct Walker {
 // The plane's row sums sit in LDS; the plan is five threshold edges (below),
 // found by two wave scans; stretches planned exact or in the binades of
 // 2^53 and 2^54 are added from prefix differences (closed form); a row
-// across an edge is split into 64 lane runs the same way, and only the
-// terms at an edge go one at a time, with the double add.  Anything else
-// (planes taller than one chunk, rows wider than kStage, sums from 2^55, a
-// stretch that is refused, test modes) returns false and the general walk
-// runs instead.
+// across an edge, staged beforehand by the whole block, is split into 64
+// lane runs the same way, and only the terms at an edge go one at a time,
+// with the double add.  Anything else (planes taller than one chunk, rows
+// wider than kStage, sums from 2^56, a stretch that is refused, test modes)
+// returns false and the general walk runs instead.
 
 // With every sum below 2^55 an item's plan follows from where its exact
 // interval [P - M, P + E + M] lies against 2^53, 2^54 and 2^55.  Each edge
@@ -1085,8 +1086,9 @@ struct RowStage {
 __device__ __forceinline__ int run_chunks(int w) { return (((w + 7) >> 3) + 63) >> 6; }
 
 // Loads row i of the plane into st by one wave: each lane loads its own
-// run (16-byte loads when the row allows them) and sums its terms from the
-// loaded registers.
+// run (16-byte loads when the row allows them, kStageRound of them in
+// flight at a time: one round for rows up to 4096 samples, two up to
+// kStage) and sums its terms from the loaded registers.
 __device__ void wave_stage_row(RowStage& st, int i, const void* plane, long stride, int w,
                                int bpc8) {
   const int lane = threadIdx.x & 63;
@@ -1097,22 +1099,23 @@ __device__ void wave_stage_row(RowStage& st, int i, const void* plane, long stri
     const uint16_t* row = (const uint16_t*)plane + (long)i * stride;
     if (((uintptr_t)row & 15) == 0 && (w & 7) == 0) {
       const int nv = w >> 3;
-      constexpr int U = kStage / 8 / 64;
-      v4u v[U];
+      for (int r0 = 0; r0 < cpl; r0 += kStageRound) {
+        v4u v[kStageRound];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {  // every load issued before the first use
-        const int cidx = lane * cpl + u;
-        v[u] = u < cpl && cidx < nv ? ((const v4u*)row)[cidx] : (v4u){0u, 0u, 0u, 0u};
-      }
+        for (int u = 0; u < kStageRound; ++u) {  // the round's loads issued before the first use
+          const int cidx = lane * cpl + r0 + u;
+          v[u] = r0 + u < cpl && cidx < nv ? ((const v4u*)row)[cidx] : (v4u){0u, 0u, 0u, 0u};
+        }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (u < cpl) {
-          ((v4u*)st.x)[lane * cpl + u] = v[u];
+        for (int u = 0; u < kStageRound; ++u) {
+          if (r0 + u < cpl) {
+            ((v4u*)st.x)[lane * cpl + r0 + u] = v[u];
 #pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            const uint32_t t = fsq_units((v[u][q >> 1] >> (16 * (q & 1))) & 0xFFFFu);
-            e += t;
-            c += t & 1u;
+            for (int q = 0; q < 8; ++q) {
+              const uint32_t t = fsq_units((v[u][q >> 1] >> (16 * (q & 1))) & 0xFFFFu);
+              e += t;
+              c += t & 1u;
+            }
           }
         }
       }
@@ -1141,52 +1144,80 @@ __device__ void wave_stage_row(RowStage& st, int i, const void* plane, long stri
   st.runC[lane] = c;
 }
 
-// Rows ia and ib staged into sa and sb as wave_stage_row does, with both
-// rows' loads in flight before either is used (one memory round trip for
-// the two) when both rows hold whole 8-sample chunks on 16-byte
-// boundaries; otherwise one after the other.
-__device__ void wave_stage_rows2(RowStage& sa, int ia, RowStage& sb, int ib, const void* plane,
-                                 long stride, int w, int bpc8) {
-  const int lane = threadIdx.x & 63;
-  const uint16_t* ra = (const uint16_t*)plane + (long)ia * stride;
-  const uint16_t* rb = (const uint16_t*)plane + (long)ib * stride;
-  if (bpc8 || (w & 7) != 0 || (((uintptr_t)ra | (uintptr_t)rb) & 15) != 0) {
-    wave_stage_row(sa, ia, plane, stride, w, bpc8);
-    wave_stage_row(sb, ib, plane, stride, w, bpc8);
-    return;
-  }
-  const int cpl = run_chunks(w), nv = w >> 3;
-  constexpr int U = kStage / 8 / 64;
-  v4u va[U], vb[U];
+// The rows rr[0..2] of the plane (-1: none) staged in st[0..2] by the whole
+// block, as wave_stage_row stages one: every thread loads its share of
+// every row, coalesced, all loads in flight at once (16-byte chunks when
+// the rows allow them, else sample by sample), with zeros from w up to the
+// lanes' last run; after a block barrier, the eight threads [8l, 8l + 8) sum
+// run l of each row (every eighth chunk each), joined by three DPP steps
+// inside their group of eight lanes.  Ends with a block barrier: every
+// thread of the block must call it, with the same rows.
+__device__ void block_stage_rows(RowStage* st, const int* rr, const void* plane, long stride,
+                                 int w, int bpc8) {
+  const int t = threadIdx.x;
+  const int cpl = run_chunks(w), nc = 64 * cpl;  // chunks held per row
+  bool vec = !bpc8 && (w & 7) == 0;
+  for (int r = 0; r < 3; ++r)
+    if (rr[r] >= 0) vec = vec && ((uintptr_t)((const uint16_t*)plane + (long)rr[r] * stride) & 15) == 0;
+  if (vec) {
+    const int nv = w >> 3;
+    constexpr int K = kStage / 8 / kT;  // chunks of a row per thread
+    v4u v[3][K];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {  // every load of both rows issued before the first use
-    const int cidx = lane * cpl + u;
-    const bool in = u < cpl && cidx < nv;
-    va[u] = in ? ((const v4u*)ra)[cidx] : (v4u){0u, 0u, 0u, 0u};
-    vb[u] = in ? ((const v4u*)rb)[cidx] : (v4u){0u, 0u, 0u, 0u};
-  }
-  uint64_t ea = 0, eb = 0;
-  uint32_t ca = 0, cb = 0;
+    for (int r = 0; r < 3; ++r) {
+      const v4u* row = (const v4u*)((const uint16_t*)plane + (long)max(rr[r], 0) * stride);
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    if (u < cpl) {
-      ((v4u*)sa.x)[lane * cpl + u] = va[u];
-      ((v4u*)sb.x)[lane * cpl + u] = vb[u];
+      for (int k = 0; k < K; ++k) {
+        const int c = t + k * kT;
+        v[r][k] = rr[r] >= 0 && c < nv ? row[c] : (v4u){0u, 0u, 0u, 0u};
+      }
+    }
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const uint32_t ta = fsq_units((va[u][q >> 1] >> (16 * (q & 1))) & 0xFFFFu);
-        const uint32_t tb = fsq_units((vb[u][q >> 1] >> (16 * (q & 1))) & 0xFFFFu);
-        ea += ta;
-        ca += ta & 1u;
-        eb += tb;
-        cb += tb & 1u;
+    for (int r = 0; r < 3; ++r)
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int c = t + k * kT;
+        if (rr[r] >= 0 && c < nc) ((v4u*)st[r].x)[c] = v[r][k];
+      }
+  } else {
+    for (int r = 0; r < 3; ++r) {
+      if (rr[r] < 0) continue;
+      for (int j = t; j < 8 * nc; j += kT) {
+        uint32_t x = 0;
+        if (j < w)
+          x = bpc8 ? ((const uint8_t*)plane)[(long)rr[r] * stride + j]
+                   : ((const uint16_t*)plane)[(long)rr[r] * stride + j];
+        st[r].x[j] = (uint16_t)x;
       }
     }
   }
-  sa.runE[lane] = ea;
-  sa.runC[lane] = ca;
-  sb.runE[lane] = eb;
-  sb.runC[lane] = cb;
+  __syncthreads();
+  const int l = t >> 3, p = t & 7;
+  for (int r = 0; r < 3; ++r) {
+    if (rr[r] < 0) continue;
+    uint64_t e = 0;
+    uint32_t c = 0;
+    for (int j = p; j < cpl; j += 8) {
+      const v4u x = ((const v4u*)st[r].x)[l * cpl + j];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const uint32_t tq = fsq_units((x[q >> 1] >> (16 * (q & 1))) & 0xFFFFu);
+        e += tq;
+        c += tq & 1u;
+      }
+    }
+    e += dpp64<0xB1>(e);   // quad_perm [1,0,3,2]
+    e += dpp64<0x4E>(e);   // quad_perm [2,3,0,1]
+    e += dpp64<0x141>(e);  // row_half_mirror: the two quads of each group of eight
+    c += dpp32<0xB1>(c);
+    c += dpp32<0x4E>(c);
+    c += dpp32<0x141>(c);
+    if (p == 0) {
+      st[r].runE[l] = e;
+      st[r].runC[l] = c;
+    }
+  }
+  __syncthreads();
 }
 
 // The pair, inside the binade of 2^55, of the terms [ia, b) of a row staged
@@ -1236,11 +1267,13 @@ __device__ bool wave_cross_row(uint64_t* sp, const RowStage& st, int w) {
   });
   if (!ed.ok) return false;
   uint64_t s = s0;
-  int ia = 0;
-  uint64_t Pa = s0, PCa = 0;
 #pragma unroll
   for (int g = 0; g <= NE; ++g) {
-    const int b = ed.x[g];
+    // the segment [ia, b) and the exact prefix and odd count at its start,
+    // read from the edges (nothing carried from one segment to the next)
+    const int ia = g == 0 ? 0 : ed.x[g > 0 ? g - 1 : 0], b = ed.x[g];
+    const uint64_t Pa = g == 0 ? s0 : ed.P[g > 0 ? g - 1 : 0];
+    const uint64_t PCa = g == 0 ? 0 : ed.PC[g > 0 ? g - 1 : 0];
     if (b < ia) return false;  // edges out of order: not the premise
     if (b > ia) {
       if (g == 1 || g == 3 || (NE == kEdges56 && g == 5)) {
@@ -1253,32 +1286,34 @@ __device__ bool wave_cross_row(uint64_t* sp, const RowStage& st, int w) {
         return false;
       }
     }
-    ia = b;
-    Pa = ed.P[g];
-    PCa = ed.PC[g];
   }
   *sp = s;
   return true;
 }
 
-// The fast walk of one plane by one wave: rows' exact sums and odd counts
-// in lE / lC (LDS, h <= kChunk), and per block thread t the sums of rows
-// [t*cs, t*cs + cs) in pe / pc; lane l takes the rows of threads
-// [8l, 8l + 8).  Samples are read only for rows across an edge (w <=
-// kStage).  Margin: with every sum below 2^55 the CPU's sum strays from the
-// exact prefix by at most 2 units per term added past 2^53.  Returns false
-// when the plane needs the general walk; *exact is set either way.
-// With seven edges (NE, for a plane whose exact sum k_plan found in
-// [2^55, 2^56)) the margin is 4 units per term (u/2 in the binade of
-// 2^55), the rows across 2^55 are walked like the others (staged in st0
-// when their turn comes), and the stretch inside the binade of 2^55
-// composes the rows' pairs that k_pairs left in rp (global, [row][2]): each
-// lane a run of rows in order, then the lanes in order.
+// The fast walk of one plane: rows' exact sums and odd counts in lE / lC
+// (LDS, h <= kChunk), and per block thread t the sums of rows [t*cs, t*cs +
+// cs) in pe / pc; lane l takes the rows of threads [8l, 8l + 8).  Samples
+// are read only for rows across an edge (w <= kStage).  Margin: with every
+// sum below 2^55 the CPU's sum strays from the exact prefix by at most 2
+// units per term added past 2^53.  With seven edges (NE, for a plane whose
+// exact sum k_plan found in [2^55, 2^56)) the margin is 4 units per term
+// (u/2 in the binade of 2^55), the rows across 2^55 are walked like the
+// others, and the stretch inside the binade of 2^55 composes the rows'
+// pairs that k_pairs left in rp (global, [row][2]): each lane a run of rows
+// in order, then the lanes in order.
+//
+// In three steps: wave 0 finds the plane's edges (plane_edges), the block
+// stages the first row of each stretch across an edge (block_stage_rows),
+// then wave 0 walks the segments (walk_segments).
+
+// The plane's edges, by one wave; ed.ok false when the plane is not the
+// fast walk's (not the premise, or a sum past the form's last edge, or no
+// pairs for a stretch in the binade of 2^55).
 template <int NE = kEdges>
-__device__ bool wave_walk(uint64_t* out, uint64_t* exact, const uint64_t* lE, const uint16_t* lC,
-                          const uint64_t* pe, const uint32_t* pc, int cs, int h,
-                          const void* plane, long stride, int w, int bpc8, RowStage& st0,
-                          RowStage& st1, const uint64_t* rp) {
+__device__ WEdgesN<NE> plane_edges(const uint64_t* lE, const uint16_t* lC, const uint64_t* pe,
+                                   const uint32_t* pc, int cs, int h, int w,
+                                   const uint64_t* rp) {
   const int lane = threadIdx.x & 63;
   constexpr int PER = kT / 64;
   const int c = PER * cs;
@@ -1292,32 +1327,44 @@ __device__ bool wave_walk(uint64_t* out, uint64_t* exact, const uint64_t* lE, co
   }
   const uint64_t elast = cl > 0 ? lE[a + cl - 1] : 0;
   const uint64_t M = (NE == kEdges56 ? 4ull : 2ull) * (uint64_t)w * (uint64_t)h;
-  const WEdgesN<NE> ed = wave_edges<NE>(h, c, le, lc, elast, 0, M, [&](int k, uint64_t* e, uint32_t* cc) {
+  WEdgesN<NE> ed = wave_edges<NE>(h, c, le, lc, elast, 0, M, [&](int k, uint64_t* e, uint32_t* cc) {
     *e = lE[k];
     *cc = lC[k];
   });
-  *exact = ed.P[NE];
-  if (!ed.ok || ed.P[NE] >= (NE == kEdges56 ? (1ull << 56) : (1ull << 55))) return false;
-  if (NE == kEdges56 && ed.x[5] < ed.x[6] && !rp) return false;  // no pairs for the binade of 2^55
-  // the first row of each stretch across an edge, staged before its turn
-  const int ra = ed.x[0] < ed.x[1] ? ed.x[0] : -1, rb = ed.x[2] < ed.x[3] ? ed.x[2] : -1;
-  if (ra >= 0 && rb >= 0) {
-    wave_stage_rows2(st0, ra, st1, rb, plane, stride, w, bpc8);
-  } else {
-    if (ra >= 0) wave_stage_row(st0, ra, plane, stride, w, bpc8);
-    if (rb >= 0) wave_stage_row(st1, rb, plane, stride, w, bpc8);
-  }
-  wave_lds_sync();
+  if (ed.P[NE] >= (NE == kEdges56 ? (1ull << 56) : (1ull << 55))) ed.ok = false;
+  if (NE == kEdges56 && ed.x[5] < ed.x[6] && !rp) ed.ok = false;  // no pairs for the binade of 2^55
+  return ed;
+}
+
+// The first row of each stretch across an edge (g = 1, 3 and, with seven
+// edges, 5), or -1 where the stretch is empty.
+template <int NE = kEdges>
+__device__ __forceinline__ int across_row(const WEdgesN<NE>& ed, int k) {
+  if (k == 2 && NE != kEdges56) return -1;
+  return ed.x[2 * k] < ed.x[2 * k + 1] ? ed.x[2 * k] : -1;
+}
+
+// The segments in order, by one wave, from S = 0: st[k] holds row
+// staged[k], the first row of stretch g = 2k + 1; a further row of such a
+// stretch is staged by the wave in its turn.  Returns false when the plane
+// needs the general walk.
+template <int NE = kEdges>
+__device__ bool walk_segments(uint64_t* out, const WEdgesN<NE>& ed, const uint64_t* lE,
+                              const uint16_t* lC, const void* plane, long stride, int w, int bpc8,
+                              RowStage* st, int* staged, const uint64_t* rp) {
+  const int lane = threadIdx.x & 63;
   uint64_t s = 0;
-  int ia = 0;
-  uint64_t Pa = 0, PCa = 0;
-  int rc = -1;  // the row of the third stretch across an edge held in st0
 #pragma unroll
   for (int g = 0; g <= NE; ++g) {
-    const int b = ed.x[g];
+    // the segment [ia, b) and the exact prefix and odd count at its start,
+    // read from the edges (nothing carried from one segment to the next)
+    const int ia = g == 0 ? 0 : ed.x[g > 0 ? g - 1 : 0], b = ed.x[g];
+    const uint64_t Pa = g == 0 ? 0 : ed.P[g > 0 ? g - 1 : 0];
+    const uint64_t PCa = g == 0 ? 0 : ed.PC[g > 0 ? g - 1 : 0];
     if (b < ia) return false;  // edges out of order: not the premise
     if (b > ia) {
       if (g == 1 || g == 3 || (NE == kEdges56 && g == 5)) {
+        RowStage& sg = st[g >> 1];
         for (int i = ia; i < b; ++i) {
           // a row that, from the actual S, adds exactly or stays inside its
           // binade needs no samples (rows of zeros after a crossing, say)
@@ -1326,12 +1373,11 @@ __device__ bool wave_walk(uint64_t* out, uint64_t* exact, const uint64_t* lE, co
             const int e = binade(s);
             if (e <= 54 && try_apply(&s, closed_pair(lE[i], lC[i], e), e)) continue;
           }
-          RowStage& sg = g == 3 ? st1 : st0;
-          if (i != (g == 1 ? ra : g == 3 ? rb : rc)) {  // a further row of the stretch
+          if (i != staged[g >> 1]) {  // a further row of the stretch
             wave_lds_sync();
             wave_stage_row(sg, i, plane, stride, w, bpc8);
             wave_lds_sync();
-            if (g == 5) rc = i;
+            staged[g >> 1] = i;
           }
           if (!wave_cross_row<NE>(&s, sg, w)) return false;
         }
@@ -1353,12 +1399,44 @@ __device__ bool wave_walk(uint64_t* out, uint64_t* exact, const uint64_t* lE, co
         return false;
       }
     }
-    ia = b;
-    Pa = ed.P[g];
-    PCa = ed.PC[g];
   }
   *out = s;
   return true;
+}
+
+// The fast walk by the whole block (every thread calls it): on success *S
+// (the CPU's sum), *E (the exact sum) and *s1 (the first-moment sum, from
+// pz) are set in wave 0.  xs: four ints of LDS for wave 0's word to the
+// block; ok: an int of LDS.
+template <int NE = kEdges>
+__device__ bool block_fast_walk(uint64_t* S, uint64_t* E, uint64_t* s1, const RowLds& rows,
+                                const uint64_t* pe, const uint32_t* pc, const uint64_t* pz,
+                                int cs, int h, const void* plane, long stride, int w, int bpc8,
+                                RowStage* st, const uint64_t* rp, int* xs, int* ok) {
+  const int wave = threadIdx.x >> 6;
+  WEdgesN<NE> ed;
+  if (wave == 0) {
+    ed = plane_edges<NE>(rows.R, rows.C, pe, pc, cs, h, w, rp);
+    *E = ed.P[NE];
+    uint64_t zz = 0;  // the first-moment sum, off the walk's path
+#pragma unroll
+    for (int q = 0; q < kT / 64; ++q) zz += pz[(threadIdx.x & 63) * (kT / 64) + q];
+    *s1 = wave_sum_u64(zz);
+    if (threadIdx.x == 0) {
+      for (int k = 0; k < 3; ++k) xs[k] = across_row<NE>(ed, k);
+      xs[3] = ed.ok;
+    }
+  }
+  __syncthreads();
+  if (!xs[3]) return false;  // uniform: every thread read the same word
+  int staged[3] = {xs[0], xs[1], xs[2]};
+  block_stage_rows(st, staged, plane, stride, w, bpc8);
+  if (wave == 0) {
+    const bool okw = walk_segments<NE>(S, ed, rows.R, rows.C, plane, stride, w, bpc8, st, staged, rp);
+    if (threadIdx.x == 0) *ok = okw;
+  }
+  __syncthreads();
+  return *ok != 0;
 }
 
 // The fast PSNR noise by one wave, over one chunk of n rows: their exact
@@ -1392,11 +1470,12 @@ __device__ bool wave_noise(uint64_t* sp, uint64_t* exact, const uint64_t* lR, co
   *exact = ed.P[kEdges];
   if (!ed.ok || ed.P[kEdges] >= (1ull << 55)) return false;
   uint64_t s = *sp;
-  int ia = 0;
-  uint64_t Pa = P0;
 #pragma unroll
   for (int g = 0; g <= kEdges; ++g) {
-    const int b = ed.x[g];
+    // the segment [ia, b) and the exact prefix at its start, read from the
+    // edges (nothing carried from one segment to the next)
+    const int ia = g == 0 ? 0 : ed.x[g > 0 ? g - 1 : 0], b = ed.x[g];
+    const uint64_t Pa = g == 0 ? P0 : ed.P[g > 0 ? g - 1 : 0];
     if (b < ia) return false;  // edges out of order: not the premise
     if (b > ia) {
       const int ep = fast_plan(g);
@@ -1417,8 +1496,6 @@ __device__ bool wave_noise(uint64_t* sp, uint64_t* exact, const uint64_t* lR, co
         return false;
       }
     }
-    ia = b;
-    Pa = ed.P[g];
   }
   *sp = s;
   return true;
@@ -1521,19 +1598,30 @@ __device__ __noinline__ void general_walk(const char* plane, long stride, int w,
 // One 512-thread block per (frame, job): jobs 0 and 1 the moments of ref and
 // dis, job 2 the PSNR noise (a call may ask for the moments or the noise
 // alone: jobs [job0, job0 + njobs)).  Fast path: every thread loads the rows' sums
-// into LDS (coalesced), then wave 0 alone walks the plane while the other
-// waves wait at the next barrier (the wave's code has no block barrier);
-// when it does not apply, the whole block takes the general walk.
+// into LDS, then wave 0 finds the plane's edges, the block stages the rows
+// across them, and wave 0 alone walks the segments while the other waves
+// wait at the next barrier (its walk has no block barrier); when it does
+// not apply, the whole block takes the general walk.
 __global__ void __launch_bounds__(kT) k_walk(Geometry g, RowArrays ra, double* results,
                                              uint64_t* units, unsigned dbg) {
   __shared__ BlockScratch sm;
   __shared__ RowLds rows;
   __shared__ RunLds runs;
   __shared__ Seg rseg[kMaxSeg + 1], useg[kMaxSeg + 1];
-  __shared__ __attribute__((aligned(16))) RowStage stage[2];
   __shared__ uint64_t pe[kT], pz[kT];
   __shared__ uint32_t pc[kT];
-  __shared__ __attribute__((aligned(16))) uint16_t wide_row[kRowMax];  // a row the general walk leaves its plan in
+  // one buffer for both walks, which never run at once in a block: the
+  // fast walk's two staged rows, or the row the general walk leaves its
+  // plan in (a block barrier separates a failed fast walk from the general
+  // walk)
+  __shared__ __attribute__((aligned(16))) union RowBuf {
+    RowStage stage[3];
+    uint16_t wide[kRowMax];
+  } rowbuf;
+  static_assert(sizeof(RowStage) * 3 <= sizeof(uint16_t) * kRowMax, "staged rows fit the row buffer");
+  __shared__ int xs[4];
+  RowStage* const stage = rowbuf.stage;
+  uint16_t* const wide_row = rowbuf.wide;
   __shared__ int staged, fast_ok;
   __shared__ uint64_t res[3];
   const int f = blockIdx.x / g.njobs, job = g.job0 + blockIdx.x % g.njobs;
@@ -1616,47 +1704,46 @@ __global__ void __launch_bounds__(kT) k_walk(Geometry g, RowArrays ra, double* r
   } else {
     bool fast = false;
     if (try_fast) {
+      // the rows' sums into LDS, coalesced, every load issued before the
+      // first use; then each thread's contiguous run of cs rows from LDS
       const int cs = (g.h + kT - 1) / kT, i0 = (int)threadIdx.x * cs;
       uint64_t v[kRowsPer];
       uint32_t cv[kRowsPer], zv[kRowsPer];
 #pragma unroll
-      for (int q = 0; q < kRowsPer; ++q) {  // every load issued before the first use
-        const bool in = q < cs && i0 + q < g.h;
-        v[q] = in ? ra.r2[off + i0 + q] : 0;
-        cv[q] = in ? ra.codd[off + i0 + q] : 0;
-        zv[q] = in ? ra.r1[off + i0 + q] : 0;
+      for (int q = 0; q < kRowsPer; ++q) {
+        const int i = q * kT + (int)threadIdx.x;
+        v[q] = i < g.h ? ra.r2[off + i] : 0;
+        cv[q] = i < g.h ? ra.codd[off + i] : 0;
+        zv[q] = i < g.h ? ra.r1[off + i] : 0;
       }
-      uint64_t e = 0, z = 0;
-      uint32_t c = 0;
+      uint64_t z = 0;
 #pragma unroll
       for (int q = 0; q < kRowsPer; ++q) {
-        if (q < cs && i0 + q < g.h) {
-          rows.R[i0 + q] = v[q];
-          rows.C[i0 + q] = (uint16_t)cv[q];  // at most w <= kStage
+        const int i = q * kT + (int)threadIdx.x;
+        if (i < g.h) {
+          rows.R[i] = v[q];
+          rows.C[i] = (uint16_t)cv[q];  // at most w <= kStage
         }
-        e += v[q];
-        c += cv[q];
         z += zv[q];
+      }
+      __syncthreads();
+      uint64_t e = 0;
+      uint32_t c = 0;
+      for (int q = 0; q < cs && i0 + q < g.h; ++q) {
+        e += rows.R[i0 + q];
+        c += rows.C[i0 + q];
       }
       pe[threadIdx.x] = e;
       pc[threadIdx.x] = c;
       pz[threadIdx.x] = z;
       __syncthreads();
-      if (wave == 0) {
-        const bool ok =
-            planned_sum >= (1ull << 55)
-                ? wave_walk<kEdges56>(&S, &E, rows.R, rows.C, pe, pc, cs, g.h, plane, g.stride,
-                                      g.w, g.bpc == 8, stage[0], stage[1], ra.pairs + 2 * off)
-                : wave_walk<kEdges>(&S, &E, rows.R, rows.C, pe, pc, cs, g.h, plane, g.stride,
-                                    g.w, g.bpc == 8, stage[0], stage[1], nullptr);
-        uint64_t zz = 0;  // the first-moment sum, off the walk's path
-#pragma unroll
-        for (int q = 0; q < kT / 64; ++q) zz += pz[(threadIdx.x & 63) * (kT / 64) + q];
-        s1 = wave_sum_u64(zz);
-        if (threadIdx.x == 0) fast_ok = ok;
-      }
-      __syncthreads();
-      fast = fast_ok != 0;
+      fast = planned_sum >= (1ull << 55)
+                 ? block_fast_walk<kEdges56>(&S, &E, &s1, rows, pe, pc, pz, cs, g.h, plane,
+                                             g.stride, g.w, g.bpc == 8, stage, ra.pairs + 2 * off,
+                                             xs, &fast_ok)
+                 : block_fast_walk<kEdges>(&S, &E, &s1, rows, pe, pc, pz, cs, g.h, plane,
+                                           g.stride, g.w, g.bpc == 8, stage, nullptr, xs,
+                                           &fast_ok);
     }
     path = fast ? kPathFast : kPathGeneral;
     if (!fast) {

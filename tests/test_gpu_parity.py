@@ -231,9 +231,9 @@ def test_past_2_55_8k_noise(api, orc):
 
 @pytest.mark.parametrize("flags", [1, 2, 1 | 16, 2 | 32, 32 | 64])
 def test_8k_noise_debug_paths(api, orc, flags):
-    """8K noise (past 2^55, rows wider than the fast path stages) under
-    wrong plans, no plans, no stretches, no closed forms and split pair
-    dispatches: the general walk's every path gives the CPU's bits."""
+    """8K noise (past 2^55) under wrong plans, no plans, no stretches, no
+    closed forms and split pair dispatches, each of which sends the planes
+    to the general walk: its every path gives the CPU's bits."""
     ref, dis = synth.uniform_planes(8000, 1, 4320, 7680, 7680, 16)
     old = api.bef_debug_set(flags)
     try:
@@ -267,13 +267,14 @@ def test_past_2_55_4096x2560(api, orc):
     check_batch(api, orc, ref, dis, 16, label="4096x2560 past 2^55")
 
 
-def binade55_plane(k: int):
+def binade55_plane(k: int, wide: bool = False):
     """Seeded near-maximum 16-bit plane (a fraction of small codewords, some
-    of whose squares tie in the binade of 2^55) of width 3500-4096 and at
-    most 4352 rows, its exact sum in the binade of 2^55; k == 5: its last
-    15% of rows are zeros."""
-    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([0xBEF, 5555, k])))
-    w = int(rng.integers(3500, 4097))
+    of whose squares tie in the binade of 2^55) of width 3500-4096 (wide:
+    4097-8192, on its own seeds) and at most 4352 rows, its exact sum in
+    the binade of 2^55; k == 5: its last 15% of rows are zeros."""
+    seed = [0xBEF, 5556 if wide else 5555, k]
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
+    w = int(rng.integers(4097, 8193) if wide else rng.integers(3500, 4097))
     pad = int(rng.choice([0, 0, 3, 8]))
     lo = int(rng.integers(50000, 62000))
     small = float(rng.choice([0.0, 0.02, 0.05, 0.2]))
@@ -291,15 +292,17 @@ def binade55_plane(k: int):
     return ref, dis, w
 
 
+@pytest.mark.parametrize("wide", [False, True])
 @pytest.mark.parametrize("k", range(6))
-def test_fast_walk_in_the_binade_of_2_55(api, orc, k):
-    """Planes whose exact sum lies in [2^55, 2^56), at most 4096 wide and
-    4352 tall, take the fast walk's seven-edge form (rows across 2^53, 2^54
-    and 2^55 walked term-wise, the stretch inside the binade of 2^55 as the
-    rows' pairs joined in order, a crossing row's part in that binade from
-    its lanes' runs) and give the oracle's bits; case 5 ends in rows of
-    zeros past 2^55 (ADR-1497, Decision: the walk's steps)."""
-    ref, dis, w = binade55_plane(k)
+def test_fast_walk_in_the_binade_of_2_55(api, orc, k, wide):
+    """Planes whose exact sum lies in [2^55, 2^56), at most 8192 wide (the
+    wide cases stage a crossing row in two rounds of loads) and 4352 tall,
+    take the fast walk's seven-edge form (rows across 2^53, 2^54 and 2^55
+    walked term-wise, the stretch inside the binade of 2^55 as the rows'
+    pairs joined in order, a crossing row's part in that binade from its
+    lanes' runs) and give the oracle's bits; case 5 ends in rows of zeros
+    past 2^55 (ADR-1497, Decision: the walk's steps)."""
+    ref, dis, w = binade55_plane(k, wide)
     u = api.bef_frames_units(dev(ref), dev(dis), 16, w=w)
     assert (1 << 55) <= int(u[0, 2]) < (1 << 56), int(u[0, 2])
     check_batch(api, orc, ref, dis, 16, w=w, label=f"binade 55 plane {k}")
@@ -336,13 +339,19 @@ def test_random_crossings(api, orc, k):
     check_batch(api, orc, ref[None], dis[None], bpc, w=w, label=label)
 
 
-def test_wide_rows_past_2_53(api, orc):
-    """7680x1100 full-range noise crosses 2^53 in a row wider than the fast
-    path stages (the general walk reads such rows from memory)."""
-    ref, dis = synth.uniform_planes(7681, 1, 1100, 7680, 7680, 16)
-    units = api.bef_frames_units(dev(ref), dev(dis), 16)
+@pytest.mark.parametrize("w,stride,path", [(7680, 7680, 1), (8192, 8192, 1), (8190, 8193, 1),
+                                           (8200, 8200, 2), (10000, 10003, 2)])
+def test_wide_rows_past_2_53(api, orc, w, stride, path):
+    """Full-range noise, 1100 rows, crosses 2^53 inside a wide row.  Rows of
+    up to 8192 samples take the fast walk, which stages a crossing row in
+    LDS in two rounds of 16-byte loads, or sample by sample when the row is
+    not whole 16-byte chunks (8190 samples, odd stride); wider rows take
+    the general walk, which stages them with the whole block."""
+    ref, dis = synth.uniform_planes(7681 + w, 1, 1100, w, stride, 16)
+    units = api.bef_frames_units(dev(ref), dev(dis), 16, w=w)
     assert (units[:, 2] > 1 << 53).all()
-    check_batch(api, orc, ref, dis, 16, label="7680x1100")
+    check_batch(api, orc, ref, dis, 16, w=w, label=f"{w}x1100 stride {stride}")
+    assert (api.bef_walk_paths()[:, :2] == path).all(), api.bef_walk_paths()
 
 
 @pytest.mark.parametrize("h", [4352, 4353])
@@ -364,10 +373,10 @@ def test_one_chunk_of_rows_past_2_53(api, orc, h):
 def test_walk_paths(api):
     """Which path each walk block takes: the one-wave fast path on 16-bit
     3840x2160 frames (full and half range) and on 4096x2560 frames whose
-    sums lie in the binade of 2^55 (its seven-edge form), exact sums only on
-    10-bit frames that cannot pass 2^53, the general walk on 7680x4320
-    planes (rows wider than the fast path stages) and under a test flag."""
-    cases = [(4, 2, [[1, 1, 1]]), (5, 2, [[1, 1, 1]]), (2, 2, [[0, 0, 0]]), (6, 1, [[2, 2, 1]]),
+    sums lie in the binade of 2^55 and on 7680x4320 noise (its seven-edge
+    form), exact sums only on 10-bit frames that cannot pass 2^53, and the
+    general walk under a test flag."""
+    cases = [(4, 2, [[1, 1, 1]]), (5, 2, [[1, 1, 1]]), (2, 2, [[0, 0, 0]]), (6, 1, [[1, 1, 1]]),
              (7, 1, [[1, 1, 1]])]
     for key, nf, want in cases:
         ref, dis = synth.make_frames(key, frames=nf)
