@@ -202,9 +202,10 @@ int bef_frames_units(const void *ref, const void *dis, int w, int h,
  * synchronous batch (bef_frames, bef_frames_units, moment_frame,
  * psnr_noise) in the process: out[3f + j] for j = 0 ref moments, 1 dis
  * moments, 2 noise, with 0 = exact sums only (no sum can pass 2^53), 1 =
- * the one-wave fast path, 2 = the general walk, 3 = the row-by-row double
- * chain (noise), 4 = not run (the call asked for no result of that job).  Copies min(n, count) bytes to out (HOST; may be NULL)
- * and returns count = 3 * nframes of that batch (0 before any). */
+ * the fast walk (ordered steps by one wave), 2 = the general walk, 3 = the
+ * row-by-row double chain (noise), 4 = not run (the call asked for no
+ * result of that job).  Copies min(n, count) bytes to out (HOST; may be
+ * NULL) and returns count = 3 * nframes of that batch (0 before any). */
 int bef_walk_paths(uint8_t *out, int n);
 
 /* Thread-local text of the last failure ("" if none). */
