@@ -371,7 +371,7 @@ def test_one_chunk_of_rows_past_2_53(api, orc, h):
 
 
 def test_walk_paths(api):
-    """Which path each walk block takes: the one-wave fast path on 16-bit
+    """Which path each walk block takes: the fast walk on 16-bit
     3840x2160 frames (full and half range) and on 4096x2560 frames whose
     sums lie in the binade of 2^55 and on 7680x4320 noise (its seven-edge
     form), exact sums only on 10-bit frames that cannot pass 2^53, and the
