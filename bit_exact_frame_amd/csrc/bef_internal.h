@@ -41,7 +41,7 @@ struct RowArrays {
 
 // Walk paths, per (frame, job), jobs ref moments, dis moments, noise.
 constexpr uint8_t kPathSums = 0;     // no sum can pass 2^53: exact sums only
-constexpr uint8_t kPathFast = 1;     // the fast walk (moments or noise)
+constexpr uint8_t kPathFast = 1;     // the one-wave fast path (moments or noise)
 constexpr uint8_t kPathGeneral = 2;  // the general walk (moments)
 constexpr uint8_t kPathChain = 3;    // the row-by-row double chain (noise)
 constexpr uint8_t kPathSkipped = 4;  // the call asked for no result of this job
