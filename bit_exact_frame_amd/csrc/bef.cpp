@@ -38,6 +38,10 @@ constexpr int kMaxDev = 64;
 constexpr int kMaxPlanes = 4;  // planes of one bef_planes call
 constexpr int kPipeRowQ = 2;   // row streams of pipelined batches
 constexpr int kPipeSlots = 8;  // scratch slots of pipelined batches
+// A pipelined batch whose planes hold at most this many bytes runs whole on
+// the walk stream: its row pass is too short to overlap anything, and the
+// handoff between streams would cost the host more than the batch takes.
+constexpr double kPipeSmallBytes = 1 << 20;
 
 struct Layout {
   size_t r1, r2, rn, codd, plan, pairs, psum, results, units, paths, total;
@@ -490,7 +494,7 @@ int run_host(const void* ref, const void* dis, int w, int h, ptrdiff_t stride, p
 
 // Pipelined batches.  Batch n's rows (and plan and pairs) run on row
 // stream n % kPipeRowQ, its walks on the walk stream once its rows are
-// done.  The row streams take turns, so one batch's row pass overlaps the
+// done; a small batch runs whole on the walk stream.  The row streams take turns, so one batch's row pass overlaps the
 // tail of the one before (and the few microseconds a stream stalls after
 // a dispatch that signals an event), and the walks overlap later row
 // passes.  Slot n % kPipeSlots is rewritten by batch n + kPipeSlots only
@@ -588,7 +592,8 @@ int ovl_submit(const void* ref, const void* dis, int w, int h, ptrdiff_t stride,
   if ((rc = ovl_setup(c.dev, c.L.total, g_pipe_walk_cus))) return rc;
   Arena& a = g_arena[c.dev];
   const int s = (int)(a.pn % kPipeSlots);
-  const hipStream_t rq = a.prow[a.pn % kPipeRowQ];
+  const bool small = 2.0 * w * h * nframes * (bpc == 8 ? 1 : 2) <= kPipeSmallBytes;
+  const hipStream_t rq = small ? a.pwalk : a.prow[a.pn % kPipeRowQ];
   bind(c, (char*)a.pslot + (size_t)s * a.pslot_cap);
   // the batch's reads follow the caller's earlier work on its stream
   if (hipStreamQuery(st) != hipSuccess) {
@@ -598,21 +603,23 @@ int ovl_submit(const void* ref, const void* dis, int w, int h, ptrdiff_t stride,
   }
   // the slot's previous batch must have been walked; a wait costs the host
   // several microseconds, so it is skipped when that walk has already ended
-  if (a.pn >= kPipeSlots && hipEventQuery(a.pwalkdone[s]) != hipSuccess) {
+  // (or, for a small batch, comes earlier on the same stream)
+  if (!small && a.pn >= kPipeSlots && hipEventQuery(a.pwalkdone[s]) != hipSuccess) {
     (void)hipGetLastError();
     BEF_HIP(hipStreamWaitEvent(rq, a.pwalkdone[s], 0));
   }
   // the handoff events are the last dispatches' own completion (no
   // separate marker packet on either queue)
   const unsigned dbg = g_dbg;
+  hipEvent_t rows_done = small ? nullptr : a.prowdone[s];
   if (c.need_pairs) {
     BEF_HIP(launch_rows(c.g, c.ra, rq, nullptr, nullptr));
     BEF_HIP(launch_plan(c.g, c.ra, dbg, rq, nullptr, nullptr));
-    BEF_HIP(launch_pairs(c.g, c.ra, dbg, rq, nullptr, a.prowdone[s]));
+    BEF_HIP(launch_pairs(c.g, c.ra, dbg, rq, nullptr, rows_done));
   } else {
-    BEF_HIP(launch_rows(c.g, c.ra, rq, nullptr, a.prowdone[s]));
+    BEF_HIP(launch_rows(c.g, c.ra, rq, nullptr, rows_done));
   }
-  BEF_HIP(hipStreamWaitEvent(a.pwalk, a.prowdone[s], 0));
+  if (!small) BEF_HIP(hipStreamWaitEvent(a.pwalk, a.prowdone[s], 0));
   BEF_HIP(launch_walk(c.g, c.ra, dev_results, c.d_units, dbg, a.pwalk, nullptr, a.pwalkdone[s]));
   a.pn += 1;
   return 0;

@@ -118,8 +118,11 @@ int bef_frames_noalloc(const void *ref, const void *dis, int w, int h,
  * (and plan and pairs) on row stream n % 2, so that consecutive row passes
  * overlap, and its per-plane walks on a walk stream once its rows are
  * done.  The row streams run on all but n_walk of the device's CUs, the
- * walk stream on the other n_walk (bef_pipe_set_walk_cus, default 16).
- * Each batch's scratch is one of four slots, reused in turn.
+ * walk stream on the other n_walk (bef_pipe_set_walk_cus, default 16).  A
+ * batch whose planes hold at most 1 MiB runs whole on the walk stream, in
+ * order with the walks: its row pass is too short to overlap anything, and
+ * the handoff between streams would cost more than the batch.  Each
+ * batch's scratch is one of eight slots, reused in turn.
  * Arguments and limits as bef_frames_async; dev_results (DEVICE,
  * [nframes][6] doubles, caller-owned) receives the same bits.  The batch's
  * reads start after the work enqueued on `stream` before the call.  The
