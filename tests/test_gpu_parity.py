@@ -354,6 +354,20 @@ def test_wide_rows_past_2_53(api, orc, w, stride, path):
     assert (api.bef_walk_paths()[:, :2] == path).all(), api.bef_walk_paths()
 
 
+@pytest.mark.parametrize("hi,lo_e,hi_e", [(46000, 54, 55), (65536, 55, 56)])
+def test_fast_walk_at_its_largest_plane(api, orc, hi, lo_e, hi_e):
+    """16-bit 8192x4352 noise, the widest rows and the most rows the fast
+    walk takes (every staged row and every chunk of row sums full): U[0,
+    45999] sums into the binade of 2^54 (five edges), the full range into
+    that of 2^55 (seven edges, the rows' pairs in that binade).  Both
+    moment blocks take the fast walk and give the oracle's bits."""
+    ref, dis = synth.uniform_planes(8192 + hi, 1, 4352, 8192, 8192, 16, hi=hi)
+    units = api.bef_frames_units(dev(ref), dev(dis), 16)
+    assert ((units[:, 2:4] >= 1 << lo_e) & (units[:, 2:4] < 1 << hi_e)).all(), units[:, 2:4]
+    check_batch(api, orc, ref, dis, 16, label=f"8192x4352 U[0,{hi - 1}]")
+    assert (api.bef_walk_paths()[:, :2] == 1).all(), api.bef_walk_paths()
+
+
 @pytest.mark.parametrize("h", [4352, 4353])
 def test_one_chunk_of_rows_past_2_53(api, orc, h):
     """2048-wide full-range noise past 2^53 (below 2^55) in a plane of
