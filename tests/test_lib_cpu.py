@@ -286,13 +286,23 @@ def past_2_56_plane():
     return synth.nearmax_plane(rng, 4096, 5120, 60000).astype(np.uint16)
 
 
+@functools.lru_cache(maxsize=None)
+def largest_fast_plane():
+    """16-bit 8192x4352 full-range noise: the widest rows and the most rows
+    the device's fast walk takes, summed into the binade of 2^55."""
+    r, _ = synth.uniform_planes(8192 + 65536, 1, 4352, 8192, 8192, 16)
+    return r[0]
+
+
 def test_fast_emulation_matches_oracle(api):
     """The fast path's decisions (threshold edges, closed forms, rows and
     terms at an edge, and for sums in the binade of 2^55 the seven-edge form
     with its pairs joined in that binade) give the oracle's sum on every
-    plane below 2^56 (8K noise and the 4096x2560 plane reach the binade of
-    2^55), and hand the planes past 2^56 to the general walk."""
-    cases = list(planes()) + [("letterbox", letterbox_plane()), ("past 2^56", past_2_56_plane())]
+    plane below 2^56 (8K noise, the 4096x2560 plane and the 8192x4352 plane
+    reach the binade of 2^55), and hand the planes past 2^56 to the general
+    walk."""
+    cases = list(planes()) + [("letterbox", letterbox_plane()), ("past 2^56", past_2_56_plane()),
+                              ("8192x4352", largest_fast_plane())]
     seen55 = 0
     for name, p in cases:
         got = api.fast_units(p, 16)
@@ -302,13 +312,13 @@ def test_fast_emulation_matches_oracle(api):
             assert got[0] == 0, name
             continue
         seen55 += exact >= 1 << 55
-        if name == "letterbox":
+        if name in ("letterbox", "8192x4352"):
             acc = oracle.Oracle().moment_sums(p, np.zeros_like(p), 16)
             want = int(math.ldexp(acc[2], 16))
         else:
             want = oracle_units(name)[1]
         assert got[0] == 1 and got[1] == want, (name, got, want)
-    assert seen55 == 2
+    assert seen55 == 3
     assert int(checkers.terms_moment(past_2_56_plane()).sum(dtype=np.uint64)) >= 1 << 56
 
 
