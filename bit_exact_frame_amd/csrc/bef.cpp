@@ -494,10 +494,10 @@ int run_host(const void* ref, const void* dis, int w, int h, ptrdiff_t stride, p
 
 // Pipelined batches.  Batch n's rows (and plan and pairs) run on row
 // stream n % kPipeRowQ, its walks on the walk stream once its rows are
-// done; a small batch runs whole on the walk stream.  The row streams take turns, so one batch's row pass overlaps the
-// tail of the one before (and the few microseconds a stream stalls after
-// a dispatch that signals an event), and the walks overlap later row
-// passes.  Slot n % kPipeSlots is rewritten by batch n + kPipeSlots only
+// done; a small batch runs whole on the walk stream.  The row streams take
+// turns, so one batch's row pass overlaps the tail of the one before (and
+// the few microseconds a stream stalls after a dispatch that signals an
+// event), and the walks overlap later row passes.  Slot n % kPipeSlots is rewritten by batch n + kPipeSlots only
 // after batch n's walks have read it.  The walks get CUs of their own: a
 // walk block needs a whole CU's LDS, which a busy row pass never frees.
 void ovl_drain(Arena& a) {
