@@ -1158,7 +1158,8 @@ __device__ void block_stage_rows(RowStage* st, const int* rr, const void* plane,
   const int cpl = run_chunks(w), nc = 64 * cpl;  // chunks held per row
   bool vec = !bpc8 && (w & 7) == 0;
   for (int r = 0; r < 3; ++r)
-    if (rr[r] >= 0) vec = vec && ((uintptr_t)((const uint16_t*)plane + (long)rr[r] * stride) & 15) == 0;
+    if (rr[r] >= 0)
+      vec = vec && ((uintptr_t)((const uint16_t*)plane + (long)rr[r] * stride) & 15) == 0;
   if (vec) {
     const int nv = w >> 3;
     constexpr int K = kStage / 8 / kT;  // chunks of a row per thread
@@ -1432,7 +1433,8 @@ __device__ bool block_fast_walk(uint64_t* S, uint64_t* E, uint64_t* s1, const Ro
   int staged[3] = {xs[0], xs[1], xs[2]};
   block_stage_rows(st, staged, plane, stride, w, bpc8);
   if (wave == 0) {
-    const bool okw = walk_segments<NE>(S, ed, rows.R, rows.C, plane, stride, w, bpc8, st, staged, rp);
+    const bool okw =
+        walk_segments<NE>(S, ed, rows.R, rows.C, plane, stride, w, bpc8, st, staged, rp);
     if (threadIdx.x == 0) *ok = okw;
   }
   __syncthreads();
@@ -1618,7 +1620,8 @@ __global__ void __launch_bounds__(kT) k_walk(Geometry g, RowArrays ra, double* r
     RowStage stage[3];
     uint16_t wide[kRowMax];
   } rowbuf;
-  static_assert(sizeof(RowStage) * 3 <= sizeof(uint16_t) * kRowMax, "staged rows fit the row buffer");
+  static_assert(sizeof(RowStage) * 3 <= sizeof(uint16_t) * kRowMax,
+                "staged rows fit the row buffer");
   __shared__ int xs[4];
   RowStage* const stage = rowbuf.stage;
   uint16_t* const wide_row = rowbuf.wide;
